@@ -1,0 +1,310 @@
+"""Throughput of the multi-LoRA metadata + shrink + expand step on one MI355X.
+
+A step is one pass of the whole path (grouping metadata, shrink, expand) over
+one synthetic batch.  Inputs are resident in HBM before timing starts.  To keep
+the 256 MB Infinity Cache from serving repeats, R copies of every buffer (at
+least 1 GiB in total) are rotated: one HIP graph holds R consecutive steps, each
+on its own copy.  Per-kernel launch durations for the roofline figure are
+measured the same way (a graph of R launches of one kernel), with HIP events on
+the stream the graph is replayed on.  The CPU oracle is timed on the host's
+cores on the same batch, as a reported baseline.
+
+Prints exactly one JSON line on stdout (progress goes to stderr).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
+CPU_BUDGET_S = 10.0      # the CPU baseline runs full batches for about this long
+ROTATE_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: 200 graph "
+                    "replays' worth)")
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", type=int, default=1, help="workload index 0..4 (default 1: "
+                    "Llama-2-7B qkv decode, rank 8)")
+    ap.add_argument("--all", action="store_true", help="one line per workload 1..4")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--rotate", type=int, default=None, help="buffer copies (default: >= 1 GiB)")
+    ap.add_argument("--kernel-reps", type=int, default=50,
+                    help="graph replays per single-kernel timing")
+    return ap.parse_args()
+
+
+class Sets:
+    """R device copies of one workload's buffers, plus the per-copy metadata."""
+
+    def __init__(self, w, R, num_splits):
+        import torch
+
+        import segmented_rank_gemm_amd as srg
+        from tests.gpu_harness import to_dev_bf16
+
+        self.w, self.R, self.num_splits = w, R, num_splits
+        T, maxT = w.num_tokens, w.max_tokens
+        base = dict(
+            mapping=torch.from_numpy(w.mapping.astype("int32")).cuda(),
+            x=to_dev_bf16(w.x[:maxT]),
+            y=to_dev_bf16(w.y0[:maxT]),
+            a=[to_dev_bf16(a) for a in w.lora_a],
+            b=[to_dev_bf16(b) for b in w.lora_b],
+        )
+        self.sets = []
+        for r in range(R):
+            s = dict(
+                mapping=base["mapping"].clone(), x=base["x"].clone(), y=base["y"].clone(),
+                a=[t.clone() for t in base["a"]], b=[t.clone() for t in base["b"]],
+                meta=srg.LoraMeta(maxT, w.max_loras),
+                buf=torch.zeros((num_splits, w.num_slices, maxT, w.rank), dtype=torch.float32,
+                                device="cuda"),
+            )
+            self.sets.append(s)
+        del base
+        torch.cuda.synchronize()
+        self.T = T
+
+    def metadata(self, r, stream=None):
+        import segmented_rank_gemm_amd as srg
+        s = self.sets[r]
+        srg.lora_prepare_metadata(s["mapping"], self.T, s["meta"], stream)
+
+    def shrink(self, r, stream=None):
+        import segmented_rank_gemm_amd as srg
+        s = self.sets[r]
+        srg.lora_shrink(s["x"], s["a"], float(self.w.scale), s["buf"], self.num_splits, s["meta"],
+                        stream)
+
+    def expand(self, r, stream=None):
+        import segmented_rank_gemm_amd as srg
+        s = self.sets[r]
+        srg.lora_expand(s["buf"], self.num_splits, s["b"], s["y"], s["meta"], stream)
+
+    def step(self, r, stream=None):
+        self.metadata(r, stream)
+        self.shrink(r, stream)
+        self.expand(r, stream)
+
+
+def set_bytes(w, num_splits):
+    maxT = w.max_tokens
+    return (maxT * w.hidden * 2 + maxT * w.n_total * 2 + w.num_tokens * 4 + maxT * 4
+            + sum(a.nbytes for a in w.lora_a) + sum(b.nbytes for b in w.lora_b)
+            + num_splits * w.num_slices * maxT * w.rank * 4)
+
+
+def capture(fn_list):
+    """One HIP graph running the given launches in order on a side stream."""
+    import torch
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        cur = torch.cuda.current_stream()
+        for f in fn_list:
+            f(cur)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps):
+    """Average seconds per replay, HIP events on the replay stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        g.replay()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / 1e3 / reps
+
+
+def cpu_baseline(w):
+    import numpy as np
+
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    oracle.run_step(w, num_threads=threads)  # warm-up
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.run_step(w, num_threads=threads)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= CPU_BUDGET_S or (n >= 1 and el * (n + 1) / n > 3 * CPU_BUDGET_S):
+            break
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(value=w.num_tokens * n / el, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{n} full batches of {w.num_tokens} tokens (metadata+shrink+expand, fp64) "
+                       f"in {el:.1f} s; {model}".strip())
+
+
+def run_config(idx, args):
+    import torch
+
+    import segmented_rank_gemm_amd as srg
+    from workloads import CONFIGS, make_workload, workload_stats
+
+    log(f"[bench] workload {idx} ({CONFIGS[idx]['name']}): generating inputs")
+    w = make_workload(idx)
+    st = workload_stats(w)
+    splits = srg.lora_shrink_default_splits(w.hidden, w.max_tokens, w.max_loras, w.num_slices,
+                                            w.rank)
+    sb = set_bytes(w, splits)
+    R = args.rotate or max(2, math.ceil(ROTATE_BYTES / sb))
+    log(f"[bench] {R} rotated buffer sets of {sb / 1e6:.1f} MB, {splits} shrink parts")
+    sets = Sets(w, R, splits)
+
+    # eager pass on every set so the metadata exists before single-kernel graphs replay
+    for r in range(R):
+        sets.step(r)
+    torch.cuda.synchronize()
+
+    g_step = capture([lambda s, r=r: sets.step(r, s) for r in range(R)])
+    steps = args.steps if args.steps is not None else R * 200
+    warm = args.warmup if args.warmup is not None else R * 20
+    full, rem = divmod(steps, R)
+    g_rem = capture([lambda s, r=r: sets.step(r, s) for r in range(rem)]) if rem else None
+    wfull, wrem = divmod(warm, R)
+    log(f"[bench] warmup {warm} steps")
+    for _ in range(wfull):
+        g_step.replay()
+    if wrem:
+        capture([lambda s, r=r: sets.step(r, s) for r in range(wrem)]).replay()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {steps} steps")
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(full):
+        g_step.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = start.elapsed_time(end) / 1e3
+    step_s = wall / steps
+
+    # single-kernel graphs: average launch duration of each kernel, same rotation
+    reps = args.kernel_reps
+    log("[bench] per-kernel timing")
+    per = {}
+    for name in ("metadata", "shrink", "expand"):
+        g = capture([lambda s, r=r, f=getattr(sets, name): f(r, s) for r in range(R)])
+        per[name] = time_graph(g, reps) / R
+        del g
+    pair_g = capture([lambda s, r=r: (sets.shrink(r, s), sets.expand(r, s)) for r in range(R)])
+    pair_s = time_graph(pair_g, reps) / R
+    del pair_g
+
+    # practical ceiling: read+write copy of the expand's algorithmic bytes, same rotation
+    cb = (st["expand_bytes"] // 2) // 16 * 16
+    srcs = [torch.empty(cb, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    dsts = [torch.empty(cb, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    g_copy = capture([lambda s, r=r: srg.lora_stream_copy(srcs[r], dsts[r], s) for r in range(R)])
+    copy_s = time_graph(g_copy, reps) / R
+    del g_copy, srcs, dsts
+
+    exp_bytes = st["expand_bytes"]
+    achieved = exp_bytes / per["expand"] / 1e9
+    out = {
+        "metric": "fused shrink+expand tokens/s and achieved HBM GB/s (% of peak), "
+                  "Llama-2-7B qkv r=8",
+        "value": w.num_tokens / step_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": CONFIGS[idx]["name"], "num_tokens": w.num_tokens,
+            "active_tokens": st["active_tokens"], "hidden": w.hidden, "slices": w.slices,
+            "rank": w.rank, "max_loras": w.max_loras, "active_adapters": st["active_adapters"],
+            "scale": w.scale, "accumulate": "fp32", "shrink_parts": splits,
+            "rotated_sets": R, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "lora_expand", "achieved": achieved,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None, "algorithmic_bytes_per_launch": exp_bytes,
+            "avg_launch_us": per["expand"] * 1e6,
+        },
+        "step": {
+            "gpu_event_ms_per_step": gpu_s / steps * 1e3,
+            "algorithmic_bytes": st["total_bytes"],
+            "achieved_GBs": st["total_bytes"] / step_s / 1e9,
+            "frac_of_peak": st["total_bytes"] / step_s / 1e9 / HBM_PEAK_GBS,
+        },
+        "kernels_us": {k: v * 1e6 for k, v in per.items()},
+        "shrink_expand_pair": {
+            "us": pair_s * 1e6,
+            "tokens_per_s": w.num_tokens / pair_s,
+            "achieved_GBs": (st["shrink_bytes"] + st["expand_bytes"]) / pair_s / 1e9,
+            "frac_of_peak": (st["shrink_bytes"] + st["expand_bytes"]) / pair_s / 1e9 / HBM_PEAK_GBS,
+        },
+        "copy_ceiling": {"bytes_read_plus_written": 2 * cb, "us": copy_s * 1e6,
+                         "GBs": 2 * cb / copy_s / 1e9},
+    }
+    del sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(w)
+    else:
+        out["cpu_baseline"] = None
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the op shards "
+              "per token or per output column without any exchange, and no multi-GPU path is "
+              "built here", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    configs = [1, 2, 3, 4] if args.all else [args.config]
+    for i in configs:
+        print(json.dumps(run_config(i, args)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

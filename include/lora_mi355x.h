@@ -1,0 +1,201 @@
+/*
+ * lora_mi355x.h - C ABI of the MI355X (gfx950) multi-LoRA shrink/expand path.
+ *
+ * One batch of tokens, each tagged with an adapter id (or -1 for none), is
+ * projected through per-adapter low-rank weights:
+ *
+ *   shrink:  buf[s][t][0:r]            = scale * x[t][:] . A_s[l]^T
+ *   expand:  y[t][off_s : off_s + n_s] += buf[s][t][:] . B_s[l]^T
+ *
+ * with l = token_lora_mapping[t] and off_s = n_0 + ... + n_{s-1}.  The batch is
+ * not grouped by adapter; a metadata step groups it on the device first.
+ *   - vLLM PR #13096 "[V1] LoRA - Add triton kernels for V1": the summary names
+ *     the shrink and expand kernels; "Why do we need a new set of kernels"
+ *     explains that V1 batches are not grouped by LoRA id, so the kernels are
+ *     handed the token -> LoRA mapping and load the tokens it selects; "Kernel
+ *     Code Change" item 1 asks for a launch grid that CUDA graphs can capture,
+ *     item 2 for the gather of the input tokens.
+ *   - MLC-LLM issue "[Tracking] Multi-LoRA Serving", Overview: Punica's one-launch
+ *     kernel over a batch split into per-request row segments, each multiplied by
+ *     its own low-rank weights.
+ *   - vLLM PR #14626 "[Kernel] LoRA - Enable CUDAGraphs for V1", review
+ *     comments: the LoRA index buffers are static, sized by the maximum token
+ *     count, captured with their shapes; the graph's pad region is not cleared,
+ *     so inputs must never be updated in place.
+ *
+ * Conventions shared by every entry point:
+ *   - bf16 tensors are passed as raw uint16 bit patterns; fp32 as float.
+ *   - Every pointer is a DEVICE pointer unless marked "host".  All memory is
+ *     owned by the caller.  No call allocates, frees, synchronises or keeps
+ *     state between calls; host arrays are read only during the call.
+ *   - Every call enqueues exactly one kernel on `stream` and returns without
+ *     waiting.  Launch grids depend only on the size arguments (max_tokens,
+ *     max_loras, shapes), never on device data, so a sequence of calls can be
+ *     captured once into a HIP graph and replayed.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid one returns LORA_ERR_INVALID_ARGUMENT and enqueues nothing.
+ *   - Adapter ids outside [-1, max_loras) are device data and cannot raise an
+ *     error without a synchronisation; they are treated as -1 (no adapter).
+ *   - Inputs (x, A, B, the mapping) are never written.  Outputs are written only
+ *     where stated; everything else is left untouched.
+ *   - Calls that write the same buffers must be ordered on one stream.
+ */
+#ifndef LORA_MI355X_H
+#define LORA_MI355X_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lora_status {
+  LORA_OK = 0,
+  LORA_ERR_INVALID_ARGUMENT = 1, /* a null pointer, a size out of range, a misaligned buffer */
+  LORA_ERR_UNSUPPORTED = 2,      /* valid, but outside the shapes this library implements */
+  LORA_ERR_LAUNCH = 3            /* the HIP runtime refused the launch */
+} lora_status_t;
+
+/* Largest supported values of the size arguments. */
+#define LORA_MAX_LORAS 256     /* adapter slots */
+#define LORA_MAX_SLICES 4      /* output slices per call (qkv: 3, gate_up: 2) */
+#define LORA_MAX_SPLITS 64     /* hidden-dimension partitions of the shrink */
+
+/*
+ * Per-batch grouping of the tokens by adapter: the segment description that
+ * shrink and expand read.  A host struct holding device pointers; the struct
+ * itself is read only during a call.  One metadata result serves every LoRA
+ * layer of the batch.
+ *
+ *   sorted_token_ids    int32 [max_tokens]: token indices grouped by adapter id
+ *                       in ascending id order, tokens without an adapter
+ *                       first, token order kept within a group (stable).
+ *                       Entries [num_tokens, max_tokens) are never written.
+ *   active_lora_ids     int32 [max_loras]: the adapter ids that occur in the
+ *                       batch, ascending; unused slots hold -1.
+ *   num_tokens_per_lora int32 [max_loras]: tokens per active slot; unused 0.
+ *   lora_token_start    int32 [max_loras]: offset of the slot's first token in
+ *                       sorted_token_ids; unused slots hold num_tokens.
+ *   num_active          int32 [1]: number of active slots.
+ */
+typedef struct lora_meta {
+  int32_t *sorted_token_ids;
+  int32_t *active_lora_ids;
+  int32_t *num_tokens_per_lora;
+  int32_t *lora_token_start;
+  int32_t *num_active;
+} lora_meta_t;
+
+/*
+ * lora_prepare_metadata - group the batch's tokens by adapter on the device.
+ *
+ * Defined by: vLLM PR #13096, "Why do we need a new set of kernels" (the
+ * kernels must know which tokens map to which LoRA id) and "Kernel Code
+ * Change" item 1 (graph-capturable launch grid); vLLM PR #14626 review
+ * comments (static metadata buffers sized by the maximum token count); the
+ * MLC-LLM issue's Overview (Punica's per-request segment vector).
+ *
+ *   token_lora_mapping  int32 [num_tokens], device; any value, ids outside
+ *                       [-1, max_loras) count as -1.
+ *   num_tokens          0 <= num_tokens <= max_tokens.
+ *   max_tokens          capacity of sorted_token_ids, 1 <= max_tokens <= 2^24.
+ *   max_loras           adapter slots, 1 <= max_loras <= LORA_MAX_LORAS.
+ *   meta                host pointer to the output buffers (all non-null).
+ *
+ * Writes sorted_token_ids[0:num_tokens] and all max_loras entries of the three
+ * per-slot arrays, plus num_active.  A stable counting sort: bit-for-bit
+ * deterministic, no atomics on global memory.  Grid: max_loras + 1 workgroups.
+ */
+lora_status_t lora_prepare_metadata(const int32_t *token_lora_mapping, int32_t num_tokens,
+                                    int32_t max_tokens, int32_t max_loras,
+                                    const lora_meta_t *meta, hipStream_t stream);
+
+/*
+ * lora_shrink_default_splits - recommended number of hidden-dimension
+ * partitions for lora_shrink (host only, no device access).  Returns a value in
+ * [1, LORA_MAX_SPLITS], or 0 if an argument is out of range.  The result is a
+ * pure function of its arguments.
+ */
+int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t max_loras,
+                                   int32_t num_slices, int32_t rank);
+
+/*
+ * lora_shrink - gather each grouped token's activation row and project it onto
+ * its adapter's A:  buf_p[s][t][k] = scale * sum_{h in part p} x[t][h] * A_s[l][k][h].
+ *
+ * Defined by: vLLM PR #13096 summary (the shrink kernel) and "Kernel Code
+ * Change" item 2 (the input tokens are loaded through the token -> LoRA map);
+ * the MLC-LLM issue's Overview (the per-segment low-rank multiplication).
+ *
+ *   x           bf16 [max_tokens][ldx]; columns [0, hidden) are read for the
+ *               tokens that have an adapter.  Rows [0, max_tokens) must be
+ *               addressable.  16-byte aligned.
+ *   ldx         row stride of x in elements; ldx >= hidden, multiple of 8.
+ *   hidden      input width; multiple of 8, 8 <= hidden <= 65536.
+ *   lora_a      host array [num_slices] of device pointers, each
+ *               bf16 [max_loras][rank][hidden], 16-byte aligned.
+ *   num_slices  1 <= num_slices <= LORA_MAX_SLICES.
+ *   rank        one of 8, 16, 32, 64 (LORA_ERR_UNSUPPORTED otherwise).
+ *   scale       applied once, to every partial sum.
+ *   buf         fp32 [num_splits][num_slices][max_tokens][rank], 16-byte
+ *               aligned.  Part p holds the contribution of the p-th of
+ *               num_splits contiguous ranges of the hidden dimension; the
+ *               projection is the sum of the parts (with num_splits == 1 the
+ *               buffer is the projection itself).  Only rows of tokens with an
+ *               adapter are written, in every part.
+ *   num_splits  1 <= num_splits <= LORA_MAX_SPLITS (see
+ *               lora_shrink_default_splits); lora_expand must be given the
+ *               same value.
+ *   meta        output of lora_prepare_metadata for this batch.
+ */
+lora_status_t lora_shrink(const uint16_t *x, int64_t ldx, int32_t hidden,
+                          const uint16_t *const *lora_a, int32_t num_slices, int32_t rank,
+                          float scale, float *buf, int32_t num_splits, const lora_meta_t *meta,
+                          int32_t max_tokens, int32_t max_loras, hipStream_t stream);
+
+/*
+ * lora_expand - project each grouped token's rank-r vector up through its
+ * adapter's B and add it into the output, slice by slice:
+ *   y[t][off_s + n] = bf16( y[t][off_s + n] + sum_k buf[s][t][k] * B_s[l][n][k] ),
+ * where buf[s][t][k] is the fp32 sum over the num_splits parts, the sum is
+ * accumulated in fp32 and the result is rounded to bf16 (nearest, ties even).
+ *
+ * Defined by: vLLM PR #13096 summary (the expand kernel); the MLC-LLM issue's
+ * Overview (per-segment low-rank multiplication); several output slices per
+ * call cover fused projections such as qkv and gate_up.
+ *
+ *   buf         fp32 [num_splits][num_slices][max_tokens][rank], written by
+ *               lora_shrink with the same num_splits.
+ *   lora_b      host array [num_slices] of device pointers, each
+ *               bf16 [max_loras][slice_sizes[s]][rank], 16-byte aligned.
+ *   slice_sizes host array [num_slices]; each a multiple of 8, >= 8.
+ *   y           bf16 [max_tokens][ldy], updated in place: only rows of tokens
+ *               with an adapter, only columns [0, sum of slice_sizes).
+ *               16-byte aligned.
+ *   ldy         row stride of y in elements; >= sum of slice_sizes, multiple
+ *               of 8.
+ *   Other arguments as in lora_shrink.
+ */
+lora_status_t lora_expand(const float *buf, int32_t num_splits, const uint16_t *const *lora_b,
+                          const int32_t *slice_sizes, int32_t num_slices, int32_t rank,
+                          uint16_t *y, int64_t ldy, const lora_meta_t *meta, int32_t max_tokens,
+                          int32_t max_loras, hipStream_t stream);
+
+/* lora_status_string - static, human-readable name of a status code. */
+const char *lora_status_string(lora_status_t status);
+
+/*
+ * lora_stream_copy - measurement aid: copy `bytes` bytes from src to dst with
+ * the same 16-byte vector loads and stores the kernels above use, giving the
+ * practical HBM read+write ceiling next to the nominal 8 TB/s.  bytes must be a
+ * multiple of 16, both pointers 16-byte aligned, buffers not overlapping.
+ */
+lora_status_t lora_stream_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_MI355X_H */

@@ -1,0 +1,201 @@
+"""MI355X (gfx950) multi-LoRA shrink/expand: Python binding of liblora_mi355x.so.
+
+The functions below carry the names of the C entry points declared in
+``include/lora_mi355x.h`` and only marshal arguments: tensors become device
+pointers, the current (or given) torch stream becomes the ``hipStream_t``.
+Every step of the path runs in the library's HIP kernels; there is no other
+implementation to fall back to, and importing this module fails if the
+library has not been built.
+
+torch is imported first so that the library binds to the HIP runtime torch
+has already loaded (same soname), keeping one runtime per process.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch  # noqa: F401  (must precede loading the library, see above)
+
+__all__ = [
+    "LIB_PATH", "LoraError", "LoraMeta", "lib", "lora_prepare_metadata", "lora_shrink",
+    "lora_shrink_default_splits", "lora_expand", "lora_stream_copy", "lora_status_string",
+    "LORA_MAX_LORAS", "LORA_MAX_SLICES", "LORA_MAX_SPLITS", "SUPPORTED_RANKS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora_mi355x.so")
+
+LORA_OK = 0
+LORA_ERR_INVALID_ARGUMENT = 1
+LORA_ERR_UNSUPPORTED = 2
+LORA_ERR_LAUNCH = 3
+LORA_MAX_LORAS = 256
+LORA_MAX_SLICES = 4
+LORA_MAX_SPLITS = 64
+SUPPORTED_RANKS = (8, 16, 32, 64)
+
+
+class LoraError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {lora_status_string(status)} ({status})")
+        self.status = status
+
+
+class _MetaStruct(ctypes.Structure):
+    _fields_ = [("sorted_token_ids", ctypes.c_void_p), ("active_lora_ids", ctypes.c_void_p),
+                ("num_tokens_per_lora", ctypes.c_void_p), ("lora_token_start", ctypes.c_void_p),
+                ("num_active", ctypes.c_void_p)]
+
+
+_VP = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python segmented_rank_gemm_amd/build.py` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        MP = ctypes.POINTER(_MetaStruct)
+        L.lora_status_string.argtypes = [ctypes.c_int]
+        L.lora_status_string.restype = ctypes.c_char_p
+        L.lora_prepare_metadata.argtypes = [_VP, _I32, _I32, _I32, MP, _VP]
+        L.lora_prepare_metadata.restype = ctypes.c_int
+        L.lora_shrink_default_splits.argtypes = [_I32, _I32, _I32, _I32, _I32]
+        L.lora_shrink_default_splits.restype = _I32
+        L.lora_shrink.argtypes = [_VP, _I64, _I32, ctypes.POINTER(_VP), _I32, _I32, ctypes.c_float,
+                                  _VP, _I32, MP, _I32, _I32, _VP]
+        L.lora_shrink.restype = ctypes.c_int
+        L.lora_expand.argtypes = [_VP, _I32, ctypes.POINTER(_VP), ctypes.POINTER(_I32), _I32, _I32,
+                                  _VP, _I64, MP, _I32, _I32, _VP]
+        L.lora_expand.restype = ctypes.c_int
+        L.lora_stream_copy.argtypes = [_VP, _VP, _I64, _VP]
+        L.lora_stream_copy.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+lib()  # fail at import, loudly, if the native library is absent
+
+
+def lora_status_string(status: int) -> str:
+    return lib().lora_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != LORA_OK:
+        raise LoraError(fn, status)
+
+
+def _stream_handle(stream: Optional[torch.cuda.Stream]) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _dev_ptr(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return int(t.data_ptr())
+
+
+class LoraMeta:
+    """Device buffers of one batch's grouping (the ``lora_meta_t`` outputs).
+
+    Allocated once for a (max_tokens, max_loras) pair and reused for every
+    batch, as static buffers that a captured graph keeps pointing at.
+    """
+
+    def __init__(self, max_tokens: int, max_loras: int, device="cuda"):
+        self.max_tokens = int(max_tokens)
+        self.max_loras = int(max_loras)
+        opts = dict(dtype=torch.int32, device=device)
+        self.sorted_token_ids = torch.empty(self.max_tokens, **opts)
+        self.active_lora_ids = torch.empty(self.max_loras, **opts)
+        self.num_tokens_per_lora = torch.empty(self.max_loras, **opts)
+        self.lora_token_start = torch.empty(self.max_loras, **opts)
+        self.num_active = torch.empty(1, **opts)
+        self._struct = _MetaStruct(*(int(t.data_ptr()) for t in self.tensors()))
+
+    def tensors(self):
+        return (self.sorted_token_ids, self.active_lora_ids, self.num_tokens_per_lora,
+                self.lora_token_start, self.num_active)
+
+    @property
+    def struct_ref(self):
+        return ctypes.byref(self._struct)
+
+
+def lora_prepare_metadata(token_lora_mapping: torch.Tensor, num_tokens: int, meta: LoraMeta,
+                          stream: Optional[torch.cuda.Stream] = None) -> None:
+    ptr = _dev_ptr(token_lora_mapping, torch.int32, "token_lora_mapping") if num_tokens else 0
+    if num_tokens and token_lora_mapping.numel() < num_tokens:
+        raise ValueError("token_lora_mapping is shorter than num_tokens")
+    _check("lora_prepare_metadata", lib().lora_prepare_metadata(
+        ptr, int(num_tokens), meta.max_tokens, meta.max_loras, meta.struct_ref,
+        _stream_handle(stream)))
+
+
+def lora_shrink_default_splits(hidden: int, max_tokens: int, max_loras: int, num_slices: int,
+                               rank: int) -> int:
+    return int(lib().lora_shrink_default_splits(hidden, max_tokens, max_loras, num_slices, rank))
+
+
+def lora_shrink(x: torch.Tensor, lora_a: Sequence[torch.Tensor], scale: float, buf: torch.Tensor,
+                num_splits: int, meta: LoraMeta,
+                stream: Optional[torch.cuda.Stream] = None) -> None:
+    """x: bf16 [max_tokens, >=hidden] (row stride x.stride(0)); lora_a[s]: bf16
+    [max_loras, rank, hidden]; buf: fp32 [num_splits, S, max_tokens, rank]."""
+    S = len(lora_a)
+    _, rank, hidden = lora_a[0].shape
+    if x.dim() != 2 or x.stride(1) != 1 or x.shape[0] < meta.max_tokens:
+        raise ValueError("x must be [>=max_tokens, hidden] with unit column stride")
+    if tuple(buf.shape) != (num_splits, S, meta.max_tokens, rank) or not buf.is_contiguous():
+        raise ValueError("buf must be contiguous [num_splits, S, max_tokens, rank]")
+    for a in lora_a:
+        if tuple(a.shape) != (meta.max_loras, rank, hidden) or not a.is_contiguous():
+            raise ValueError("lora_a[s] must be contiguous [max_loras, rank, hidden]")
+    aptrs = (_VP * S)(*[_dev_ptr(a, torch.bfloat16, "lora_a") for a in lora_a])
+    _check("lora_shrink", lib().lora_shrink(
+        _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), int(hidden), aptrs, S, int(rank),
+        float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits), meta.struct_ref,
+        meta.max_tokens, meta.max_loras, _stream_handle(stream)))
+
+
+def lora_expand(buf: torch.Tensor, num_splits: int, lora_b: Sequence[torch.Tensor], y: torch.Tensor,
+                meta: LoraMeta, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """buf: fp32 [num_splits, S, max_tokens, rank]; lora_b[s]: bf16 [max_loras, n_s, rank];
+    y: bf16 [>=max_tokens, >=sum(n_s)] (row stride y.stride(0)), updated in place."""
+    S = len(lora_b)
+    rank = int(lora_b[0].shape[2])
+    sizes = [int(b.shape[1]) for b in lora_b]
+    if tuple(buf.shape) != (num_splits, S, meta.max_tokens, rank) or not buf.is_contiguous():
+        raise ValueError("buf must be contiguous [num_splits, S, max_tokens, rank]")
+    if y.dim() != 2 or y.stride(1) != 1 or y.shape[0] < meta.max_tokens or y.shape[1] < sum(sizes):
+        raise ValueError("y must be [>=max_tokens, >=sum(n_s)] with unit column stride")
+    for b, n in zip(lora_b, sizes):
+        if tuple(b.shape) != (meta.max_loras, n, rank) or not b.is_contiguous():
+            raise ValueError("lora_b[s] must be contiguous [max_loras, n_s, rank]")
+    bptrs = (_VP * S)(*[_dev_ptr(b, torch.bfloat16, "lora_b") for b in lora_b])
+    nsz = (_I32 * S)(*sizes)
+    _check("lora_expand", lib().lora_expand(
+        _dev_ptr(buf, torch.float32, "buf"), int(num_splits), bptrs, nsz, S, rank,
+        _dev_ptr(y, torch.bfloat16, "y"), int(y.stride(0)), meta.struct_ref, meta.max_tokens,
+        meta.max_loras, _stream_handle(stream)))
+
+
+def lora_stream_copy(src: torch.Tensor, dst: torch.Tensor,
+                     stream: Optional[torch.cuda.Stream] = None) -> None:
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    _check("lora_stream_copy", lib().lora_stream_copy(int(src.data_ptr()), int(dst.data_ptr()),
+                                                      int(nbytes), _stream_handle(stream)))

@@ -1,0 +1,155 @@
+// Device-side helpers shared by the gfx950 kernels of the multi-LoRA path:
+// 16-byte vector types, bf16 <-> fp32 conversion, wave-level scans, and the
+// per-workgroup segment table that maps a flat tile index onto an adapter's
+// group of tokens.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lora_mi355x.h"
+
+namespace lora {
+
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// MFMA operand types: 8 bf16 (16x16x32) and 4 x 16-bit (16x16x16, "1k" form).
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x2 load8(const void* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+__device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Low / high bf16 of a packed pair, widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two fp32 values rounded to bf16 (nearest, ties to even) and packed, `lo` in
+// the low half; one hardware conversion on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x & (kWave - 1)); }
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+// Segment table: the active adapter slots of one batch (from the metadata
+// step) cut into tiles of TILE consecutive grouped tokens.  A tile never spans
+// two adapters.  Built by wave 0 of every workgroup; slot data that does not
+// describe a range inside [0, max_tokens) is dropped, so a corrupted metadata
+// buffer cannot send a kernel outside its arrays.
+struct SegmentTable {
+  int start[LORA_MAX_LORAS];     // first grouped position of the slot
+  int count[LORA_MAX_LORAS];     // tokens of the slot (0 if dropped)
+  int lora[LORA_MAX_LORAS];      // adapter id of the slot
+  int tile_end[LORA_MAX_LORAS];  // inclusive running sum of tiles per slot
+  int num_slots;
+  int num_tiles;
+};
+
+template <int TILE>
+__device__ void build_segment_table(SegmentTable& tab, const int32_t* __restrict__ active_ids,
+                                    const int32_t* __restrict__ counts,
+                                    const int32_t* __restrict__ starts,
+                                    const int32_t* __restrict__ num_active, int max_loras,
+                                    int max_tokens) {
+  if (threadIdx.x < kWave) {
+    const int lane = lane_id();
+    int na = *num_active;
+    na = na < 0 ? 0 : (na > max_loras ? max_loras : na);
+    int carry = 0;
+    for (int base = 0; base < na; base += kWave) {
+      const int i = base + lane;
+      int cnt = 0, st = 0, id = 0;
+      if (i < na) {
+        cnt = counts[i];
+        st = starts[i];
+        id = active_ids[i];
+        const bool ok = id >= 0 && id < max_loras && cnt > 0 && st >= 0 && st <= max_tokens &&
+                        cnt <= max_tokens - st;
+        if (!ok) cnt = 0;
+      }
+      const int incl = wave_inclusive_scan((cnt + TILE - 1) / TILE);
+      if (i < na) {
+        tab.start[i] = st;
+        tab.count[i] = cnt;
+        tab.lora[i] = id;
+        tab.tile_end[i] = carry + incl;
+      }
+      carry += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) {
+      tab.num_slots = na;
+      tab.num_tiles = carry;
+    }
+  }
+  __syncthreads();
+}
+
+// Slot holding flat tile m (0 <= m < num_tiles), the first slot whose running
+// tile count exceeds m.  Must be called with the same m by all lanes of a wave.
+__device__ __forceinline__ int find_slot(const SegmentTable& tab, int m) {
+  const int lane = lane_id();
+  for (int base = 0; base < tab.num_slots; base += kWave) {
+    const int i = base + lane;
+    const unsigned long long hit = __ballot(i < tab.num_slots && tab.tile_end[i] > m);
+    if (hit) return base + __ffsll(static_cast<long long>(hit)) - 1;
+  }
+  return 0;  // unreachable for m < num_tiles
+}
+
+// Tile m resolved to its adapter and grouped-token range [first, first + rows).
+struct Tile {
+  int lora;
+  int first;
+  int rows;
+};
+
+template <int TILE>
+__device__ __forceinline__ Tile resolve_tile(const SegmentTable& tab, int m) {
+  const int slot = find_slot(tab, m);
+  const int before = slot > 0 ? tab.tile_end[slot - 1] : 0;
+  const int j = m - before;
+  Tile t;
+  t.lora = tab.lora[slot];
+  t.first = tab.start[slot] + j * TILE;
+  const int left = tab.count[slot] - j * TILE;
+  t.rows = left < TILE ? left : TILE;
+  return t;
+}
+
+// Token index at grouped position `pos`, or -1 if outside [0, max_tokens).
+__device__ __forceinline__ int token_at(const int32_t* __restrict__ sorted, int pos,
+                                        int max_tokens) {
+  const int t = sorted[pos];
+  return (t >= 0 && t < max_tokens) ? t : -1;
+}
+
+}  // namespace lora

@@ -1,0 +1,150 @@
+// C ABI of the multi-LoRA shrink/expand library: host-side argument checks,
+// then exactly one kernel launch per call on the caller's stream.  No call
+// allocates, synchronises or keeps state; launch grids depend only on the size
+// arguments, so captured graphs stay valid for any batch of the same sizes
+// (vLLM PR #13096 "[V1] LoRA - Add triton kernels for V1", "Kernel Code
+// Change" item 1; vLLM PR #14626 "[Kernel] LoRA - Enable CUDAGraphs for V1").
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lora_mi355x.h"
+
+namespace lora {
+hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_loras,
+                           const lora_meta_t& meta, hipStream_t stream);
+hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint16_t* const* lora_a,
+                         int num_slices, int rank, float scale, float* buf, int num_splits,
+                         const lora_meta_t& meta, int max_tokens, int max_loras, int num_cus,
+                         hipStream_t stream);
+hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const* lora_b,
+                         const int32_t* slice_sizes, int num_slices, int rank, uint16_t* y,
+                         int64_t ldy, const lora_meta_t& meta, int max_tokens, int max_loras,
+                         int num_cus, hipStream_t stream);
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int num_cus,
+                              hipStream_t stream);
+}  // namespace lora
+
+namespace {
+
+constexpr int32_t kMaxTokens = 1 << 24;
+constexpr int32_t kMaxHidden = 65536;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool meta_ok(const lora_meta_t* m) {
+  return m && m->sorted_token_ids && m->active_lora_ids && m->num_tokens_per_lora &&
+         m->lora_token_start && m->num_active;
+}
+
+bool sizes_ok(int32_t max_tokens, int32_t max_loras) {
+  return max_tokens >= 1 && max_tokens <= kMaxTokens && max_loras >= 1 &&
+         max_loras <= LORA_MAX_LORAS;
+}
+
+bool rank_supported(int32_t rank) { return rank == 8 || rank == 16 || rank == 32 || rank == 64; }
+
+// Compute units of the current device: sizes the persistent grids.  A host
+// query answered from the runtime's cached device properties.
+int current_cus() {
+  int dev = 0;
+  int cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  return cus;
+}
+
+lora_status_t launch_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lora_status_string(lora_status_t status) {
+  switch (status) {
+    case LORA_OK: return "LORA_OK";
+    case LORA_ERR_INVALID_ARGUMENT: return "LORA_ERR_INVALID_ARGUMENT";
+    case LORA_ERR_UNSUPPORTED: return "LORA_ERR_UNSUPPORTED";
+    case LORA_ERR_LAUNCH: return "LORA_ERR_LAUNCH";
+  }
+  return "LORA_ERR_UNKNOWN";
+}
+
+lora_status_t lora_prepare_metadata(const int32_t* token_lora_mapping, int32_t num_tokens,
+                                    int32_t max_tokens, int32_t max_loras,
+                                    const lora_meta_t* meta, hipStream_t stream) {
+  if (!meta_ok(meta) || !sizes_ok(max_tokens, max_loras)) return LORA_ERR_INVALID_ARGUMENT;
+  if (num_tokens < 0 || num_tokens > max_tokens) return LORA_ERR_INVALID_ARGUMENT;
+  if (num_tokens > 0 && !token_lora_mapping) return LORA_ERR_INVALID_ARGUMENT;
+  return launch_status(lora::launch_metadata(token_lora_mapping, num_tokens, max_loras, *meta, stream));
+}
+
+int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t max_loras,
+                                   int32_t num_slices, int32_t rank) {
+  if (hidden < 8 || hidden > kMaxHidden || !sizes_ok(max_tokens, max_loras) || num_slices < 1 ||
+      num_slices > LORA_MAX_SLICES || rank < 1 || rank > 64)
+    return 0;
+  // Enough (tile, part) units for ~4 workgroups per CU of a 256-CU device at
+  // the largest batch, with parts no shorter than 512 hidden elements.
+  const int64_t tiles = (static_cast<int64_t>(max_tokens) + 15) / 16 + max_loras;
+  int64_t splits = (1024 + tiles - 1) / tiles;
+  const int64_t by_len = hidden / 512 > 0 ? hidden / 512 : 1;
+  splits = splits < by_len ? splits : by_len;
+  splits = splits < 1 ? 1 : (splits > LORA_MAX_SPLITS ? LORA_MAX_SPLITS : splits);
+  return static_cast<int32_t>(splits);
+}
+
+lora_status_t lora_shrink(const uint16_t* x, int64_t ldx, int32_t hidden,
+                          const uint16_t* const* lora_a, int32_t num_slices, int32_t rank,
+                          float scale, float* buf, int32_t num_splits, const lora_meta_t* meta,
+                          int32_t max_tokens, int32_t max_loras, hipStream_t stream) {
+  if (!meta_ok(meta) || !sizes_ok(max_tokens, max_loras)) return LORA_ERR_INVALID_ARGUMENT;
+  if (!x || !lora_a || !buf || !aligned16(x) || !aligned16(buf)) return LORA_ERR_INVALID_ARGUMENT;
+  if (hidden < 8 || hidden > kMaxHidden || hidden % 8 != 0) return LORA_ERR_INVALID_ARGUMENT;
+  if (ldx < hidden || ldx % 8 != 0) return LORA_ERR_INVALID_ARGUMENT;
+  if (num_slices < 1 || num_slices > LORA_MAX_SLICES) return LORA_ERR_INVALID_ARGUMENT;
+  if (num_splits < 1 || num_splits > LORA_MAX_SPLITS) return LORA_ERR_INVALID_ARGUMENT;
+  if (rank < 1 || rank > 64) return LORA_ERR_INVALID_ARGUMENT;
+  for (int32_t s = 0; s < num_slices; ++s)
+    if (!lora_a[s] || !aligned16(lora_a[s])) return LORA_ERR_INVALID_ARGUMENT;
+  if (!rank_supported(rank)) return LORA_ERR_UNSUPPORTED;
+  return launch_status(lora::launch_shrink(x, ldx, hidden, lora_a, num_slices, rank, scale, buf,
+                                           num_splits, *meta, max_tokens, max_loras,
+                                           current_cus(), stream));
+}
+
+lora_status_t lora_expand(const float* buf, int32_t num_splits, const uint16_t* const* lora_b,
+                          const int32_t* slice_sizes, int32_t num_slices, int32_t rank,
+                          uint16_t* y, int64_t ldy, const lora_meta_t* meta, int32_t max_tokens,
+                          int32_t max_loras, hipStream_t stream) {
+  if (!meta_ok(meta) || !sizes_ok(max_tokens, max_loras)) return LORA_ERR_INVALID_ARGUMENT;
+  if (!buf || !lora_b || !slice_sizes || !y || !aligned16(buf) || !aligned16(y))
+    return LORA_ERR_INVALID_ARGUMENT;
+  if (num_slices < 1 || num_slices > LORA_MAX_SLICES) return LORA_ERR_INVALID_ARGUMENT;
+  if (num_splits < 1 || num_splits > LORA_MAX_SPLITS) return LORA_ERR_INVALID_ARGUMENT;
+  if (rank < 1 || rank > 64) return LORA_ERR_INVALID_ARGUMENT;
+  int64_t n_total = 0;
+  for (int32_t s = 0; s < num_slices; ++s) {
+    if (!lora_b[s] || !aligned16(lora_b[s])) return LORA_ERR_INVALID_ARGUMENT;
+    if (slice_sizes[s] < 8 || slice_sizes[s] % 8 != 0) return LORA_ERR_INVALID_ARGUMENT;
+    n_total += slice_sizes[s];
+  }
+  if (n_total > (int64_t{1} << 30) || ldy < n_total || ldy % 8 != 0) return LORA_ERR_INVALID_ARGUMENT;
+  if (!rank_supported(rank)) return LORA_ERR_UNSUPPORTED;
+  return launch_status(lora::launch_expand(buf, num_splits, lora_b, slice_sizes, num_slices, rank,
+                                           y, ldy, *meta, max_tokens, max_loras, current_cus(),
+                                           stream));
+}
+
+lora_status_t lora_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  if (!src || !dst || bytes <= 0 || bytes % 16 != 0 || !aligned16(src) || !aligned16(dst))
+    return LORA_ERR_INVALID_ARGUMENT;
+  const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+  if (s < d + static_cast<uintptr_t>(bytes) && d < s + static_cast<uintptr_t>(bytes))
+    return LORA_ERR_INVALID_ARGUMENT;
+  return launch_status(lora::launch_stream_copy(src, dst, bytes, current_cus(), stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+"""Helpers for the GPU tests: move a seeded workload onto the device, run the
+HIP path through the binding, bring results back, and apply the comparison
+criteria against the oracle."""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+import segmented_rank_gemm_amd as srg
+from workloads import f32_from_bf16_bits
+
+
+def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(a).cuda().view(torch.bfloat16)
+
+
+def from_dev_bf16(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return f32_from_bf16_bits(bits).astype(np.float64)
+
+
+@dataclasses.dataclass
+class DeviceWorkload:
+    w: object
+    mapping: torch.Tensor
+    x: torch.Tensor
+    lora_a: List[torch.Tensor]
+    lora_b: List[torch.Tensor]
+    y: torch.Tensor
+    meta: srg.LoraMeta
+    buf: torch.Tensor
+    num_splits: int
+
+
+def upload(w, num_splits: Optional[int] = None, ldx_pad: int = 0, ldy_pad: int = 0,
+           buf_fill: float = float("nan"), sorted_fill: int = -7) -> DeviceWorkload:
+    maxT = w.max_tokens
+    mapping = torch.from_numpy(np.ascontiguousarray(w.mapping, dtype=np.int32)).cuda()
+    x_host = np.zeros((maxT, w.hidden + ldx_pad), dtype=np.uint16)
+    x_host[:, :w.hidden] = w.x[:maxT]
+    x = to_dev_bf16(x_host)
+    y_host = np.full((maxT, w.n_total + ldy_pad), 0x7FC1, dtype=np.uint16)  # sentinel NaN pad
+    y_host[:, :w.n_total] = w.y0[:maxT]
+    y = to_dev_bf16(y_host)
+    lora_a = [to_dev_bf16(a) for a in w.lora_a]
+    lora_b = [to_dev_bf16(b) for b in w.lora_b]
+    if num_splits is None:
+        num_splits = srg.lora_shrink_default_splits(w.hidden, maxT, w.max_loras, w.num_slices,
+                                                    w.rank)
+    meta = srg.LoraMeta(maxT, w.max_loras)
+    meta.sorted_token_ids.fill_(sorted_fill)
+    buf = torch.full((num_splits, w.num_slices, maxT, w.rank), buf_fill, dtype=torch.float32,
+                     device="cuda")
+    return DeviceWorkload(w, mapping, x, lora_a, lora_b, y, meta, buf, num_splits)
+
+
+def run_step(d: DeviceWorkload, stream=None) -> None:
+    srg.lora_prepare_metadata(d.mapping, d.w.num_tokens, d.meta, stream)
+    srg.lora_shrink(d.x, d.lora_a, float(d.w.scale), d.buf, d.num_splits, d.meta, stream)
+    srg.lora_expand(d.buf, d.num_splits, d.lora_b, d.y, d.meta, stream)
+
+
+def meta_host(d: DeviceWorkload) -> dict:
+    return {k: v.cpu().numpy() for k, v in zip(
+        ["sorted_token_ids", "active_lora_ids", "num_tokens_per_lora", "lora_token_start",
+         "num_active"], d.meta.tensors())}
+
+
+def ulp_bf16(v: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 numbers at |v| (8 significant bits; 2^-133 below 2^-126)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    _, e = np.frexp(a)          # a = m * 2^e, m in [0.5, 1)
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
+def y_report(y_gpu_bits: np.ndarray, y64: np.ndarray, y_ref_bits: np.ndarray) -> dict:
+    """Tolerance max|y_gpu - y_ref| <= 1e-2 rms(y_ref) + 1e-3, read on top of the
+    half-ulp that rounding the output to bf16 costs (see the design notes)."""
+    g = bf16_to_f64(y_gpu_bits)
+    rms = float(np.sqrt(np.mean(y64 * y64))) if y64.size else 0.0
+    tol = 1e-2 * rms + 1e-3
+    err = np.abs(g - y64)
+    excess = err - 0.5 * ulp_bf16(y64)
+    ref_rne = bf16_to_f64(y_ref_bits)
+    return dict(
+        tol=tol, rms=rms,
+        max_excess_over_half_ulp=float(excess.max()) if excess.size else 0.0,
+        max_abs_err_vs_y64=float(err.max()) if err.size else 0.0,
+        literal_over_tol_vs_y64=int(np.sum(err > tol)),
+        literal_over_tol_vs_rne=int(np.sum(np.abs(g - ref_rne) > tol)),
+        ulp_mismatch_vs_rne=int(np.sum(y_gpu_bits != y_ref_bits)),
+        n=int(y64.size),
+    )
+
+
+def buf_sum(d: DeviceWorkload) -> np.ndarray:
+    """Sum over the shrink's parts, in part order, in float64: [S, max_tokens, r]."""
+    b = d.buf.cpu().numpy().astype(np.float64)
+    return b.sum(axis=0)

@@ -1,0 +1,143 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point the header declares, and rejects invalid arguments before
+enqueuing anything.  No call here reaches the HIP runtime."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import segmented_rank_gemm_amd as srg
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "lora_mi355x.h")
+
+FAKE = 0x10000  # a 16-byte aligned non-null address that is never dereferenced
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ["lora_prepare_metadata", "lora_shrink", "lora_expand", "lora_status_string",
+              "lora_shrink_default_splits", "lora_stream_copy"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(srg.LIB_PATH)
+    for n in _declared():
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert srg.lora_status_string(0) == "LORA_OK"
+    assert srg.lora_status_string(1) == "LORA_ERR_INVALID_ARGUMENT"
+    assert srg.lora_status_string(2) == "LORA_ERR_UNSUPPORTED"
+    assert srg.lora_status_string(3) == "LORA_ERR_LAUNCH"
+    assert srg.lora_status_string(99) == "LORA_ERR_UNKNOWN"
+
+
+def _meta(**null):
+    fields = dict(sorted_token_ids=FAKE, active_lora_ids=FAKE, num_tokens_per_lora=FAKE,
+                  lora_token_start=FAKE, num_active=FAKE)
+    fields.update(null)
+    return ctypes.byref(srg._MetaStruct(**fields))
+
+
+def _ptrs(n, value=FAKE):
+    return (ctypes.c_void_p * n)(*([value] * n))
+
+
+@pytest.mark.parametrize("num_tokens,max_tokens,max_loras,meta", [
+    (-1, 16, 4, None), (17, 16, 4, None), (4, 0, 4, None), (4, 16, 0, None), (4, 16, 257, None),
+    (4, 1 << 25, 4, None), (4, 16, 4, dict(num_active=None)), (4, 16, 4, dict(sorted_token_ids=None)),
+])
+def test_prepare_metadata_rejects(num_tokens, max_tokens, max_loras, meta):
+    m = _meta(**(meta or {}))
+    assert srg.lib().lora_prepare_metadata(FAKE, num_tokens, max_tokens, max_loras, m, None) == 1
+
+
+def test_prepare_metadata_rejects_null_mapping_with_tokens():
+    assert srg.lib().lora_prepare_metadata(None, 3, 16, 4, _meta(), None) == 1
+
+
+SHRINK_OK = dict(x=FAKE, ldx=4096, hidden=4096, a=3, S=3, rank=8, scale=1.0, buf=FAKE, splits=4,
+                 maxT=256, L=4)
+
+
+def _shrink(**kw):
+    a = dict(SHRINK_OK)
+    a.update(kw)
+    aptr = a["a"] if not isinstance(a["a"], int) else _ptrs(a["a"])
+    return srg.lib().lora_shrink(a["x"], a["ldx"], a["hidden"], aptr, a["S"], a["rank"],
+                                 a["scale"], a["buf"], a["splits"], _meta(), a["maxT"], a["L"],
+                                 None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(x=FAKE + 2), 1), (dict(buf=FAKE + 4), 1), (dict(hidden=4092), 1),
+    (dict(hidden=0), 1), (dict(ldx=4000), 1), (dict(ldx=4100), 1), (dict(S=0), 1), (dict(S=5), 1),
+    (dict(splits=0), 1), (dict(splits=65), 1), (dict(rank=0), 1), (dict(rank=65), 1),
+    (dict(maxT=0), 1), (dict(L=300), 1), (dict(a=_ptrs(3, None)), 1),
+    (dict(a=_ptrs(3, FAKE + 8)), 1), (dict(hidden=1 << 17, ldx=1 << 17), 1),
+    (dict(rank=12), 2), (dict(rank=4), 2), (dict(rank=128 // 2 - 1), 2),
+])
+def test_shrink_rejects(kw, status):
+    assert _shrink(**kw) == status
+
+
+EXPAND_OK = dict(buf=FAKE, splits=4, b=3, sizes=(4096, 4096, 4096), S=3, rank=8, y=FAKE,
+                 ldy=12288, maxT=256, L=4)
+
+
+def _expand(**kw):
+    a = dict(EXPAND_OK)
+    a.update(kw)
+    bptr = a["b"] if not isinstance(a["b"], int) else _ptrs(a["b"])
+    sizes = (ctypes.c_int32 * len(a["sizes"]))(*a["sizes"]) if a["sizes"] is not None else None
+    return srg.lib().lora_expand(a["buf"], a["splits"], bptr, sizes, a["S"], a["rank"], a["y"],
+                                 a["ldy"], _meta(), a["maxT"], a["L"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(buf=None), 1), (dict(y=None), 1), (dict(y=FAKE + 2), 1), (dict(sizes=None), 1),
+    (dict(sizes=(4096, 4096, 4092)), 1), (dict(sizes=(4096, 0, 4096)), 1), (dict(ldy=12280), 1),
+    (dict(ldy=12290), 1), (dict(S=0), 1), (dict(S=5), 1), (dict(splits=0), 1),
+    (dict(b=_ptrs(3, None)), 1), (dict(rank=80), 1), (dict(rank=24), 2),
+])
+def test_expand_rejects(kw, status):
+    assert _expand(**kw) == status
+
+
+def test_stream_copy_rejects():
+    L = srg.lib()
+    assert L.lora_stream_copy(None, FAKE, 64, None) == 1
+    assert L.lora_stream_copy(FAKE, FAKE + 4096, 20, None) == 1
+    assert L.lora_stream_copy(FAKE, FAKE + 32, 64, None) == 1  # overlap
+    assert L.lora_stream_copy(FAKE, FAKE + 4096, 0, None) == 1
+
+
+def test_default_splits_is_pure_and_in_range():
+    f = srg.lora_shrink_default_splits
+    assert f(4096, 256, 4, 3, 8) == f(4096, 256, 4, 3, 8)
+    for args in [(4096, 256, 4, 3, 8), (4096, 8192, 4, 2, 16), (11008, 2048, 16, 1, 64),
+                 (8192, 4096, 64, 3, 32), (256, 16, 2, 1, 8), (8, 1, 1, 1, 8)]:
+        v = f(*args)
+        assert 1 <= v <= srg.LORA_MAX_SPLITS, args
+    assert f(0, 256, 4, 3, 8) == 0
+    assert f(4096, 256, 4, 9, 8) == 0
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    meta_like = type("M", (), {"max_tokens": 4, "max_loras": 2})()
+    with pytest.raises((TypeError, ValueError)):
+        srg.lora_shrink(torch.zeros(4, 8, dtype=torch.bfloat16),
+                        [torch.zeros(2, 8, 8, dtype=torch.bfloat16)], 1.0,
+                        torch.zeros(1, 1, 4, 8), 1, meta_like)

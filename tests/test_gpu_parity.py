@@ -1,0 +1,253 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Metadata and integer-exact runs must match bit for bit; floating-point outputs
+must meet max|y_gpu - y_ref| <= 1e-2 * rms(y_ref) + 1e-3 on top of the half
+ulp of the bf16 output (the reading of the tolerance for a bf16 output), and
+the shrink's fp32 projection the same bound without the rounding term.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import segmented_rank_gemm_amd as srg
+from tests import gpu_harness as H
+from workloads import (CONFIGS, make_custom_workload, make_fuzz_mapping,
+                       make_integer_exact_workload, make_mapping, make_workload)
+
+pytestmark = pytest.mark.gpu
+
+META_KEYS = ["sorted_token_ids", "active_lora_ids", "num_tokens_per_lora", "lora_token_start",
+             "num_active"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the GPU tests need a visible MI355X"
+    arch = torch.cuda.get_device_properties(0).gcnArchName
+    assert arch.startswith("gfx950"), arch
+    yield
+    torch.cuda.synchronize()
+
+
+def _sanitize(mapping, L):
+    m = np.asarray(mapping, dtype=np.int64)
+    return np.where((m >= -1) & (m < L), m, -1)
+
+
+def _check_meta(meta_gpu, ref, T, max_tokens, sorted_fill=-7):
+    assert np.array_equal(meta_gpu["sorted_token_ids"][:T], ref["sorted_token_ids"])
+    assert np.all(meta_gpu["sorted_token_ids"][T:max_tokens] == sorted_fill)
+    for k in META_KEYS[1:]:
+        assert np.array_equal(meta_gpu[k], ref[k]), k
+
+
+def _run_metadata(mapping, T, max_tokens, L):
+    meta = srg.LoraMeta(max_tokens, L)
+    meta.sorted_token_ids.fill_(-7)
+    for t in meta.tensors()[1:]:
+        t.fill_(-99)
+    m = torch.from_numpy(np.ascontiguousarray(mapping, dtype=np.int32)).cuda()
+    srg.lora_prepare_metadata(m, T, meta)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in zip(META_KEYS, meta.tensors())}
+
+
+# ------------------------------------------------------------------ metadata
+
+@pytest.mark.parametrize("cfg", range(len(CONFIGS)))
+def test_metadata_bit_exact_full_size(cfg):
+    mapping = make_mapping(cfg)
+    T = mapping.shape[0]
+    L = CONFIGS[cfg]["max_loras"]
+    got = _run_metadata(mapping, T, T + 37, L)
+    _check_meta(got, oracle.prepare_metadata(mapping, L), T, T + 37)
+
+
+FUZZ = [(0, 1, 1, "wild"), (0, 64, 8, "wild"), (1, 1, 1, "single"), (1, 5, 256, "wild"),
+        (63, 64, 3, "runs"), (64, 64, 2, "wild"), (65, 100, 4, "extreme"), (1023, 1024, 16, "wild"),
+        (1024, 1024, 64, "all_none"), (1025, 3000, 64, "runs"), (3000, 3000, 1, "wild"),
+        (4097, 5000, 256, "wild"), (8192, 8192, 4, "runs"), (20000, 20000, 256, "extreme"),
+        (65536, 70000, 33, "wild"), (777, 777, 255, "single")]
+
+
+@pytest.mark.parametrize("T,maxT,L,kind", FUZZ)
+def test_metadata_bit_exact_fuzz(T, maxT, L, kind):
+    rng = np.random.default_rng(T * 7 + L)
+    mapping = make_fuzz_mapping(rng, T, L, kind)
+    got = _run_metadata(mapping, T, maxT, L)
+    _check_meta(got, oracle.prepare_metadata(mapping, L), T, maxT)
+
+
+# --------------------------------------------------------- shrink + expand
+
+def _full_check(w, d, literal=False):
+    T = w.num_tokens
+    ref = oracle.run_step(w)
+    _check_meta(H.meta_host(d), ref, T, w.max_tokens)
+    ids = _sanitize(w.mapping, w.max_loras)
+    act = ids >= 0
+    # shrink: sum of the parts against the fp64 projection (rows with an adapter)
+    bs = H.buf_sum(d)[:, :T]
+    if act.any():
+        b64 = ref["buf"][:, act]
+        brms = float(np.sqrt(np.mean(b64 * b64)))
+        berr = float(np.max(np.abs(bs[:, act] - b64)))
+        assert berr <= 1e-2 * brms + 1e-3, (berr, brms)
+    # expand
+    yg = H.from_dev_bf16(d.y)
+    rep = H.y_report(yg[:T, :w.n_total], ref["y64"][:, :w.n_total],
+                     ref["y_bf16"][:, :w.n_total])
+    assert rep["max_excess_over_half_ulp"] <= rep["tol"], rep
+    # rows without an adapter untouched, bit for bit; so are pad columns and rows >= T
+    assert np.array_equal(yg[:T][~act, :w.n_total], w.y0[:T][~act])
+    assert np.all(yg[:, w.n_total:] == 0x7FC1)
+    if w.max_tokens > T:
+        assert np.array_equal(yg[T:w.max_tokens, :w.n_total], w.y0[T:w.max_tokens])
+    # buf rows of tokens without an adapter keep their fill (NaN), in every part
+    braw = d.buf.cpu().numpy()
+    assert np.all(np.isnan(braw[:, :, :T][:, :, ~act]))
+    if literal:
+        print(f"\n[{w.name}] T={T} tol={rep['tol']:.4g} max_excess={rep['max_excess_over_half_ulp']:.3g} "
+              f"literal_over_tol(y64)={rep['literal_over_tol_vs_y64']} "
+              f"literal_over_tol(rne)={rep['literal_over_tol_vs_rne']} "
+              f"ulp_mismatch(rne)={rep['ulp_mismatch_vs_rne']}/{rep['n']}", flush=True)
+    return rep
+
+
+REDUCED_T = [16, 200, 1000, 700, 900]
+
+
+@pytest.mark.parametrize("cfg", range(len(CONFIGS)))
+@pytest.mark.parametrize("splits", ["default", 1, 3])
+def test_step_parity_reduced(cfg, splits):
+    w = make_workload(cfg, num_tokens=REDUCED_T[cfg], max_tokens=REDUCED_T[cfg] + 19)
+    d = H.upload(w, num_splits=None if splits == "default" else splits, ldy_pad=8)
+    H.run_step(d)
+    torch.cuda.synchronize()
+    _full_check(w, d)
+
+
+@pytest.mark.parametrize("cfg", range(len(CONFIGS)))
+def test_step_parity_full_size(cfg):
+    # full sizes, default number of parts: the launch configuration the benchmark times
+    w = make_workload(cfg)
+    d = H.upload(w)
+    H.run_step(d)
+    torch.cuda.synchronize()
+    _full_check(w, d, literal=True)
+
+
+@pytest.mark.parametrize("rank", [8, 16, 32, 64])
+@pytest.mark.parametrize("splits", [1, 5])
+def test_integer_exact_bitwise(rank, splits):
+    w = make_integer_exact_workload(100 + rank, 300, 328, [136, 40, 8], rank, 6,
+                                    scale=2.0 if rank == 16 else 1.0)
+    d = H.upload(w, num_splits=splits)
+    H.run_step(d)
+    torch.cuda.synchronize()
+    ref = oracle.run_step(w)
+    yg = H.from_dev_bf16(d.y)[:, :w.n_total]
+    assert np.array_equal(yg, ref["y_bf16"])
+    act = _sanitize(w.mapping, w.max_loras) >= 0
+    assert np.array_equal(H.buf_sum(d)[:, act], ref["buf"][:, act])
+
+
+SHAPES = [
+    # (T, maxT, hidden, slices, rank, L, ldx_pad, ldy_pad, splits)
+    (37, 40, 72, [8], 8, 1, 0, 0, 1),
+    (130, 130, 264, [40, 136], 16, 3, 8, 16, 3),
+    (257, 300, 1032, [128, 8, 24, 200], 32, 5, 0, 8, 64),
+    (96, 96, 512, [64, 64, 64], 64, 2, 16, 0, 2),
+    (500, 512, 2048, [1024], 64, 256, 0, 0, 4),
+    (33, 33, 128, [16, 16, 16, 16], 8, 7, 0, 0, 7),
+]
+
+
+@pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,ldx_pad,ldy_pad,splits", SHAPES)
+def test_shape_sweep(T, maxT, hidden, slices, rank, L, ldx_pad, ldy_pad, splits):
+    rng = np.random.default_rng(T + hidden)
+    mapping = rng.integers(-2, L + 1, size=T)
+    w = make_custom_workload(T, T, hidden, slices, rank, L, 0.5, mapping, max_tokens=maxT)
+    d = H.upload(w, num_splits=splits, ldx_pad=ldx_pad, ldy_pad=ldy_pad)
+    H.run_step(d)
+    torch.cuda.synchronize()
+    _full_check(w, d)
+
+
+@pytest.mark.parametrize("kind", ["empty", "all_none", "single", "one_token"])
+def test_degenerate_batches(kind):
+    T = {"empty": 0, "all_none": 50, "single": 80, "one_token": 1}[kind]
+    mapping = {"empty": np.zeros(0), "all_none": np.full(50, -1), "single": np.full(80, 2),
+               "one_token": np.array([1])}[kind]
+    w = make_custom_workload(9, T, 256, [64, 32], 16, 3, 1.0, mapping, max_tokens=max(T, 1) + 5)
+    d = H.upload(w, ldy_pad=8)
+    H.run_step(d)
+    torch.cuda.synchronize()
+    yg = H.from_dev_bf16(d.y)
+    if kind in ("empty", "all_none"):
+        assert np.array_equal(yg[:, :w.n_total], w.y0[:w.max_tokens])
+        assert int(d.meta.num_active.item()) == 0
+    else:
+        _full_check(w, d)
+
+
+def test_inputs_never_written():
+    w = make_workload(0, num_tokens=16, max_tokens=24)
+    d = H.upload(w)
+    before = [t.clone() for t in [d.mapping, d.x, *d.lora_a, *d.lora_b]]
+    H.run_step(d)
+    torch.cuda.synchronize()
+    for a, b in zip(before, [d.mapping, d.x, *d.lora_a, *d.lora_b]):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+def test_bitwise_deterministic():
+    w = make_workload(4, num_tokens=900)
+    outs = []
+    for _ in range(3):
+        d = H.upload(w)
+        H.run_step(d)
+        torch.cuda.synchronize()
+        outs.append((H.from_dev_bf16(d.y), d.buf.cpu().numpy().view(np.uint32)))
+    for y, b in outs[1:]:
+        assert np.array_equal(y, outs[0][0])
+        assert np.array_equal(b, outs[0][1])
+
+
+def test_token_permutation_permutes_rows():
+    w = make_workload(3, num_tokens=300)
+    d = H.upload(w)
+    H.run_step(d)
+    perm = np.random.default_rng(3).permutation(w.num_tokens)
+    w2 = make_custom_workload(0, w.num_tokens, w.hidden, w.slices, w.rank, w.max_loras, w.scale,
+                              w.mapping[perm])
+    w2.x, w2.y0, w2.lora_a, w2.lora_b = w.x[perm], w.y0[perm], w.lora_a, w.lora_b
+    d2 = H.upload(w2, num_splits=d.num_splits)
+    H.run_step(d2)
+    torch.cuda.synchronize()
+    assert np.array_equal(H.from_dev_bf16(d2.y), H.from_dev_bf16(d.y)[perm])
+
+
+def test_graph_replay_matches_eager():
+    w = make_workload(1, num_tokens=256)
+    d = H.upload(w)
+    y0 = d.y.clone()
+    H.run_step(d)
+    torch.cuda.synchronize()
+    eager = H.from_dev_bf16(d.y)
+
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    d.y.copy_(y0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        H.run_step(d, stream=torch.cuda.current_stream())
+    for _ in range(4):
+        d.y.copy_(y0)          # eager reset between replays, outside the graph
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(H.from_dev_bf16(d.y), eager)

@@ -14,5 +14,6 @@ from .gen import (  # noqa: F401
     make_integer_exact_workload,
     make_custom_workload,
     make_fuzz_mapping,
+    make_mapping,
     workload_stats,
 )

@@ -201,6 +201,16 @@ def make_workload(index: int, seed: Optional[int] = None, num_tokens: Optional[i
                     mapping, x, lora_a, lora_b, y0)
 
 
+def make_mapping(index: int, seed: Optional[int] = None,
+                 num_tokens: Optional[int] = None) -> np.ndarray:
+    """Only the adapter map of workload ``index`` (identical to the one
+    ``make_workload`` draws with the same seed and size: it is the first draw)."""
+    cfg = CONFIGS[index]
+    rng = np.random.default_rng(index if seed is None else seed)
+    T = cfg["num_tokens"] if num_tokens is None else int(num_tokens)
+    return _draw_mapping(rng, T, cfg["ids"])
+
+
 def make_custom_workload(seed: int, num_tokens: int, hidden: int, slices: List[int], rank: int,
                          max_loras: int, scale: float, mapping: np.ndarray,
                          max_tokens: Optional[int] = None, name: str = "custom") -> Workload:
