@@ -22,13 +22,27 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 
+// Every buffer of the path lives in device global memory: say so, so that
+// pointers that went through LDS or a select still compile to global_* (not
+// flat_*) instructions.
+#define LORA_GLOBAL __attribute__((address_space(1)))
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+  return *(const LORA_GLOBAL u32x4*)(p);
 }
 __device__ __forceinline__ u32x2 load8(const void* p) {
-  return *reinterpret_cast<const u32x2*>(p);
+  return *(const LORA_GLOBAL u32x2*)(p);
 }
-__device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void store16(void* p, u32x4 v) { *(LORA_GLOBAL u32x4*)(p) = v; }
+
+// Streamed data touched once (the y rows): non-temporal hint, so it does not
+// displace the adapter weights that every tile re-reads from L2.
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load((const LORA_GLOBAL u32x4*)(p));
+}
+__device__ __forceinline__ void store16_stream(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, (LORA_GLOBAL u32x4*)(p));
+}
 
 // Low / high bf16 of a packed pair, widened exactly to fp32.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -82,25 +96,36 @@ __device__ void build_segment_table(SegmentTable& tab, const int32_t* __restrict
                                     int max_tokens) {
   if (threadIdx.x < kWave) {
     const int lane = lane_id();
+    // Every slot array is written in full by the metadata step, so all loads
+    // go out together with the slot count: one round trip.
     int na = *num_active;
+    int cnt0 = 0, st0 = 0, id0 = 0;
+    if (lane < max_loras) {
+      cnt0 = counts[lane];
+      st0 = starts[lane];
+      id0 = active_ids[lane];
+    }
     na = na < 0 ? 0 : (na > max_loras ? max_loras : na);
     int carry = 0;
     for (int base = 0; base < na; base += kWave) {
       const int i = base + lane;
-      int cnt = 0, st = 0, id = 0;
-      if (i < na) {
-        cnt = counts[i];
-        st = starts[i];
-        id = active_ids[i];
-        const bool ok = id >= 0 && id < max_loras && cnt > 0 && st >= 0 && st <= max_tokens &&
-                        cnt <= max_tokens - st;
-        if (!ok) cnt = 0;
+      int cnt = cnt0, st = st0, id = id0;
+      if (base > 0) {
+        cnt = 0;
+        if (i < na) {
+          cnt = counts[i];
+          st = starts[i];
+          id = active_ids[i];
+        }
       }
+      const bool ok = i < na && id >= 0 && id < max_loras && cnt > 0 && st >= 0 &&
+                      st <= max_tokens && cnt <= max_tokens - st;
+      if (!ok) cnt = 0;
       const int incl = wave_inclusive_scan((cnt + TILE - 1) / TILE);
       if (i < na) {
         tab.start[i] = st;
         tab.count[i] = cnt;
-        tab.lora[i] = id;
+        tab.lora[i] = ok ? id : 0;
         tab.tile_end[i] = carry + incl;
       }
       carry += __shfl(incl, kWave - 1, kWave);
@@ -145,11 +170,59 @@ __device__ __forceinline__ Tile resolve_tile(const SegmentTable& tab, int m) {
   return t;
 }
 
-// Token index at grouped position `pos`, or -1 if outside [0, max_tokens).
-__device__ __forceinline__ int token_at(const int32_t* __restrict__ sorted, int pos,
-                                        int max_tokens) {
-  const int t = sorted[pos];
-  return (t >= 0 && t < max_tokens) ? t : -1;
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2),
+// so workgroup b runs on XCD b % 8.  Unit streams are remapped so that each XCD
+// takes one contiguous run of the natural unit order (consecutive tiles of one
+// adapter, sharing its weights in that XCD's L2): workgroup b walks units
+// xcd * per_xcd + slot, + slots_per_xcd, ... within its XCD's run.
+constexpr int kXcds = 8;
+
+struct XcdWalk {
+  int next;  // next unit index, or >= end when done
+  int end;
+  int step;
+};
+
+__device__ __forceinline__ XcdWalk xcd_walk(int units, int grid) {
+  const int b = blockIdx.x;
+  const int xcd = b % kXcds;
+  const int slot = b / kXcds;
+  const int per_xcd = (units + kXcds - 1) / kXcds;
+  const int slots = grid / kXcds;  // grid is a multiple of kXcds
+  XcdWalk w;
+  w.next = xcd * per_xcd + slot;
+  w.end = min(units, (xcd + 1) * per_xcd);
+  w.step = slots;
+  return w;
+}
+
+// Loads below are issued unconditionally from addresses that are always valid
+// (masked lanes are pointed at a clamped, in-bounds location) and masked
+// afterwards.  A load inside a branch would force a wait for it at the branch's
+// join; unconditional loads let every load of a step be in flight together.
+
+// Token index of row `r` of a tile (grouped positions first .. first+rows-1),
+// or -1 for rows past the tile or an index outside [0, max_tokens).  rows >= 1.
+__device__ __forceinline__ int tile_token(const int32_t* __restrict__ sorted, int first, int rows,
+                                          int r, int max_tokens) {
+  const int t = sorted[first + (r < rows ? r : rows - 1)];
+  return (r < rows && t >= 0 && t < max_tokens) ? t : -1;
+}
+
+// All-ones or all-zeros, hidden from the optimizer (an empty asm with a VGPR
+// operand, no instruction): `v & mask` then cannot be turned back into a load
+// under a branch, which would wait for the load at the branch's join.
+__device__ __forceinline__ uint32_t opaque_mask(bool keep) {
+  uint32_t m = keep ? 0xFFFFFFFFu : 0u;
+  asm volatile("" : "+v"(m));
+  return m;
+}
+__device__ __forceinline__ u32x4 masked(u32x4 v, bool keep) { return v & opaque_mask(keep); }
+__device__ __forceinline__ u32x2 masked(u32x2 v, bool keep) { return v & opaque_mask(keep); }
+
+// Index of this thread's wave in the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
 }
 
 }  // namespace lora

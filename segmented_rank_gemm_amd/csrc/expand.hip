@@ -24,6 +24,10 @@
 
 #include "device_common.hpp"
 
+#ifdef LORA_TUNING
+#include <cstdlib>
+#endif
+
 namespace lora {
 
 constexpr int kExpandThreads = 256;
@@ -67,23 +71,53 @@ struct RankOperand {
   bf16x8 op[RANK / 16];
 };
 
+// One chunk of one 16-token block: y of tokens 4*grp..4*grp+3, 8 columns each.
+struct YBlock {
+  u32x4 v[4];
+};
+
+// B operand of one 128-column chunk: block b, MFMA step q.
 template <int RANK>
+struct BChunk;
+template <>
+struct BChunk<8> {
+  u32x2 w[8][1];
+};
+template <int RANK>
+struct BChunk {
+  u32x4 w[8][RANK / 16];
+};
+
+// MW = 16-token blocks per tile; every block shares the B operand loads.
+//
+// A workgroup unit is (tile of 16*MW tokens of one adapter, slice s, column
+// range of 4*cpr chunks); wave w takes chunks w, w+4, ... of the range, so the
+// four waves stream neighbouring columns together.  The rank operand of the
+// tile (sum over the shrink's parts, split hi/lo, already in MFMA operand
+// layout) is built once per unit into LDS and shared by the four waves.
+template <int RANK, int MW>
 __global__ __launch_bounds__(kExpandThreads) void expand_kernel(ExpandParams p) {
+  constexpr int kTile = 16 * MW;
+  constexpr int kSteps = RankOperand<RANK>::kSteps;
+  constexpr int kOpWords = RANK == 8 ? 2 : 4;  // 32-bit words per lane per MFMA step
   __shared__ SegmentTable tab;
-  build_segment_table<kExpandTile>(tab, p.active_ids, p.counts, p.starts, p.num_active,
-                                   p.max_loras, p.max_tokens);
+  __shared__ uint32_t a_lds[MW][kSteps][kOpWords][kWave];
+  build_segment_table<kTile>(tab, p.active_ids, p.counts, p.starts, p.num_active, p.max_loras,
+                             p.max_tokens);
   const int num_tiles = tab.num_tiles;
   const int ranges = p.range_end[p.num_slices - 1];
   const int units = num_tiles * ranges;
 
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
+  const int wave = wave_index();
   const int c = lane & 15;   // MFMA row (token) for the buf operand, column for B / D
   const int grp = lane >> 4;
   const int khalf = grp & 1;  // which half of each 16-rank (or 8-rank) group
   const bool use_lo = grp >= 2;
+  const int cpr = p.chunks_per_range;
 
-  for (int u = blockIdx.x * kExpandWaves + wave; u < units; u += gridDim.x * kExpandWaves) {
+  for (XcdWalk walk = xcd_walk(units, gridDim.x); walk.next < walk.end; walk.next += walk.step) {
+    const int u = walk.next;
     const int m = u % num_tiles;
     const int cr = u / num_tiles;
     int s = 0;
@@ -100,120 +134,190 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(ExpandParams p) 
         bslice = p.b[i];
       }
     }
-    const int chunk_begin = (cr - r_before) * p.chunks_per_range;
     const int chunks_s = (n_s + kExpandCols - 1) / kExpandCols;
-    const int chunk_end = min(chunks_s, chunk_begin + p.chunks_per_range);
+    const int range_begin = (cr - r_before) * cpr * kExpandWaves;
+    const int range_end = min(chunks_s, range_begin + cpr * kExpandWaves);
+    const int ch0 = range_begin + wave;  // this wave's chunks: ch0, ch0 + 4, ...
+    const Tile tile = resolve_tile<kTile>(tab, m);
+    const uint16_t* bmat = bslice + static_cast<int64_t>(tile.lora) * n_s * RANK;
 
-    const Tile tile = resolve_tile<kExpandTile>(tab, m);
+    // Loads are unconditional and never masked here: a lane whose row is past
+    // the tile (or whose column is past the slice) reads a clamped, valid
+    // location, and its results are simply not stored; the matrix-core rows of
+    // such a token, and the columns of such a column, touch nothing else.
 
-    // Rank operand: token c of the tile, fp32 sum over the shrink's parts.
-    RankOperand<RANK> a;
-    {
-      const int ta = c < tile.rows ? token_at(p.sorted, tile.first + c, p.max_tokens) : -1;
-      constexpr int kPer = RANK == 8 ? 4 : 8;  // ranks per lane per MFMA
+    // B operand of a chunk: depends on the adapter and the columns only.
+    auto load_b = [&](int ch, BChunk<RANK>& bc) {
+      const int col = ch * kExpandCols + 8 * c;
+      const int colc = col < n_s ? col : n_s - 8;  // n_s is a multiple of 8
 #pragma unroll
-      for (int q = 0; q < RankOperand<RANK>::kSteps; ++q) {
+      for (int b = 0; b < 8; ++b) {
+        const uint16_t* brow = bmat + static_cast<int64_t>(colc + b) * RANK;
+        if constexpr (RANK == 8) {
+          bc.w[b][0] = load8(brow + 4 * khalf);
+        } else {
+#pragma unroll
+          for (int q = 0; q < kSteps; ++q) bc.w[b][q] = load16(brow + 16 * q + 8 * khalf);
+        }
+      }
+    };
+    BChunk<RANK> bcur, bnext;
+    if (ch0 < range_end) load_b(ch0, bcur);
+
+    // Output rows of this lane in every block: 4*grp + j; the rank-operand
+    // rows are c (+16 per block).
+    int td[MW][4], ta[MW];
+#pragma unroll
+    for (int mb = 0; mb < MW; ++mb) {
+      ta[mb] = tile_token(p.sorted, tile.first, tile.rows, 16 * mb + c, p.max_tokens);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        td[mb][j] = tile_token(p.sorted, tile.first, tile.rows, 16 * mb + 4 * grp + j, p.max_tokens);
+    }
+    const int t_first = tile_token(p.sorted, tile.first, tile.rows, 0, p.max_tokens);
+    const int t_safe = t_first >= 0 ? t_first : 0;
+    int64_t yrow[MW][4];
+#pragma unroll
+    for (int mb = 0; mb < MW; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        yrow[mb][j] = static_cast<int64_t>(td[mb][j] >= 0 ? td[mb][j] : t_safe) * p.ldy + off_s;
+
+    auto load_y = [&](int ch, YBlock (&yb)[MW]) {
+      const int col = ch * kExpandCols + 8 * c;
+      const int colc = col < n_s ? col : n_s - 8;
+#pragma unroll
+      for (int mb = 0; mb < MW; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yb[mb].v[j] = load16_stream(p.y + yrow[mb][j] + colc);
+    };
+    YBlock ycur[MW], ynext[MW];
+    if (ch0 < range_end) load_y(ch0, ycur);
+
+    // Rank operand, built cooperatively: item (mb, q) is one MFMA step of one
+    // block, i.e. one register set of the wave; its lane (c, grp) sums the
+    // parts of ranks [k0, k0 + kPer) of token row c.  Parts go in groups of 8
+    // whose loads are all issued before the first add; the adds run in part
+    // order.  Part slots past the last re-read the group's first and are masked.
+    {
+      constexpr int kPer = RANK == 8 ? 4 : 8;
+      const int64_t plane = static_cast<int64_t>(p.num_slices) * p.max_tokens * RANK;
+      for (int item = wave; item < MW * kSteps; item += kExpandWaves) {
+        const int mb = item / kSteps;
+        const int q = item - mb * kSteps;
+        const int k0 = RANK == 8 ? 4 * khalf : 16 * q + 8 * khalf;
+        const int trow = ta[mb] >= 0 ? ta[mb] : t_safe;
+        const float* src0 = p.buf + (static_cast<int64_t>(s) * p.max_tokens + trow) * RANK + k0;
         float v[kPer];
 #pragma unroll
         for (int e = 0; e < kPer; ++e) v[e] = 0.f;
-        if (ta >= 0) {
-          const int k0 = RANK == 8 ? 4 * khalf : 16 * q + 8 * khalf;
-          for (int sp = 0; sp < p.num_splits; ++sp) {
-            const float* src = p.buf + ((static_cast<int64_t>(sp) * p.num_slices + s) * p.max_tokens + ta) *
-                                           RANK + k0;
+        for (int sp0 = 0; sp0 < p.num_splits; sp0 += 8) {
+          uint32_t pm[8];
 #pragma unroll
-            for (int e4 = 0; e4 < kPer; e4 += 4) {
-              const f32x4 w = __builtin_bit_cast(f32x4, load16(src + e4));
-              v[e4 + 0] += w[0];
-              v[e4 + 1] += w[1];
-              v[e4 + 2] += w[2];
-              v[e4 + 3] += w[3];
-            }
+          for (int i = 0; i < 8; ++i) pm[i] = opaque_mask(sp0 + i < p.num_splits);
+          u32x4 w[8][kPer / 4];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int sp = sp0 + i < p.num_splits ? sp0 + i : sp0;
+#pragma unroll
+            for (int e4 = 0; e4 < kPer / 4; ++e4) w[i][e4] = load16(src0 + sp * plane + 4 * e4);
           }
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e4 = 0; e4 < kPer / 4; ++e4)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[4 * e4 + e] += __uint_as_float(w[i][e4][e] & pm[i]);
         }
-        uint32_t packed[kPer / 2];
 #pragma unroll
         for (int e = 0; e < kPer; e += 2) {
           const uint32_t hi = pack_bf16x2(v[e], v[e + 1]);
-          if (use_lo) {
-            packed[e / 2] = pack_bf16x2(v[e] - bf16_lo(hi), v[e + 1] - bf16_hi(hi));
-          } else {
-            packed[e / 2] = hi;
+          a_lds[mb][q][e / 2][lane] =
+              use_lo ? pack_bf16x2(v[e] - bf16_lo(hi), v[e + 1] - bf16_hi(hi)) : hi;
+        }
+      }
+    }
+    __syncthreads();
+    RankOperand<RANK> a[MW];
+#pragma unroll
+    for (int mb = 0; mb < MW; ++mb)
+#pragma unroll
+      for (int q = 0; q < kSteps; ++q) {
+        if constexpr (RANK == 8) {
+          a[mb].op[q] = __builtin_bit_cast(i16x4, u32x2{a_lds[mb][q][0][lane], a_lds[mb][q][1][lane]});
+        } else {
+          a[mb].op[q] = __builtin_bit_cast(
+              bf16x8, u32x4{a_lds[mb][q][0][lane], a_lds[mb][q][1][lane], a_lds[mb][q][2][lane],
+                            a_lds[mb][q][3][lane]});
+        }
+      }
+    __syncthreads();  // the next unit may overwrite a_lds
+
+    for (int ch = ch0; ch < range_end; ch += kExpandWaves) {
+      const bool more = ch + kExpandWaves < range_end;
+      if (more) {
+        load_y(ch + kExpandWaves, ynext);
+        if constexpr (RANK <= 32) load_b(ch + kExpandWaves, bnext);
+      }
+      const int col = ch * kExpandCols + 8 * c;  // first of this lane's 8 columns
+      const bool col_ok = col < n_s;
+
+#pragma unroll
+      for (int mb = 0; mb < MW; ++mb) {
+        if (16 * mb >= tile.rows) break;  // wave-uniform: empty block
+        f32x4 acc[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t w = ycur[mb].v[j][b >> 1];
+            acc[b][j] = (b & 1) ? bf16_hi(w) : bf16_lo(w);
           }
         }
-        if constexpr (RANK == 8) {
-          a.op[q] = __builtin_bit_cast(i16x4, u32x2{packed[0], packed[1]});
-        } else {
-          a.op[q] = __builtin_bit_cast(bf16x8, u32x4{packed[0], packed[1], packed[2], packed[3]});
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+#pragma unroll
+          for (int q = 0; q < kSteps; ++q) {
+            if constexpr (RANK == 8) {
+              acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                  a[mb].op[q], __builtin_bit_cast(i16x4, bcur.w[b][0]), acc[b], 0, 0, 0);
+            } else {
+              acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  a[mb].op[q], __builtin_bit_cast(bf16x8, bcur.w[b][q]), acc[b], 0, 0, 0);
+            }
+          }
         }
-      }
-    }
-
-    // Output tokens of this lane in the D layout: rows 4*grp + j.
-    int td[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * grp + j;
-      td[j] = r < tile.rows ? token_at(p.sorted, tile.first + r, p.max_tokens) : -1;
-    }
-    const uint16_t* bmat = bslice + static_cast<int64_t>(tile.lora) * n_s * RANK;
-
-    for (int ch = chunk_begin; ch < chunk_end; ++ch) {
-      const int col = ch * kExpandCols + 8 * c;  // first of this lane's 8 columns
-      const bool col_ok = col < n_s;             // n_s is a multiple of 8
-
-      u32x4 yv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        yv[j] = (col_ok && td[j] >= 0)
-                    ? load16(p.y + static_cast<int64_t>(td[j]) * p.ldy + off_s + col)
-                    : u32x4{0u, 0u, 0u, 0u};
-      }
-
-      f32x4 acc[8];
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t w = yv[j][b >> 1];
-          acc[b][j] = (b & 1) ? bf16_hi(w) : bf16_lo(w);
-        }
-      }
-
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const uint16_t* brow = bmat + static_cast<int64_t>(col + b) * RANK;
-#pragma unroll
-        for (int q = 0; q < RankOperand<RANK>::kSteps; ++q) {
-          if constexpr (RANK == 8) {
-            const u32x2 bw = col_ok ? load8(brow + 4 * khalf) : u32x2{0u, 0u};
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                a.op[q], __builtin_bit_cast(i16x4, bw), acc[b], 0, 0, 0);
-          } else {
-            const u32x4 bw = col_ok ? load16(brow + 16 * q + 8 * khalf) : u32x4{0u, 0u, 0u, 0u};
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                a.op[q], __builtin_bit_cast(bf16x8, bw), acc[b], 0, 0, 0);
+          if (col_ok && td[mb][j] >= 0) {
+            const u32x4 out = {pack_bf16x2(acc[0][j], acc[1][j]), pack_bf16x2(acc[2][j], acc[3][j]),
+                               pack_bf16x2(acc[4][j], acc[5][j]), pack_bf16x2(acc[6][j], acc[7][j])};
+            store16_stream(p.y + yrow[mb][j] + col, out);
           }
         }
       }
-
+      if (more) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (col_ok && td[j] >= 0) {
-          const u32x4 out = {pack_bf16x2(acc[0][j], acc[1][j]), pack_bf16x2(acc[2][j], acc[3][j]),
-                             pack_bf16x2(acc[4][j], acc[5][j]), pack_bf16x2(acc[6][j], acc[7][j])};
-          store16(p.y + static_cast<int64_t>(td[j]) * p.ldy + off_s + col, out);
+        for (int mb = 0; mb < MW; ++mb) ycur[mb] = ynext[mb];
+        if constexpr (RANK <= 32) {
+          bcur = bnext;
+        } else {
+          load_b(ch + kExpandWaves, bcur);
         }
       }
     }
   }
 }
 
-template <int RANK>
+template <int RANK, int MW>
 hipError_t launch_expand_rank(const ExpandParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(expand_kernel<RANK>, dim3(grid), dim3(kExpandThreads), 0, stream, p);
+  hipLaunchKernelGGL((expand_kernel<RANK, MW>), dim3(grid), dim3(kExpandThreads), 0, stream, p);
   return hipGetLastError();
 }
+
+// 16-token blocks per wave unit: two for rank >= 32, where the B operand of a
+// chunk (128 columns x rank) outweighs the y bytes of one block.
+int expand_tile_blocks(int rank) { return rank >= 32 ? 2 : 1; }
 
 hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const* lora_b,
                          const int32_t* slice_sizes, int num_slices, int rank, uint16_t* y,
@@ -238,17 +342,26 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
       p.off[s] = off;
     }
   }
-  // Chunks per wave unit: enough units to give every CU ~16 waves at the
-  // largest batch, but at most 8 chunks so a unit stays a short stream.
-  const int64_t tiles = (static_cast<int64_t>(max_tokens) + kExpandTile - 1) / kExpandTile + max_loras;
-  int64_t cpr = tiles * total_chunks / (static_cast<int64_t>(num_cus) * 16);
+  // Chunks per wave in a workgroup unit (the unit spans 4x as many): at least
+  // rank/16, so that building the rank operand (which reads rank floats per
+  // token and part) stays small next to the y bytes of the unit; more when the
+  // batch is large enough to still give every CU ~32 units; at most 8.
+  const int mw = expand_tile_blocks(rank);
+  const int64_t tiles =
+      (static_cast<int64_t>(max_tokens) + kExpandTile * mw - 1) / (kExpandTile * mw) + max_loras;
+  int64_t cpr = tiles * total_chunks / (static_cast<int64_t>(num_cus) * 32);
+  cpr = cpr > rank / 16 ? cpr : rank / 16;
   cpr = cpr < 1 ? 1 : (cpr > 8 ? 8 : cpr);
+#ifdef LORA_TUNING
+  if (const char* e = getenv("LORA_EXPAND_CPR")) cpr = atoi(e);
+#endif
   p.chunks_per_range = static_cast<int>(cpr);
+  const int per_unit = p.chunks_per_range * kExpandWaves;
   int ranges = 0;
   for (int s = 0; s < LORA_MAX_SLICES; ++s) {
     if (s < num_slices) {
       const int chunks = (slice_sizes[s] + kExpandCols - 1) / kExpandCols;
-      ranges += (chunks + p.chunks_per_range - 1) / p.chunks_per_range;
+      ranges += (chunks + per_unit - 1) / per_unit;
     }
     p.range_end[s] = ranges;
   }
@@ -262,16 +375,15 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
   p.max_tokens = max_tokens;
   p.max_loras = max_loras;
 
-  const int64_t wave_units = tiles * ranges;
-  int64_t grid = (wave_units + kExpandWaves - 1) / kExpandWaves;
-  const int64_t cap = static_cast<int64_t>(num_cus) * 16;
+  int64_t grid = tiles * ranges;
+  const int64_t cap = static_cast<int64_t>(num_cus) * 8;
   grid = grid < cap ? grid : cap;
-  grid = grid < 1 ? 1 : grid;
+  grid = (grid + kXcds - 1) / kXcds * kXcds;  // whole rounds over the XCDs
   switch (rank) {
-    case 8: return launch_expand_rank<8>(p, static_cast<int>(grid), stream);
-    case 16: return launch_expand_rank<16>(p, static_cast<int>(grid), stream);
-    case 32: return launch_expand_rank<32>(p, static_cast<int>(grid), stream);
-    default: return launch_expand_rank<64>(p, static_cast<int>(grid), stream);
+    case 8: return launch_expand_rank<8, 1>(p, static_cast<int>(grid), stream);
+    case 16: return launch_expand_rank<16, 1>(p, static_cast<int>(grid), stream);
+    case 32: return launch_expand_rank<32, 2>(p, static_cast<int>(grid), stream);
+    default: return launch_expand_rank<64, 2>(p, static_cast<int>(grid), stream);
   }
 }
 

@@ -23,6 +23,8 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
                          int num_cus, hipStream_t stream);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int num_cus,
                               hipStream_t stream);
+int shrink_group_blocks(int nb_total);
+int shrink_tile_blocks(int max_tokens, int nb);
 }  // namespace lora
 
 namespace {
@@ -86,12 +88,20 @@ int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t m
   if (hidden < 8 || hidden > kMaxHidden || !sizes_ok(max_tokens, max_loras) || num_slices < 1 ||
       num_slices > LORA_MAX_SLICES || rank < 1 || rank > 64)
     return 0;
-  // Enough (tile, part) units for ~4 workgroups per CU of a 256-CU device at
-  // the largest batch, with parts no shorter than 512 hidden elements.
-  const int64_t tiles = (static_cast<int64_t>(max_tokens) + 15) / 16 + max_loras;
-  int64_t splits = (1024 + tiles - 1) / tiles;
-  const int64_t by_len = hidden / 512 > 0 ? hidden / 512 : 1;
+  // Enough (tile, part, output group) units for ~1 workgroup per CU of a
+  // 256-CU device at the largest batch, with parts of at least 256 hidden
+  // elements, and parts * rank <= 256 so that the expand, which sums the parts
+  // once per workgroup unit, reads at most 1 KB of them per token there.
+  const int nb_total = (num_slices * rank + 15) / 16;
+  const int nb = lora::shrink_group_blocks(nb_total);
+  const int64_t groups = (nb_total + nb - 1) / nb;
+  const int64_t tile = 16 * lora::shrink_tile_blocks(max_tokens, nb);
+  const int64_t tiles = (static_cast<int64_t>(max_tokens) + tile - 1) / tile + max_loras;
+  int64_t splits = (256 + tiles * groups - 1) / (tiles * groups);
+  const int64_t by_len = hidden / 256 > 0 ? hidden / 256 : 1;
+  const int64_t by_fold = 256 / rank > 0 ? 256 / rank : 1;
   splits = splits < by_len ? splits : by_len;
+  splits = splits < by_fold ? splits : by_fold;
   splits = splits < 1 ? 1 : (splits > LORA_MAX_SPLITS ? LORA_MAX_SPLITS : splits);
   return static_cast<int32_t>(splits);
 }

@@ -8,12 +8,15 @@
 // sized by the maximum token count, so the launch must be too.
 //
 // One workgroup per group (group 0 = no adapter, group g = adapter g-1), so the
-// grid is max_loras + 1 workgroups whatever the ids are.  Every workgroup
-// builds the full histogram in LDS (order-free counts), derives its group's
-// start and its slot among the adapters present, then walks the map in token
-// order and places its members with a ballot prefix count: position = start +
-// number of earlier members.  No workgroup depends on another and no global
-// atomic is used, so the result is the same bits on every run.
+// grid is max_loras + 1 workgroups whatever the ids are.  The map is walked in
+// blocks of kMetaBlock tokens, kPerThread consecutive tokens per thread, each
+// token read once.  For its group g a workgroup needs three things: how many
+// tokens sit in lower groups (its start), which groups occur at all (its slot
+// among the adapters present and, for group 0, how many there are), and, per
+// member, how many members precede it in token order (its rank).  Counts come
+// from per-thread tallies summed in a fixed order, occurrence from an LDS flag
+// per group, ranks from a block-wide exclusive scan of the per-thread member
+// counts; no global atomics, so the result is the same bits on every run.
 
 #include "device_common.hpp"
 
@@ -21,9 +24,42 @@ namespace lora {
 
 constexpr int kMetaThreads = 1024;
 constexpr int kMetaWaves = kMetaThreads / kWave;
+constexpr int kPerThread = 8;
+constexpr int kMetaBlock = kMetaThreads * kPerThread;
 
 __device__ __forceinline__ int group_of(int32_t id, int max_loras) {
   return (id >= -1 && id < max_loras) ? id + 1 : 0;
+}
+
+// Groups of this thread's kPerThread consecutive tokens starting at t0 (-1 past
+// the end of the batch).
+__device__ __forceinline__ void load_groups(const int32_t* __restrict__ mapping, int num_tokens,
+                                            int max_loras, int t0, int (&grp)[kPerThread]) {
+  if (t0 + kPerThread <= num_tokens && (reinterpret_cast<uintptr_t>(mapping + t0) & 15) == 0) {
+    const u32x4 a = load16(mapping + t0);
+    const u32x4 c = load16(mapping + t0 + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      grp[e] = group_of(static_cast<int32_t>(a[e]), max_loras);
+      grp[4 + e] = group_of(static_cast<int32_t>(c[e]), max_loras);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)
+      grp[e] = t0 + e < num_tokens ? group_of(mapping[t0 + e], max_loras) : -1;
+  }
+}
+
+// Block-wide sum of one int per thread, added in wave order.
+__device__ __forceinline__ int block_sum(int v, int* scratch) {
+  const int ws = wave_sum(v);
+  if (lane_id() == 0) scratch[threadIdx.x / kWave] = ws;
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kMetaWaves; ++w) total += scratch[w];
+  __syncthreads();
+  return total;
 }
 
 __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(
@@ -31,41 +67,47 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(
     int32_t* __restrict__ sorted, int32_t* __restrict__ active_ids,
     int32_t* __restrict__ counts, int32_t* __restrict__ starts,
     int32_t* __restrict__ num_active) {
-  __shared__ int hist[LORA_MAX_LORAS + 1];
-  __shared__ int wave_total[kMetaWaves];
-  __shared__ int s_start, s_slot, s_present;
+  __shared__ int present[LORA_MAX_LORAS + 1];
+  __shared__ int scratch[kMetaWaves];
+  __shared__ int s_slot, s_present;
 
   const int g = blockIdx.x;
   const int groups = max_loras + 1;
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-
-  for (int i = tid; i < groups; i += kMetaThreads) hist[i] = 0;
-  __syncthreads();
-  for (int t = tid; t < num_tokens; t += kMetaThreads) atomicAdd(&hist[group_of(mapping[t], max_loras)], 1);
+  for (int i = tid; i < groups; i += kMetaThreads) present[i] = 0;
   __syncthreads();
 
-  // Start of group g (tokens in lower groups), its slot among the adapters
-  // present (present adapters with a lower id), and the number present.
-  if (wave == 0) {
-    int below = 0, slot = 0, present = 0;
-    for (int base = 0; base < groups; base += kWave) {
-      const int i = base + lane;
-      const int h = i < groups ? hist[i] : 0;
-      below += wave_sum(i < g ? h : 0);
-      slot += __popcll(__ballot(i >= 1 && i < g && h > 0));
-      present += __popcll(__ballot(i >= 1 && i < groups && h > 0));
+  // Count pass: tokens in lower groups, members of g, occurring groups.
+  int grp[kPerThread];
+  int below = 0, members = 0;
+  for (int b0 = 0; b0 < num_tokens; b0 += kMetaBlock) {
+    load_groups(mapping, num_tokens, max_loras, b0 + tid * kPerThread, grp);
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      if (grp[e] >= 0) present[grp[e]] = 1;  // benign: every writer stores 1
+      below += (grp[e] >= 0 && grp[e] < g) ? 1 : 0;
+      members += grp[e] == g ? 1 : 0;
     }
-    if (lane == 0) {
-      s_start = below;
+  }
+  const int start = block_sum(below, scratch);
+  const int total = block_sum(members, scratch);
+
+  // Slot of g among the adapters present, and how many are present.
+  if (tid < kWave) {
+    int slot = 0, npresent = 0;
+    for (int base = 0; base < groups; base += kWave) {
+      const int i = base + tid;
+      const bool p = i >= 1 && i < groups && present[i] != 0;
+      slot += __popcll(__ballot(p && i < g));
+      npresent += __popcll(__ballot(p));
+    }
+    if (tid == 0) {
       s_slot = slot;
-      s_present = present;
+      s_present = npresent;
     }
   }
   __syncthreads();
 
-  const int members = hist[g];
   if (g == 0) {
     for (int i = s_present + tid; i < max_loras; i += kMetaThreads) {
       active_ids[i] = -1;
@@ -73,32 +115,43 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(
       starts[i] = num_tokens;
     }
     if (tid == 0) *num_active = s_present;
-  } else if (members > 0 && tid == 0) {
+  } else if (total > 0 && tid == 0) {
     active_ids[s_slot] = g - 1;
-    counts[s_slot] = members;
-    starts[s_slot] = s_start;
+    counts[s_slot] = total;
+    starts[s_slot] = start;
   }
-  if (members == 0) return;  // uniform across the workgroup
+  if (total == 0) return;  // uniform across the workgroup
 
-  const unsigned long long below_lane = (1ull << lane) - 1ull;
-  int base = s_start;
-  for (int c = 0; c < num_tokens; c += kMetaThreads) {
-    const int t = c + tid;
-    const bool mine = t < num_tokens && group_of(mapping[t], max_loras) == g;
-    const unsigned long long ballot = __ballot(mine);
-    if (lane == 0) wave_total[wave] = __popcll(ballot);
+  // Place pass: member rank = members in earlier blocks + exclusive scan of the
+  // per-thread member counts (thread order is token order within a block).  A
+  // batch of one block reuses the groups already in registers.
+  int placed = 0;
+  for (int b0 = 0; b0 < num_tokens; b0 += kMetaBlock) {
+    const int t0 = b0 + tid * kPerThread;
+    if (num_tokens > kMetaBlock) load_groups(mapping, num_tokens, max_loras, t0, grp);
+    int mine = 0;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) mine += grp[e] == g ? 1 : 0;
+    const int incl = wave_inclusive_scan(mine);
+    if (lane_id() == kWave - 1) scratch[tid / kWave] = incl;
     __syncthreads();
-    int before = 0, total = 0;
+    int before = 0, block_total = 0;
 #pragma unroll
     for (int w = 0; w < kMetaWaves; ++w) {
-      const int n = wave_total[w];
-      before += w < wave ? n : 0;
-      total += n;
+      const int n = scratch[w];
+      before += w < tid / kWave ? n : 0;
+      block_total += n;
     }
-    const int pos = base + before + __popcll(ballot & below_lane);
-    if (mine && pos < num_tokens) sorted[pos] = t;
-    base += total;
     __syncthreads();
+    int pos = start + placed + before + incl - mine;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      if (grp[e] == g) {
+        if (pos < num_tokens) sorted[pos] = t0 + e;
+        ++pos;
+      }
+    }
+    placed += block_total;
   }
 }
 

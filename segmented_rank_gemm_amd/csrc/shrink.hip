@@ -7,20 +7,26 @@
 // Serving", Overview: one launch covers every segment, each with its own
 // low-rank weights.
 //
-// gfx950 mapping.  A work unit is (tile of 16 grouped tokens of one adapter,
-// part p of the hidden dimension).  Each unit is a dense 16-token x (S*r)-output
-// contraction, computed on the matrix cores as D^T = A . x^T with
-// v_mfma_f32_16x16x32_bf16: the M dimension is the S*r outputs (blocks of 16),
-// N the 16 tokens, K the hidden dimension.  The sum over K is order-free, so
+// gfx950 mapping.  A work unit is (tile of 16*MW grouped tokens of one
+// adapter, part p of the hidden dimension).  Each unit is a dense
+// (16*MW)-token x (S*r)-output contraction, computed on the matrix cores as
+// D^T = A . x^T with v_mfma_f32_16x16x32_bf16: the M dimension is the S*r
+// outputs (blocks of 16), N the tokens (blocks of 16), K the hidden dimension.
+// Every wave holds all MW x NB accumulator blocks, so each 16-byte operand it
+// fetches feeds MW (or NB) matrix-core ops.  The sum over K is order-free, so
 // lane group g (lanes 16g..16g+15) feeds MFMA i of a 64-wide chunk with the
-// elements [16g + 8i, 16g + 8i + 8) of that chunk for BOTH operands: every lane
-// then reads 32 contiguous bytes of its token's x row and of its A row, the
-// four lane groups together one 128-byte line per row.  The four waves of a
+// elements [32i + 8g, 32i + 8g + 8) of that chunk for BOTH operands: one load
+// instruction covers 64 contiguous bytes of each of 16 rows, and the two
+// instructions of a row's 128-byte line are issued back to back.  The four waves of a
 // workgroup take interleaved chunks of the part and are summed through LDS in a
 // fixed order, so results are bit-identical run to run.  The grid is fixed by
 // the size arguments; workgroups stride over the units of the actual batch.
 
 #include "device_common.hpp"
+
+#ifdef LORA_TUNING
+#include <cstdlib>
+#endif
 
 namespace lora {
 
@@ -36,10 +42,12 @@ struct ShrinkParams {
   const uint16_t* a[LORA_MAX_SLICES];
   int num_slices;
   int rank;
+  int rank_shift;  // log2(rank)
   float scale;
   float* buf;
   int num_splits;
   int split_len;  // hidden elements per part, a multiple of kShrinkChunk
+  int num_groups; // output groups of up to NB 16-output blocks each
   const int32_t* sorted;
   const int32_t* active_ids;
   const int32_t* counts;
@@ -49,113 +57,216 @@ struct ShrinkParams {
   int max_loras;
 };
 
-__device__ __forceinline__ const uint16_t* slice_ptr(const ShrinkParams& p, int s) {
-  // select chain: per-lane slice index must not index the kernel-argument array
-  const uint16_t* r = p.a[0];
-  r = s == 1 ? p.a[1] : r;
-  r = s == 2 ? p.a[2] : r;
-  r = s == 3 ? p.a[3] : r;
-  return r;
-}
-
-// NB = number of 16-output blocks covering num_slices * rank outputs.
-template <int NB>
+// NB = number of 16-output blocks covering num_slices * rank outputs;
+// MW = 16-token blocks per tile, all held by every wave so that each A operand
+// fetched feeds MW matrix-core ops.
+template <int NB, int MW>
 __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) {
+  constexpr int kTile = 16 * MW;
   __shared__ SegmentTable tab;
-  __shared__ f32x4 partial[kShrinkWaves - 1][NB][kWave];
+  __shared__ f32x4 red[kShrinkWaves][NB][kWave];
+  __shared__ const uint16_t* slice_a[LORA_MAX_SLICES];  // per-lane slice lookup without
+                                                        // indexing the argument block
+  if (threadIdx.x < LORA_MAX_SLICES) slice_a[threadIdx.x] = p.a[threadIdx.x];
 
-  build_segment_table<kShrinkTile>(tab, p.active_ids, p.counts, p.starts, p.num_active,
-                                   p.max_loras, p.max_tokens);
+  build_segment_table<kTile>(tab, p.active_ids, p.counts, p.starts, p.num_active, p.max_loras,
+                             p.max_tokens);
   const int num_tiles = tab.num_tiles;
-  const int units = num_tiles * p.num_splits;
+  const int units = num_tiles * p.num_splits * p.num_groups;
 
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  const int col = lane & 15;  // token within the tile (MFMA N index)
+  const int wave = wave_index();
+  const int col = lane & 15;  // token within a 16-token block (MFMA N index)
   const int grp = lane >> 4;  // lane group: K sub-range, and output rows 4*grp..4*grp+3
   const int nout = p.num_slices * p.rank;
 
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    const int part = u / num_tiles;
-    const int m = u - part * num_tiles;
-    const Tile tile = resolve_tile<kShrinkTile>(tab, m);
-
-    const int t = col < tile.rows ? token_at(p.sorted, tile.first + col, p.max_tokens) : -1;
-    const uint16_t* xrow = t >= 0 ? p.x + static_cast<int64_t>(t) * p.ldx : nullptr;
-
-    // A-operand rows: output o = 16*nb + col of this lane's MFMA M index.
-    const uint16_t* arow[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int o = 16 * nb + col;
-      arow[nb] = nullptr;
-      if (o < nout) {
-        const int s = o / p.rank;
-        const int k = o - s * p.rank;
-        arow[nb] = slice_ptr(p, s) + (static_cast<int64_t>(tile.lora) * p.rank + k) * p.hidden;
-      }
-    }
-
-    f32x4 acc[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  for (XcdWalk walk = xcd_walk(units, gridDim.x); walk.next < walk.end; walk.next += walk.step) {
+    const int u = walk.next;
+    const int pg = u / num_tiles;  // (part, output group), group fastest
+    const int m = u - pg * num_tiles;
+    const int part = pg / p.num_groups;
+    const int o0 = (pg - part * p.num_groups) * 16 * NB;  // first output of the group
+    const Tile tile = resolve_tile<kTile>(tab, m);
     const int kbeg = part * p.split_len;
     const int kend = min(p.hidden, kbeg + p.split_len);
-    for (int kc = kbeg + wave * kShrinkChunk; kc < kend; kc += kShrinkWaves * kShrinkChunk) {
-      u32x4 xv[2];
-      u32x4 av[NB][2];
+
+    // A-operand rows: output o = o0 + 16*nb + col (the MFMA M index of this
+    // lane); outputs past the last are pointed at the last and masked.
+    const uint16_t* arow[NB];
+    uint32_t amask[NB];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int k = kc + 16 * grp + 8 * i;
-        const bool in = k < kend;  // kend is a multiple of 8: a piece is wholly in or out
-        xv[i] = (in && xrow) ? load16(xrow + k) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          av[nb][i] = (in && arow[nb]) ? load16(arow[nb] + k) : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, av[nb][i]), __builtin_bit_cast(bf16x8, xv[i]),
-              acc[nb], 0, 0, 0);
-      }
+    for (int nb = 0; nb < NB; ++nb) {
+      const int o = o0 + 16 * nb + col;
+      const bool ok = o < nout;
+      const int oc = ok ? o : nout - 1;
+      const int s = oc >> p.rank_shift;
+      const int k = oc & (p.rank - 1);
+      arow[nb] = slice_a[s] + (static_cast<int64_t>(tile.lora) * p.rank + k) * p.hidden;
+      amask[nb] = opaque_mask(ok);
     }
 
-    if (wave > 0) {
+    // One 64-element chunk of both operands, as loaded (masks are applied at
+    // use, so a chunk's loads stay in flight until its MFMAs need them).
+    // Lane group g, MFMA i <-> elements [32i + 8g, +8) of the chunk: one
+    // instruction reads 64 contiguous bytes of each of 16 rows, and the two
+    // instructions of a row's 128-byte line are issued back to back.
+    struct Chunk {
+      u32x4 x[MW][2];
+      u32x4 a[NB][2];
+      uint32_t kmask[2];  // pieces inside the part (all ones except in a tail chunk)
+    };
+    // A chunk that runs past the part's end re-reads its first piece and masks
+    // (kend is a multiple of 8, so a piece is wholly in or out).
+    auto piece = [&](int kc, int i, bool full, uint32_t& km) {
+      const int k = kc + 32 * i + 8 * grp;
+      if (full) {
+        km = 0xFFFFFFFFu;
+        return k;
+      }
+      km = opaque_mask(k < kend);
+      return k < kend ? k : kbeg;
+    };
+    auto load_a = [&](int kc, Chunk& c) {
+      const bool full = kc + kShrinkChunk <= kend;  // wave-uniform
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) partial[wave - 1][nb][lane] = acc[nb];
+      for (int i = 0; i < 2; ++i) {
+        const int k = piece(kc, i, full, c.kmask[i]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) c.a[nb][i] = load16(arow[nb] + k);
+      }
+    };
+    const uint16_t* xrow[MW];
+    uint32_t xmask[MW];
+    auto load_x = [&](int kc, Chunk& c) {
+      const bool full = kc + kShrinkChunk <= kend;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        uint32_t km;
+        const int k = piece(kc, i, full, km);
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb) c.x[mb][i] = load16(xrow[mb] + k);
+      }
+    };
+
+    // The first A chunk does not depend on the gathered token ids: issue it
+    // before waiting for them.
+    constexpr int kStride = kShrinkWaves * kShrinkChunk;
+    int kc = kbeg + wave * kShrinkChunk;
+    Chunk c0, c1;
+    if (kc < kend) load_a(kc, c0);
+
+    int tok[MW];
+#pragma unroll
+    for (int mb = 0; mb < MW; ++mb)
+      tok[mb] = tile_token(p.sorted, tile.first, tile.rows, 16 * mb + col, p.max_tokens);
+#pragma unroll
+    for (int mb = 0; mb < MW; ++mb) {
+      xrow[mb] = p.x + static_cast<int64_t>(tok[mb] >= 0 ? tok[mb] : 0) * p.ldx;
+      xmask[mb] = opaque_mask(tok[mb] >= 0);
     }
-    __syncthreads();
-    if (wave == 0 && t >= 0) {
+    if (kc < kend) load_x(kc, c0);
+
+    f32x4 acc[MW][NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        f32x4 v = acc[nb];
+    for (int mb = 0; mb < MW; ++mb)
 #pragma unroll
-        for (int w = 0; w < kShrinkWaves - 1; ++w) v += partial[w][nb][lane];
-        // D^T layout: this lane holds outputs o = 16*nb + 4*grp + j (j = 0..3)
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto mma = [&](const Chunk& c) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        u32x4 xv[MW];
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb) xv[mb] = c.x[mb][i] & (xmask[mb] & c.kmask[i]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const u32x4 av = c.a[nb][i] & amask[nb];
+#pragma unroll
+          for (int mb = 0; mb < MW; ++mb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, xv[mb]), acc[mb][nb],
+                0, 0, 0);
+        }
+      }
+    };
+
+    // Double-buffered walk over this wave's chunks (every kShrinkWaves-th one).
+    while (kc < kend) {
+      if (kc + kStride < kend) {
+        load_a(kc + kStride, c1);
+        load_x(kc + kStride, c1);
+      }
+      mma(c0);
+      kc += kStride;
+      if (kc >= kend) break;
+      if (kc + kStride < kend) {
+        load_a(kc + kStride, c0);
+        load_x(kc + kStride, c0);
+      }
+      mma(c1);
+      kc += kStride;
+    }
+
+    // Sum the four waves' partial sums in a fixed order, one 16-token block at a
+    // time; wave w finishes the output blocks nb = w, w+4, ...
+#pragma unroll
+    for (int mb = 0; mb < MW; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) red[wave][nb][lane] = acc[mb][nb];
+      __syncthreads();
+      const int t = tok[mb];  // token of this lane's column `col`
+      for (int nb = wave; nb < NB; nb += kShrinkWaves) {
+        f32x4 v = red[0][nb][lane];
+#pragma unroll
+        for (int w = 1; w < kShrinkWaves; ++w) v += red[w][nb][lane];
+        // D^T layout: this lane holds outputs o = o0 + 16*nb + 4*grp + j (j = 0..3)
         // of token column `col`; rank is a multiple of 8, so the four share a slice.
-        const int o = 16 * nb + 4 * grp;
-        if (o < nout) {
-          const int s = o / p.rank;
-          const int k = o - s * p.rank;
+        const int o = o0 + 16 * nb + 4 * grp;
+        if (t >= 0 && o < nout) {
+          const int s = o >> p.rank_shift;
+          const int k = o & (p.rank - 1);
           v *= p.scale;
-          float* dst = p.buf + ((static_cast<int64_t>(part) * p.num_slices + s) * p.max_tokens + t) *
-                                   p.rank + k;
+          float* dst = p.buf +
+                       ((static_cast<int64_t>(part) * p.num_slices + s) * p.max_tokens + t) * p.rank + k;
           store16(dst, __builtin_bit_cast(u32x4, v));
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
-template <int NB>
+template <int NB, int MW>
 hipError_t launch_shrink_nb(const ShrinkParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(shrink_kernel<NB>, dim3(grid), dim3(kShrinkThreads), 0, stream, p);
+  hipLaunchKernelGGL((shrink_kernel<NB, MW>), dim3(grid), dim3(kShrinkThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int MW>
+hipError_t launch_shrink_mw(const ShrinkParams& p, int nb, int grid, hipStream_t stream) {
+  switch (nb) {
+    case 1: return launch_shrink_nb<1, MW>(p, grid, stream);
+    case 2: return launch_shrink_nb<2, MW>(p, grid, stream);
+    case 3: return launch_shrink_nb<3, MW>(p, grid, stream);
+    case 4: return launch_shrink_nb<4, MW>(p, grid, stream);
+    case 5:
+    case 6: return launch_shrink_nb<6, MW>(p, grid, stream);
+    default: return launch_shrink_nb<8, MW>(p, grid, stream);
+  }
+}
+
+// Output blocks per group: all of them up to 8 (128 outputs), else groups of 8.
+int shrink_group_blocks(int nb_total) { return nb_total <= 8 ? nb_total : 8; }
+
+// 16-token blocks per tile: one for small batches (more tiles in flight), four
+// for large ones so each A operand serves 64 tokens, keeping the accumulators
+// (MW x NB blocks of 4 registers) within 64 registers.
+int shrink_tile_blocks(int max_tokens, int nb) {
+#ifdef LORA_TUNING
+  if (const char* e = getenv("LORA_SHRINK_MW")) return atoi(e);
+#endif
+  if (max_tokens <= 512) return 1;
+  return nb <= 4 ? 4 : 2;
 }
 
 int shrink_split_len(int hidden, int num_splits) {
@@ -163,11 +274,14 @@ int shrink_split_len(int hidden, int num_splits) {
   return (per + kShrinkChunk - 1) / kShrinkChunk * kShrinkChunk;
 }
 
-int shrink_grid(int max_tokens, int max_loras, int num_splits, int num_cus) {
-  const int64_t tiles = (static_cast<int64_t>(max_tokens) + kShrinkTile - 1) / kShrinkTile + max_loras;
-  const int64_t units = tiles * num_splits;
+int shrink_grid(int max_tokens, int max_loras, int num_splits, int num_groups, int mw,
+                int num_cus) {
+  const int tile = kShrinkTile * mw;
+  const int64_t tiles = (static_cast<int64_t>(max_tokens) + tile - 1) / tile + max_loras;
+  const int64_t units = tiles * num_splits * num_groups;
   const int64_t cap = static_cast<int64_t>(num_cus) * 8;
-  return static_cast<int>(units < cap ? units : cap);
+  const int64_t g = units < cap ? units : cap;
+  return static_cast<int>((g + kXcds - 1) / kXcds * kXcds);  // whole rounds over the XCDs
 }
 
 hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint16_t* const* lora_a,
@@ -181,6 +295,7 @@ hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint1
   for (int s = 0; s < LORA_MAX_SLICES; ++s) p.a[s] = s < num_slices ? lora_a[s] : lora_a[0];
   p.num_slices = num_slices;
   p.rank = rank;
+  p.rank_shift = rank == 8 ? 3 : rank == 16 ? 4 : rank == 32 ? 5 : 6;
   p.scale = scale;
   p.buf = buf;
   p.num_splits = num_splits;
@@ -192,22 +307,15 @@ hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint1
   p.num_active = meta.num_active;
   p.max_tokens = max_tokens;
   p.max_loras = max_loras;
-  const int grid = shrink_grid(max_tokens, max_loras, num_splits, num_cus);
-  const int nb = (num_slices * rank + 15) / 16;
-  switch (nb) {
-    case 1: return launch_shrink_nb<1>(p, grid, stream);
-    case 2: return launch_shrink_nb<2>(p, grid, stream);
-    case 3: return launch_shrink_nb<3>(p, grid, stream);
-    case 4: return launch_shrink_nb<4>(p, grid, stream);
-    case 5:
-    case 6: return launch_shrink_nb<6>(p, grid, stream);
-    case 7:
-    case 8: return launch_shrink_nb<8>(p, grid, stream);
-    case 9:
-    case 10:
-    case 11:
-    case 12: return launch_shrink_nb<12>(p, grid, stream);
-    default: return launch_shrink_nb<16>(p, grid, stream);
+  const int nb_total = (num_slices * rank + 15) / 16;
+  const int nb = shrink_group_blocks(nb_total);
+  p.num_groups = (nb_total + nb - 1) / nb;
+  const int mw = shrink_tile_blocks(max_tokens, nb);
+  const int grid = shrink_grid(max_tokens, max_loras, num_splits, p.num_groups, mw, num_cus);
+  switch (mw) {
+    case 1: return launch_shrink_mw<1>(p, nb, grid, stream);
+    case 2: return launch_shrink_mw<2>(p, nb, grid, stream);
+    default: return launch_shrink_mw<4>(p, nb, grid, stream);
   }
 }
 
