@@ -194,6 +194,14 @@ const char *lora_status_string(lora_status_t status);
  */
 lora_status_t lora_stream_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
 
+/*
+ * lora_stream_update - measurement aid: read every 16-byte piece of `buf`,
+ * change it and write it back in place (the output access pattern of
+ * lora_expand), giving the practical in-place update ceiling.  bytes must be a
+ * multiple of 16, buf 16-byte aligned.  The buffer's contents are scrambled.
+ */
+lora_status_t lora_stream_update(void *buf, int64_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

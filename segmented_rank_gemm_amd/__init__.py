@@ -21,7 +21,8 @@ import torch  # noqa: F401  (must precede loading the library, see above)
 
 __all__ = [
     "LIB_PATH", "LoraError", "LoraMeta", "lib", "lora_prepare_metadata", "lora_shrink",
-    "lora_shrink_default_splits", "lora_expand", "lora_stream_copy", "lora_status_string",
+    "lora_shrink_default_splits", "lora_expand", "lora_stream_copy", "lora_stream_update",
+    "lora_status_string",
     "LORA_MAX_LORAS", "LORA_MAX_SLICES", "LORA_MAX_SPLITS", "SUPPORTED_RANKS",
 ]
 
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.lora_expand.restype = ctypes.c_int
         L.lora_stream_copy.argtypes = [_VP, _VP, _I64, _VP]
         L.lora_stream_copy.restype = ctypes.c_int
+        L.lora_stream_update.argtypes = [_VP, _I64, _VP]
+        L.lora_stream_update.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -199,3 +202,9 @@ def lora_stream_copy(src: torch.Tensor, dst: torch.Tensor,
         raise ValueError("dst smaller than src")
     _check("lora_stream_copy", lib().lora_stream_copy(int(src.data_ptr()), int(dst.data_ptr()),
                                                       int(nbytes), _stream_handle(stream)))
+
+
+def lora_stream_update(buf: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
+    nbytes = buf.numel() * buf.element_size()
+    _check("lora_stream_update", lib().lora_stream_update(int(buf.data_ptr()), int(nbytes),
+                                                          _stream_handle(stream)))

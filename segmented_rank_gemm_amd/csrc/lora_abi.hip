@@ -23,6 +23,7 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
                          int num_cus, hipStream_t stream);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int num_cus,
                               hipStream_t stream);
+hipError_t launch_stream_update(void* buf, int64_t bytes, int num_cus, hipStream_t stream);
 int shrink_group_blocks(int nb_total);
 int shrink_tile_blocks(int max_tokens, int nb);
 }  // namespace lora
@@ -155,6 +156,11 @@ lora_status_t lora_stream_copy(const void* src, void* dst, int64_t bytes, hipStr
   if (s < d + static_cast<uintptr_t>(bytes) && d < s + static_cast<uintptr_t>(bytes))
     return LORA_ERR_INVALID_ARGUMENT;
   return launch_status(lora::launch_stream_copy(src, dst, bytes, current_cus(), stream));
+}
+
+lora_status_t lora_stream_update(void* buf, int64_t bytes, hipStream_t stream) {
+  if (!buf || bytes <= 0 || bytes % 16 != 0 || !aligned16(buf)) return LORA_ERR_INVALID_ARGUMENT;
+  return launch_status(lora::launch_stream_update(buf, bytes, current_cus(), stream));
 }
 
 }  // extern "C"

@@ -25,7 +25,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["lora_prepare_metadata", "lora_shrink", "lora_expand", "lora_status_string",
-              "lora_shrink_default_splits", "lora_stream_copy"]:
+              "lora_shrink_default_splits", "lora_stream_copy", "lora_stream_update"]:
         assert n in names
 
 
@@ -121,6 +121,9 @@ def test_stream_copy_rejects():
     assert L.lora_stream_copy(FAKE, FAKE + 4096, 20, None) == 1
     assert L.lora_stream_copy(FAKE, FAKE + 32, 64, None) == 1  # overlap
     assert L.lora_stream_copy(FAKE, FAKE + 4096, 0, None) == 1
+    assert L.lora_stream_update(None, 64, None) == 1
+    assert L.lora_stream_update(FAKE + 8, 64, None) == 1
+    assert L.lora_stream_update(FAKE, 24, None) == 1
 
 
 def test_default_splits_is_pure_and_in_range():
