@@ -90,23 +90,22 @@ struct BChunk {
 
 // MW = 16-token blocks per tile; every block shares the B operand loads.
 //
-// A workgroup unit is (tile of 16*MW tokens of one adapter, slice s, column
-// range of 4*cpr chunks); wave w takes chunks w, w+4, ... of the range, so the
-// four waves stream neighbouring columns together.  The rank operand of the
-// tile (sum over the shrink's parts, split hi/lo, already in MFMA operand
-// layout) is built once per unit into LDS and shared by the four waves.
+// A workgroup unit is (fixed tile of 16*MW consecutive grouped positions,
+// slice s, column range of 4*cpr chunks); wave w takes chunks w, w+4, ... of the
+// range, so the four waves stream neighbouring columns together.  The unit's
+// token ids load together with the slot table.  The rank operand of the tile
+// (sum over the shrink's parts, split hi/lo, already in MFMA operand layout) is
+// built once per unit into LDS and shared by the four waves.  A tile that
+// straddles two adapters loads y once per chunk and runs one B pass per
+// adapter, each storing its own rows.
 template <int RANK, int MW>
-__global__ __launch_bounds__(kExpandThreads) void expand_kernel(ExpandParams p) {
+__global__ __launch_bounds__(kExpandThreads) __attribute__((amdgpu_waves_per_eu(RANK <= 16 ? 2 : 1)))
+void expand_kernel(ExpandParams p) {
   constexpr int kTile = 16 * MW;
   constexpr int kSteps = RankOperand<RANK>::kSteps;
   constexpr int kOpWords = RANK == 8 ? 2 : 4;  // 32-bit words per lane per MFMA step
-  __shared__ SegmentTable tab;
+  __shared__ SlotTable tab;
   __shared__ uint32_t a_lds[MW][kSteps][kOpWords][kWave];
-  build_segment_table<kTile>(tab, p.active_ids, p.counts, p.starts, p.num_active, p.max_loras,
-                             p.max_tokens);
-  const int num_tiles = tab.num_tiles;
-  const int ranges = p.range_end[p.num_slices - 1];
-  const int units = num_tiles * ranges;
 
   const int lane = lane_id();
   const int wave = wave_index();
@@ -116,10 +115,38 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(ExpandParams p) 
   const bool use_lo = grp >= 2;
   const int cpr = p.chunks_per_range;
 
-  for (XcdWalk walk = xcd_walk(units, gridDim.x); walk.next < walk.end; walk.next += walk.step) {
+  const int tiles = (p.max_tokens + kTile - 1) / kTile;
+  const int ranges = p.range_end[p.num_slices - 1];
+  const int units = tiles * ranges;
+  XcdWalk walk = xcd_walk(units, gridDim.x);
+
+  // Token ids of a unit's rows: the rank-operand row c and the output rows
+  // 4*grp + j of every 16-token block.
+  int ta[MW], td[MW][4];
+  auto load_tokens = [&](int u) {
+    const int pos0 = (u % tiles) * kTile;
+#pragma unroll
+    for (int mb = 0; mb < MW; ++mb) {
+      ta[mb] = token_at_clamped(p.sorted, pos0 + 16 * mb + c, p.max_tokens);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        td[mb][j] = token_at_clamped(p.sorted, pos0 + 16 * mb + 4 * grp + j, p.max_tokens);
+    }
+  };
+  if (walk.next < walk.end) load_tokens(walk.next);
+  if (wave == 0)
+    load_slot_table(tab, p.active_ids, p.counts, p.starts, p.num_active, p.max_loras, p.max_tokens);
+  __syncthreads();
+
+  for (bool first = true; walk.next < walk.end; walk.next += walk.step, first = false) {
     const int u = walk.next;
-    const int m = u % num_tiles;
-    const int cr = u / num_tiles;
+    if (!first) load_tokens(u);
+    const int m = u % tiles;
+    const int cr = u / tiles;
+    const int pos0 = m * kTile;
+    const SlotRange sr = tile_slots(tab, pos0, kTile);
+    if (sr.first > sr.last) continue;  // wave-uniform: no row of this tile has an adapter
+
     int s = 0;
 #pragma unroll
     for (int i = 0; i < LORA_MAX_SLICES - 1; ++i) s += (i < p.num_slices - 1 && cr >= p.range_end[i]) ? 1 : 0;
@@ -138,16 +165,15 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(ExpandParams p) 
     const int range_begin = (cr - r_before) * cpr * kExpandWaves;
     const int range_end = min(chunks_s, range_begin + cpr * kExpandWaves);
     const int ch0 = range_begin + wave;  // this wave's chunks: ch0, ch0 + 4, ...
-    const Tile tile = resolve_tile<kTile>(tab, m);
-    const uint16_t* bmat = bslice + static_cast<int64_t>(tile.lora) * n_s * RANK;
 
-    // Loads are unconditional and never masked here: a lane whose row is past
-    // the tile (or whose column is past the slice) reads a clamped, valid
-    // location, and its results are simply not stored; the matrix-core rows of
-    // such a token, and the columns of such a column, touch nothing else.
-
-    // B operand of a chunk: depends on the adapter and the columns only.
-    auto load_b = [&](int ch, BChunk<RANK>& bc) {
+    // Loads are unconditional and never masked here: a lane whose row has no
+    // adapter (or whose column is past the slice) reads a clamped, valid
+    // location, and its results are simply not stored; the matrix-core rows
+    // of such a token, and the columns of such a column, touch nothing else.
+    auto bmat_of = [&](int slot) {
+      return bslice + static_cast<int64_t>(tab.lora[slot]) * n_s * RANK;
+    };
+    auto load_b = [&](const uint16_t* bmat, int ch, BChunk<RANK>& bc) {
       const int col = ch * kExpandCols + 8 * c;
       const int colc = col < n_s ? col : n_s - 8;  // n_s is a multiple of 8
 #pragma unroll
@@ -161,27 +187,22 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(ExpandParams p) 
         }
       }
     };
+    const uint16_t* bmat0 = bmat_of(sr.first);
     BChunk<RANK> bcur, bnext;
-    if (ch0 < range_end) load_b(ch0, bcur);
+    if (ch0 < range_end) load_b(bmat0, ch0, bcur);
 
-    // Output rows of this lane in every block: 4*grp + j; the rank-operand
-    // rows are c (+16 per block).
-    int td[MW][4], ta[MW];
-#pragma unroll
-    for (int mb = 0; mb < MW; ++mb) {
-      ta[mb] = tile_token(p.sorted, tile.first, tile.rows, 16 * mb + c, p.max_tokens);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        td[mb][j] = tile_token(p.sorted, tile.first, tile.rows, 16 * mb + 4 * grp + j, p.max_tokens);
-    }
-    const int t_first = tile_token(p.sorted, tile.first, tile.rows, 0, p.max_tokens);
-    const int t_safe = t_first >= 0 ? t_first : 0;
+    // y rows (a row without an adapter reads row 0 and is never stored) and
+    // the grouped position of each output row.
     int64_t yrow[MW][4];
+    bool dval[MW][4];
 #pragma unroll
     for (int mb = 0; mb < MW; ++mb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        yrow[mb][j] = static_cast<int64_t>(td[mb][j] >= 0 ? td[mb][j] : t_safe) * p.ldy + off_s;
+      for (int j = 0; j < 4; ++j) {
+        const int q = pos0 + 16 * mb + 4 * grp + j;
+        dval[mb][j] = row_valid(tab, q, td[mb][j], p.max_tokens);
+        yrow[mb][j] = static_cast<int64_t>(dval[mb][j] ? td[mb][j] : 0) * p.ldy + off_s;
+      }
 
     auto load_y = [&](int ch, YBlock (&yb)[MW]) {
       const int col = ch * kExpandCols + 8 * c;
@@ -206,8 +227,9 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(ExpandParams p) 
         const int mb = item / kSteps;
         const int q = item - mb * kSteps;
         const int k0 = RANK == 8 ? 4 * khalf : 16 * q + 8 * khalf;
-        const int trow = ta[mb] >= 0 ? ta[mb] : t_safe;
-        const float* src0 = p.buf + (static_cast<int64_t>(s) * p.max_tokens + trow) * RANK + k0;
+        const bool aval = row_valid(tab, pos0 + 16 * mb + c, ta[mb], p.max_tokens);
+        const float* src0 =
+            p.buf + (static_cast<int64_t>(s) * p.max_tokens + (aval ? ta[mb] : 0)) * RANK + k0;
         float v[kPer];
 #pragma unroll
         for (int e = 0; e < kPer; ++e) v[e] = 0.f;
@@ -253,18 +275,14 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(ExpandParams p) 
       }
     __syncthreads();  // the next unit may overwrite a_lds
 
-    for (int ch = ch0; ch < range_end; ch += kExpandWaves) {
-      const bool more = ch + kExpandWaves < range_end;
-      if (more) {
-        load_y(ch + kExpandWaves, ynext);
-        if constexpr (RANK <= 32) load_b(ch + kExpandWaves, bnext);
-      }
+    // One slot's pass over one chunk: acc = y + buf . B^T, stored for the rows
+    // of that slot.
+    auto pass = [&](const BChunk<RANK>& bc, int ch, int s_begin, int s_end) {
       const int col = ch * kExpandCols + 8 * c;  // first of this lane's 8 columns
       const bool col_ok = col < n_s;
-
 #pragma unroll
       for (int mb = 0; mb < MW; ++mb) {
-        if (16 * mb >= tile.rows) break;  // wave-uniform: empty block
+        if (pos0 + 16 * mb >= s_end || pos0 + 16 * mb + 16 <= s_begin) continue;  // wave-uniform
         f32x4 acc[8];
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
@@ -280,21 +298,36 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(ExpandParams p) 
           for (int q = 0; q < kSteps; ++q) {
             if constexpr (RANK == 8) {
               acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                  a[mb].op[q], __builtin_bit_cast(i16x4, bcur.w[b][0]), acc[b], 0, 0, 0);
+                  a[mb].op[q], __builtin_bit_cast(i16x4, bc.w[b][0]), acc[b], 0, 0, 0);
             } else {
               acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  a[mb].op[q], __builtin_bit_cast(bf16x8, bcur.w[b][q]), acc[b], 0, 0, 0);
+                  a[mb].op[q], __builtin_bit_cast(bf16x8, bc.w[b][q]), acc[b], 0, 0, 0);
             }
           }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (col_ok && td[mb][j] >= 0) {
+          const int q = pos0 + 16 * mb + 4 * grp + j;
+          if (col_ok && dval[mb][j] && q >= s_begin && q < s_end) {
             const u32x4 out = {pack_bf16x2(acc[0][j], acc[1][j]), pack_bf16x2(acc[2][j], acc[3][j]),
                                pack_bf16x2(acc[4][j], acc[5][j]), pack_bf16x2(acc[6][j], acc[7][j])};
             store16_stream(p.y + yrow[mb][j] + col, out);
           }
         }
+      }
+    };
+
+    for (int ch = ch0; ch < range_end; ch += kExpandWaves) {
+      const bool more = ch + kExpandWaves < range_end;
+      if (more) {
+        load_y(ch + kExpandWaves, ynext);
+        if constexpr (RANK <= 32) load_b(bmat0, ch + kExpandWaves, bnext);
+      }
+      pass(bcur, ch, tab.start[sr.first], tab.end[sr.first]);
+      // Rare: a tile across adapters.  bcur is free after the first pass.
+      for (int slot = sr.first + 1; slot <= sr.last; ++slot) {
+        load_b(bmat_of(slot), ch, bcur);
+        pass(bcur, ch, tab.start[slot], tab.end[slot]);
       }
       if (more) {
 #pragma unroll
@@ -302,7 +335,7 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(ExpandParams p) 
         if constexpr (RANK <= 32) {
           bcur = bnext;
         } else {
-          load_b(ch + kExpandWaves, bcur);
+          load_b(bmat0, ch + kExpandWaves, bcur);
         }
       }
     }
@@ -342,16 +375,16 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
       p.off[s] = off;
     }
   }
-  // Chunks per wave in a workgroup unit (the unit spans 4x as many): at least
-  // rank/16, so that building the rank operand (which reads rank floats per
-  // token and part) stays small next to the y bytes of the unit; more when the
-  // batch is large enough to still give every CU ~32 units; at most 8.
+  // Chunks per wave in a workgroup unit (the unit spans 4x as many): as many as
+  // still give every CU ~16 units at the largest batch, at least 2 for rank >= 32
+  // (building the rank operand reads rank floats per token and part, to be
+  // amortised over the unit's y bytes), at most 8.
   const int mw = expand_tile_blocks(rank);
-  const int64_t tiles =
-      (static_cast<int64_t>(max_tokens) + kExpandTile * mw - 1) / (kExpandTile * mw) + max_loras;
-  int64_t cpr = tiles * total_chunks / (static_cast<int64_t>(num_cus) * 32);
-  cpr = cpr > rank / 16 ? cpr : rank / 16;
-  cpr = cpr < 1 ? 1 : (cpr > 8 ? 8 : cpr);
+  const int64_t tiles = (static_cast<int64_t>(max_tokens) + kExpandTile * mw - 1) / (kExpandTile * mw);
+  int64_t cpr = tiles * total_chunks / (static_cast<int64_t>(num_cus) * 16);
+  const int64_t by_rank = rank >= 32 ? 2 : 1;
+  cpr = cpr > by_rank ? cpr : by_rank;
+  cpr = cpr > 8 ? 8 : cpr;
 #ifdef LORA_TUNING
   if (const char* e = getenv("LORA_EXPAND_CPR")) cpr = atoi(e);
 #endif

@@ -11,7 +11,7 @@
 #include "lora_mi355x.h"
 
 namespace lora {
-hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_loras,
+hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_tokens, int max_loras,
                            const lora_meta_t& meta, hipStream_t stream);
 hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint16_t* const* lora_a,
                          int num_slices, int rank, float scale, float* buf, int num_splits,
@@ -81,7 +81,8 @@ lora_status_t lora_prepare_metadata(const int32_t* token_lora_mapping, int32_t n
   if (!meta_ok(meta) || !sizes_ok(max_tokens, max_loras)) return LORA_ERR_INVALID_ARGUMENT;
   if (num_tokens < 0 || num_tokens > max_tokens) return LORA_ERR_INVALID_ARGUMENT;
   if (num_tokens > 0 && !token_lora_mapping) return LORA_ERR_INVALID_ARGUMENT;
-  return launch_status(lora::launch_metadata(token_lora_mapping, num_tokens, max_loras, *meta, stream));
+  return launch_status(
+      lora::launch_metadata(token_lora_mapping, num_tokens, max_tokens, max_loras, *meta, stream));
 }
 
 int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t max_loras,
@@ -91,8 +92,8 @@ int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t m
     return 0;
   // Enough (tile, part, output group) units for ~1 workgroup per CU of a
   // 256-CU device at the largest batch, with parts of at least 256 hidden
-  // elements, and parts * rank <= 256 so that the expand, which sums the parts
-  // once per workgroup unit, reads at most 1 KB of them per token there.
+  // elements, at most 8 parts (the expand sums them with one group of 8
+  // loads) and parts * rank <= 256 (at most 1 KB of parts per token).
   const int nb_total = (num_slices * rank + 15) / 16;
   const int nb = lora::shrink_group_blocks(nb_total);
   const int64_t groups = (nb_total + nb - 1) / nb;
@@ -100,7 +101,7 @@ int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t m
   const int64_t tiles = (static_cast<int64_t>(max_tokens) + tile - 1) / tile + max_loras;
   int64_t splits = (256 + tiles * groups - 1) / (tiles * groups);
   const int64_t by_len = hidden / 256 > 0 ? hidden / 256 : 1;
-  const int64_t by_fold = 256 / rank > 0 ? 256 / rank : 1;
+  const int64_t by_fold = 256 / rank < 8 ? 256 / rank : 8;
   splits = splits < by_len ? splits : by_len;
   splits = splits < by_fold ? splits : by_fold;
   splits = splits < 1 ? 1 : (splits > LORA_MAX_SPLITS ? LORA_MAX_SPLITS : splits);

@@ -9,8 +9,8 @@
 //
 // One workgroup per group (group 0 = no adapter, group g = adapter g-1), so the
 // grid is max_loras + 1 workgroups whatever the ids are.  The map is walked in
-// blocks of kMetaBlock tokens, kPerThread consecutive tokens per thread, each
-// token read once.  For its group g a workgroup needs three things: how many
+// blocks, kPerThread consecutive tokens per thread, each token read once (twice
+// for batches larger than one block).  For its group g a workgroup needs three things: how many
 // tokens sit in lower groups (its start), which groups occur at all (its slot
 // among the adapters present and, for group 0, how many there are), and, per
 // member, how many members precede it in token order (its rank).  Counts come
@@ -22,10 +22,7 @@
 
 namespace lora {
 
-constexpr int kMetaThreads = 1024;
-constexpr int kMetaWaves = kMetaThreads / kWave;
 constexpr int kPerThread = 8;
-constexpr int kMetaBlock = kMetaThreads * kPerThread;
 
 __device__ __forceinline__ int group_of(int32_t id, int max_loras) {
   return (id >= -1 && id < max_loras) ? id + 1 : 0;
@@ -50,37 +47,31 @@ __device__ __forceinline__ void load_groups(const int32_t* __restrict__ mapping,
   }
 }
 
-// Block-wide sum of one int per thread, added in wave order.
-__device__ __forceinline__ int block_sum(int v, int* scratch) {
-  const int ws = wave_sum(v);
-  if (lane_id() == 0) scratch[threadIdx.x / kWave] = ws;
-  __syncthreads();
-  int total = 0;
-#pragma unroll
-  for (int w = 0; w < kMetaWaves; ++w) total += scratch[w];
-  __syncthreads();
-  return total;
-}
-
-__global__ __launch_bounds__(kMetaThreads) void metadata_kernel(
+// THREADS threads per workgroup (256 for small batches: fewer waves to
+// synchronise; 1024 for large ones); a block of the map is THREADS * 8 tokens.
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void metadata_kernel(
     const int32_t* __restrict__ mapping, int num_tokens, int max_loras,
     int32_t* __restrict__ sorted, int32_t* __restrict__ active_ids,
     int32_t* __restrict__ counts, int32_t* __restrict__ starts,
     int32_t* __restrict__ num_active) {
+  constexpr int kWaves = THREADS / kWave;
+  constexpr int kBlock = THREADS * kPerThread;
   __shared__ int present[LORA_MAX_LORAS + 1];
-  __shared__ int scratch[kMetaWaves];
-  __shared__ int s_slot, s_present;
+  __shared__ int wave_below[kWaves], wave_members[kWaves], wave_scan[kWaves];
 
   const int g = blockIdx.x;
   const int groups = max_loras + 1;
   const int tid = threadIdx.x;
-  for (int i = tid; i < groups; i += kMetaThreads) present[i] = 0;
+  const int lane = lane_id();
+  const int wave = wave_index();
+  for (int i = tid; i < groups; i += THREADS) present[i] = 0;
   __syncthreads();
 
   // Count pass: tokens in lower groups, members of g, occurring groups.
   int grp[kPerThread];
   int below = 0, members = 0;
-  for (int b0 = 0; b0 < num_tokens; b0 += kMetaBlock) {
+  for (int b0 = 0; b0 < num_tokens; b0 += kBlock) {
     load_groups(mapping, num_tokens, max_loras, b0 + tid * kPerThread, grp);
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
@@ -89,36 +80,41 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(
       members += grp[e] == g ? 1 : 0;
     }
   }
-  const int start = block_sum(below, scratch);
-  const int total = block_sum(members, scratch);
+  const int wb = wave_sum(below), wm = wave_sum(members);
+  if (lane == 0) {
+    wave_below[wave] = wb;
+    wave_members[wave] = wm;
+  }
+  __syncthreads();
+  int start = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    start += wave_below[w];
+    total += wave_members[w];
+  }
 
-  // Slot of g among the adapters present, and how many are present.
-  if (tid < kWave) {
+  // Wave 0: slot of g among the adapters present, how many are present, and
+  // the slot entries (group 0 writes the unused slots and the count).
+  if (wave == 0) {
     int slot = 0, npresent = 0;
     for (int base = 0; base < groups; base += kWave) {
-      const int i = base + tid;
+      const int i = base + lane;
       const bool p = i >= 1 && i < groups && present[i] != 0;
       slot += __popcll(__ballot(p && i < g));
       npresent += __popcll(__ballot(p));
     }
-    if (tid == 0) {
-      s_slot = slot;
-      s_present = npresent;
+    if (g == 0) {
+      for (int i = npresent + lane; i < max_loras; i += kWave) {
+        active_ids[i] = -1;
+        counts[i] = 0;
+        starts[i] = num_tokens;
+      }
+      if (lane == 0) *num_active = npresent;
+    } else if (total > 0 && lane == 0) {
+      active_ids[slot] = g - 1;
+      counts[slot] = total;
+      starts[slot] = start;
     }
-  }
-  __syncthreads();
-
-  if (g == 0) {
-    for (int i = s_present + tid; i < max_loras; i += kMetaThreads) {
-      active_ids[i] = -1;
-      counts[i] = 0;
-      starts[i] = num_tokens;
-    }
-    if (tid == 0) *num_active = s_present;
-  } else if (total > 0 && tid == 0) {
-    active_ids[s_slot] = g - 1;
-    counts[s_slot] = total;
-    starts[s_slot] = start;
   }
   if (total == 0) return;  // uniform across the workgroup
 
@@ -126,23 +122,22 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(
   // per-thread member counts (thread order is token order within a block).  A
   // batch of one block reuses the groups already in registers.
   int placed = 0;
-  for (int b0 = 0; b0 < num_tokens; b0 += kMetaBlock) {
+  for (int b0 = 0; b0 < num_tokens; b0 += kBlock) {
     const int t0 = b0 + tid * kPerThread;
-    if (num_tokens > kMetaBlock) load_groups(mapping, num_tokens, max_loras, t0, grp);
+    if (num_tokens > kBlock) load_groups(mapping, num_tokens, max_loras, t0, grp);
     int mine = 0;
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) mine += grp[e] == g ? 1 : 0;
     const int incl = wave_inclusive_scan(mine);
-    if (lane_id() == kWave - 1) scratch[tid / kWave] = incl;
+    if (lane == kWave - 1) wave_scan[wave] = incl;
     __syncthreads();
     int before = 0, block_total = 0;
 #pragma unroll
-    for (int w = 0; w < kMetaWaves; ++w) {
-      const int n = scratch[w];
-      before += w < tid / kWave ? n : 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const int n = wave_scan[w];
+      before += w < wave ? n : 0;
       block_total += n;
     }
-    __syncthreads();
     int pos = start + placed + before + incl - mine;
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
@@ -152,14 +147,21 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(
       }
     }
     placed += block_total;
+    if (b0 + kBlock < num_tokens) __syncthreads();  // wave_scan is reused by the next block
   }
 }
 
-hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_loras,
+hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_tokens, int max_loras,
                            const lora_meta_t& meta, hipStream_t stream) {
-  hipLaunchKernelGGL(metadata_kernel, dim3(max_loras + 1), dim3(kMetaThreads), 0, stream,
-                     mapping, num_tokens, max_loras, meta.sorted_token_ids, meta.active_lora_ids,
-                     meta.num_tokens_per_lora, meta.lora_token_start, meta.num_active);
+  if (max_tokens <= 256 * kPerThread) {
+    hipLaunchKernelGGL(metadata_kernel<256>, dim3(max_loras + 1), dim3(256), 0, stream, mapping,
+                       num_tokens, max_loras, meta.sorted_token_ids, meta.active_lora_ids,
+                       meta.num_tokens_per_lora, meta.lora_token_start, meta.num_active);
+  } else {
+    hipLaunchKernelGGL(metadata_kernel<1024>, dim3(max_loras + 1), dim3(1024), 0, stream, mapping,
+                       num_tokens, max_loras, meta.sorted_token_ids, meta.active_lora_ids,
+                       meta.num_tokens_per_lora, meta.lora_token_start, meta.num_active);
+  }
   return hipGetLastError();
 }
 

@@ -259,14 +259,15 @@ hipError_t launch_shrink_mw(const ShrinkParams& p, int nb, int grid, hipStream_t
 int shrink_group_blocks(int nb_total) { return nb_total <= 8 ? nb_total : 8; }
 
 // 16-token blocks per tile: one for small batches (more tiles in flight), four
-// for large ones so each A operand serves 64 tokens, keeping the accumulators
-// (MW x NB blocks of 4 registers) within 64 registers.
+// for large ones so each A operand serves 64 tokens, fewer when there are many
+// output blocks, so that the accumulators and double-buffered operands fit in
+// registers without spilling.
 int shrink_tile_blocks(int max_tokens, int nb) {
 #ifdef LORA_TUNING
   if (const char* e = getenv("LORA_SHRINK_MW")) return atoi(e);
 #endif
   if (max_tokens <= 512) return 1;
-  return nb <= 4 ? 4 : 2;
+  return nb <= 4 ? 4 : (nb <= 6 ? 2 : 1);
 }
 
 int shrink_split_len(int hidden, int num_splits) {
