@@ -106,7 +106,7 @@ typedef struct lora_meta {
  *
  * Writes sorted_token_ids[0:num_tokens] and all max_loras entries of the three
  * per-slot arrays, plus num_active.  A stable counting sort: bit-for-bit
- * deterministic, no atomics on global memory.  Grid: max_loras + 1 workgroups (of 256 threads when max_tokens <= 2048, else 1024).
+ * deterministic, no atomics on global memory.  Grid: max_loras + 1 workgroups (of 64, 256 or 1024 threads by max_tokens).
  */
 lora_status_t lora_prepare_metadata(const int32_t *token_lora_mapping, int32_t num_tokens,
                                     int32_t max_tokens, int32_t max_loras,

@@ -217,11 +217,13 @@ void expand_kernel(ExpandParams p) {
 
     // Rank operand, built cooperatively: item (mb, q) is one MFMA step of one
     // block, i.e. one register set of the wave; its lane (c, grp) sums the
-    // parts of ranks [k0, k0 + kPer) of token row c.  Parts go in groups of 8
-    // whose loads are all issued before the first add; the adds run in part
-    // order.  Part slots past the last re-read the group's first and are masked.
+    // parts of ranks [k0, k0 + kPer) of token row c.  Parts go in groups (16
+    // for rank 8, else 8) whose loads are all issued before the first add; the
+    // adds run in part order.  Part slots past the last re-read the group's
+    // first and are masked.
     {
       constexpr int kPer = RANK == 8 ? 4 : 8;
+      constexpr int kGroup = RANK == 8 ? 16 : 8;
       const int64_t plane = static_cast<int64_t>(p.num_slices) * p.max_tokens * RANK;
       for (int item = wave; item < MW * kSteps; item += kExpandWaves) {
         const int mb = item / kSteps;
@@ -233,19 +235,19 @@ void expand_kernel(ExpandParams p) {
         float v[kPer];
 #pragma unroll
         for (int e = 0; e < kPer; ++e) v[e] = 0.f;
-        for (int sp0 = 0; sp0 < p.num_splits; sp0 += 8) {
-          uint32_t pm[8];
+        for (int sp0 = 0; sp0 < p.num_splits; sp0 += kGroup) {
+          uint32_t pm[kGroup];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) pm[i] = opaque_mask(sp0 + i < p.num_splits);
-          u32x4 w[8][kPer / 4];
+          for (int i = 0; i < kGroup; ++i) pm[i] = opaque_mask(sp0 + i < p.num_splits);
+          u32x4 w[kGroup][kPer / 4];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
+          for (int i = 0; i < kGroup; ++i) {
             const int sp = sp0 + i < p.num_splits ? sp0 + i : sp0;
 #pragma unroll
             for (int e4 = 0; e4 < kPer / 4; ++e4) w[i][e4] = load16(src0 + sp * plane + 4 * e4);
           }
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
+          for (int i = 0; i < kGroup; ++i)
 #pragma unroll
             for (int e4 = 0; e4 < kPer / 4; ++e4)
 #pragma unroll

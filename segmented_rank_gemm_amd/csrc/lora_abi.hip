@@ -92,18 +92,31 @@ int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t m
     return 0;
   // Enough (tile, part, output group) units for ~1 workgroup per CU of a
   // 256-CU device at the largest batch, with parts of at least 256 hidden
-  // elements, at most 8 parts (the expand sums them with one group of 8
-  // loads) and parts * rank <= 256 (at most 1 KB of parts per token).
+  // elements.  Small batches (16-token tiles): no more parts than the expand
+  // sums with one batch of loads (16 for rank 8, else 8) and parts * rank <=
+  // 256 (at most 1 KB of parts per token).  Large batches (64-token tiles):
+  // also parts of about 1024 elements, so that several workgroups share each
+  // CU, up to 8 parts (a second batch of loads in the expand at rank 64 costs
+  // far less than the shrink gains).
   const int nb_total = (num_slices * rank + 15) / 16;
   const int nb = lora::shrink_group_blocks(nb_total);
   const int64_t groups = (nb_total + nb - 1) / nb;
-  const int64_t tile = 16 * lora::shrink_tile_blocks(max_tokens, nb);
+  const int mw = lora::shrink_tile_blocks(max_tokens, nb);
+  const int64_t tile = 16 * mw;
   const int64_t tiles = (static_cast<int64_t>(max_tokens) + tile - 1) / tile + max_loras;
   int64_t splits = (256 + tiles * groups - 1) / (tiles * groups);
   const int64_t by_len = hidden / 256 > 0 ? hidden / 256 : 1;
-  const int64_t by_fold = 256 / rank < 8 ? 256 / rank : 8;
+  int64_t cap;
+  if (mw == 4) {
+    const int64_t by_work = (hidden + 1023) / 1024;
+    splits = splits > by_work ? splits : by_work;
+    cap = 8;
+  } else {
+    const int64_t group = rank == 8 ? 16 : 8;  // parts the expand sums per batch of loads
+    cap = 256 / rank < group ? 256 / rank : group;
+  }
   splits = splits < by_len ? splits : by_len;
-  splits = splits < by_fold ? splits : by_fold;
+  splits = splits < cap ? splits : cap;
   splits = splits < 1 ? 1 : (splits > LORA_MAX_SPLITS ? LORA_MAX_SPLITS : splits);
   return static_cast<int32_t>(splits);
 }

@@ -47,8 +47,9 @@ __device__ __forceinline__ void load_groups(const int32_t* __restrict__ mapping,
   }
 }
 
-// THREADS threads per workgroup (256 for small batches: fewer waves to
-// synchronise; 1024 for large ones); a block of the map is THREADS * 8 tokens.
+// THREADS threads per workgroup (64, a single wave, for batches up to 512
+// tokens, 256 up to 2048, else 1024: fewer waves to synchronise on small
+// batches); a block of the map is THREADS * 8 tokens.
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void metadata_kernel(
     const int32_t* __restrict__ mapping, int num_tokens, int max_loras,
@@ -153,7 +154,11 @@ __global__ __launch_bounds__(THREADS) void metadata_kernel(
 
 hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_tokens, int max_loras,
                            const lora_meta_t& meta, hipStream_t stream) {
-  if (max_tokens <= 256 * kPerThread) {
+  if (max_tokens <= 64 * kPerThread) {
+    hipLaunchKernelGGL(metadata_kernel<64>, dim3(max_loras + 1), dim3(64), 0, stream, mapping,
+                       num_tokens, max_loras, meta.sorted_token_ids, meta.active_lora_ids,
+                       meta.num_tokens_per_lora, meta.lora_token_start, meta.num_active);
+  } else if (max_tokens <= 256 * kPerThread) {
     hipLaunchKernelGGL(metadata_kernel<256>, dim3(max_loras + 1), dim3(256), 0, stream, mapping,
                        num_tokens, max_loras, meta.sorted_token_ids, meta.active_lora_ids,
                        meta.num_tokens_per_lora, meta.lora_token_start, meta.num_active);

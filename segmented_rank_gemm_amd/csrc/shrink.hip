@@ -236,6 +236,171 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
   }
 }
 
+// Large batches: the same contraction with both operands staged through LDS.
+// A unit is (tile of 64 grouped tokens of one adapter, part, group of NB <= 8
+// output blocks).  Per 64-element chunk the workgroup fetches the tile's 64 x
+// rows and 16*NB A rows with full-line loads (8 lanes per 128-byte row line,
+// every byte of every line used) into LDS, where the row's 16-byte pieces are
+// XOR-swizzled by row so that the MFMA-layout reads (16 rows x 16 bytes per
+// instruction) hit 16 distinct banks.  Two chunks are in flight in registers
+// ahead of the one being computed; LDS is double-buffered, one barrier per
+// chunk.  Wave w owns token block w (16 tokens) and all output blocks, so no
+// cross-wave reduction is needed.
+constexpr int kLdsTile = 64;  // tokens per tile (4 waves x 16)
+
+template <int NB>
+__global__ __launch_bounds__(kShrinkThreads) void shrink_lds_kernel(ShrinkParams p) {
+  constexpr int kRows = kLdsTile + 16 * NB;       // x rows, then A rows
+  constexpr int kJ = (kRows * 8 + kShrinkThreads - 1) / kShrinkThreads;  // pieces per thread
+  constexpr int kLdsRows = kJ * (kShrinkThreads / 8);
+  __shared__ SegmentTable tab;
+  __shared__ u32x4 stage[2][kLdsRows * 8];
+  __shared__ const uint16_t* slice_a[LORA_MAX_SLICES];
+
+  if (threadIdx.x < LORA_MAX_SLICES) slice_a[threadIdx.x] = p.a[threadIdx.x];
+  build_segment_table<kLdsTile>(tab, p.active_ids, p.counts, p.starts, p.num_active, p.max_loras,
+                                p.max_tokens);
+  const int num_tiles = tab.num_tiles;
+  const int units = num_tiles * p.num_splits * p.num_groups;
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = wave_index();
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int nout = p.num_slices * p.rank;
+  const int piece = tid & 7;     // this thread's 16-byte piece of every row it loads
+  const int row0 = tid >> 3;     // rows row0 + 32 j, j < kJ
+
+  for (XcdWalk walk = xcd_walk(units, gridDim.x); walk.next < walk.end; walk.next += walk.step) {
+    const int u = walk.next;
+    const int pg = u / num_tiles;
+    const int m = u - pg * num_tiles;
+    const int part = pg / p.num_groups;
+    const int o0 = (pg - part * p.num_groups) * 16 * NB;
+    const Tile tile = resolve_tile<kLdsTile>(tab, m);
+    const int kbeg = part * p.split_len;
+    const int kend = min(p.hidden, kbeg + p.split_len);
+    if (kbeg >= kend) {
+      // an empty part still owes its (zero) contribution
+      const int t = tile_token(p.sorted, tile.first, tile.rows, 16 * wave + col, p.max_tokens);
+      for (int nb = 0; nb < NB; ++nb) {
+        const int o = o0 + 16 * nb + 4 * grp;
+        if (t >= 0 && o < nout) {
+          float* dst = p.buf + ((static_cast<int64_t>(part) * p.num_slices + (o >> p.rank_shift)) *
+                                p.max_tokens + t) * p.rank + (o & (p.rank - 1));
+          store16(dst, u32x4{0u, 0u, 0u, 0u});
+        }
+      }
+      continue;
+    }
+
+    // Source row of each piece this thread loads: x rows of the tile's tokens
+    // (a row without a token reads row 0: its outputs are never stored), then
+    // A rows of the group's outputs (an output past the last reads the last).
+    const uint16_t* src[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int r = row0 + 32 * j;
+      if (r < kLdsTile) {
+        const int t = tile_token(p.sorted, tile.first, tile.rows, r, p.max_tokens);
+        src[j] = p.x + static_cast<int64_t>(t >= 0 ? t : 0) * p.ldx;
+      } else {
+        int o = o0 + (r - kLdsTile);
+        o = o < nout ? o : nout - 1;
+        src[j] = slice_a[o >> p.rank_shift] +
+                 (static_cast<int64_t>(tile.lora) * p.rank + (o & (p.rank - 1))) * p.hidden;
+      }
+    }
+    // x pieces past the part's end are zeroed (the A piece beside them stays
+    // finite), so they add nothing.
+    auto gload = [&](int kc, u32x4 (&v)[kJ]) {
+      const int k = kc + 8 * piece;
+      const bool in = k < kend;
+      const int kk = in ? k : kbeg;
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) v[j] = load16(src[j] + kk);
+      if (kc + kShrinkChunk > kend) {  // wave-uniform: tail chunk only
+        const uint32_t mk = opaque_mask(in);
+#pragma unroll
+        for (int j = 0; j < kJ; ++j)
+          if (row0 + 32 * j < kLdsTile) v[j] &= mk;
+      }
+    };
+    auto sstore = [&](int b, const u32x4 (&v)[kJ]) {
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const int r = row0 + 32 * j;
+        stage[b][r * 8 + (piece ^ (r & 7))] = v[j];
+      }
+    };
+
+    f32x4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int b) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int pc = 4 * i + grp;  // 16-byte piece holding elements [32i + 8*grp, +8)
+        const int xr = 16 * wave + col;
+        const u32x4 xv = stage[b][xr * 8 + (pc ^ (xr & 7))];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int ar = kLdsTile + 16 * nb + col;
+          const u32x4 av = stage[b][ar * 8 + (pc ^ (ar & 7))];
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, xv), acc[nb], 0, 0, 0);
+        }
+      }
+    };
+
+    const int nchunks = (kend - kbeg + kShrinkChunk - 1) / kShrinkChunk;
+    u32x4 ra[kJ], rb[kJ];
+    // (the previous unit ended on a barrier after its last read of stage)
+    gload(kbeg, ra);
+    if (nchunks > 1) gload(kbeg + kShrinkChunk, rb);
+    sstore(0, ra);
+    if (nchunks > 2) gload(kbeg + 2 * kShrinkChunk, ra);
+    __syncthreads();
+    for (int c = 0; c < nchunks; c += 2) {
+      compute(0);
+      if (c + 1 < nchunks) {
+        sstore(1, rb);
+        if (c + 3 < nchunks) gload(kbeg + (c + 3) * kShrinkChunk, rb);
+      }
+      __syncthreads();
+      if (c + 1 >= nchunks) break;
+      compute(1);
+      if (c + 2 < nchunks) {
+        sstore(0, ra);
+        if (c + 4 < nchunks) gload(kbeg + (c + 4) * kShrinkChunk, ra);
+      }
+      __syncthreads();
+    }
+
+    // D^T layout: this lane holds outputs o0 + 16*nb + 4*grp + j (j = 0..3) of
+    // token 16*wave + col of the tile; rank is a multiple of 8, so the four
+    // share a slice.
+    const int t = tile_token(p.sorted, tile.first, tile.rows, 16 * wave + col, p.max_tokens);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int o = o0 + 16 * nb + 4 * grp;
+      if (t >= 0 && o < nout) {
+        f32x4 v = acc[nb] * p.scale;
+        float* dst = p.buf + ((static_cast<int64_t>(part) * p.num_slices + (o >> p.rank_shift)) *
+                              p.max_tokens + t) * p.rank + (o & (p.rank - 1));
+        store16(dst, __builtin_bit_cast(u32x4, v));
+      }
+    }
+  }
+}
+
+template <int NB>
+hipError_t launch_shrink_lds_nb(const ShrinkParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((shrink_lds_kernel<NB>), dim3(grid), dim3(kShrinkThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int NB, int MW>
 hipError_t launch_shrink_nb(const ShrinkParams& p, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((shrink_kernel<NB, MW>), dim3(grid), dim3(kShrinkThreads), 0, stream, p);
@@ -258,16 +423,15 @@ hipError_t launch_shrink_mw(const ShrinkParams& p, int nb, int grid, hipStream_t
 // Output blocks per group: all of them up to 8 (128 outputs), else groups of 8.
 int shrink_group_blocks(int nb_total) { return nb_total <= 8 ? nb_total : 8; }
 
-// 16-token blocks per tile: one for small batches (more tiles in flight), four
-// for large ones so each A operand serves 64 tokens, fewer when there are many
-// output blocks, so that the accumulators and double-buffered operands fit in
-// registers without spilling.
+// 16-token blocks per tile: one for small batches (register kernel, more tiles
+// in flight, hidden split across the four waves), four (64-token tiles, the
+// LDS-staged kernel) for larger ones.
 int shrink_tile_blocks(int max_tokens, int nb) {
 #ifdef LORA_TUNING
   if (const char* e = getenv("LORA_SHRINK_MW")) return atoi(e);
 #endif
   if (max_tokens <= 512) return 1;
-  return nb <= 4 ? 4 : (nb <= 6 ? 2 : 1);
+  return 4;  // the LDS-staged kernel (64-token tiles)
 }
 
 int shrink_split_len(int hidden, int num_splits) {
@@ -312,11 +476,28 @@ hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint1
   const int nb = shrink_group_blocks(nb_total);
   p.num_groups = (nb_total + nb - 1) / nb;
   const int mw = shrink_tile_blocks(max_tokens, nb);
+  if (mw == 4) {
+    // large batch: LDS-staged kernel, 64-token tiles, at most 3 workgroups per
+    // CU (LDS), in whole rounds over the XCDs
+    const int64_t tiles = (static_cast<int64_t>(max_tokens) + kLdsTile - 1) / kLdsTile + max_loras;
+    int64_t g = tiles * num_splits * p.num_groups;
+    const int64_t cap = static_cast<int64_t>(num_cus) * 3;
+    g = g < cap ? g : cap;
+    const int grid = static_cast<int>((g + kXcds - 1) / kXcds * kXcds);
+    switch (nb) {
+      case 1: return launch_shrink_lds_nb<1>(p, grid, stream);
+      case 2: return launch_shrink_lds_nb<2>(p, grid, stream);
+      case 3: return launch_shrink_lds_nb<3>(p, grid, stream);
+      case 4: return launch_shrink_lds_nb<4>(p, grid, stream);
+      case 5:
+      case 6: return launch_shrink_lds_nb<6>(p, grid, stream);
+      default: return launch_shrink_lds_nb<8>(p, grid, stream);
+    }
+  }
   const int grid = shrink_grid(max_tokens, max_loras, num_splits, p.num_groups, mw, num_cus);
   switch (mw) {
     case 1: return launch_shrink_mw<1>(p, nb, grid, stream);
-    case 2: return launch_shrink_mw<2>(p, nb, grid, stream);
-    default: return launch_shrink_mw<4>(p, nb, grid, stream);
+    default: return launch_shrink_mw<2>(p, nb, grid, stream);
   }
 }
 

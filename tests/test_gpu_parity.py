@@ -141,8 +141,9 @@ def test_step_parity_full_size(cfg):
 
 @pytest.mark.parametrize("rank", [8, 16, 32, 64])
 @pytest.mark.parametrize("splits", [1, 5])
-def test_integer_exact_bitwise(rank, splits):
-    w = make_integer_exact_workload(100 + rank, 300, 328, [136, 40, 8], rank, 6,
+@pytest.mark.parametrize("T", [300, 700])  # batches up to 512 tokens and larger take different kernels
+def test_integer_exact_bitwise(rank, splits, T):
+    w = make_integer_exact_workload(100 + rank, T, 328, [136, 40, 8], rank, 6,
                                     scale=2.0 if rank == 16 else 1.0)
     d = H.upload(w, num_splits=splits)
     H.run_step(d)
@@ -162,6 +163,14 @@ SHAPES = [
     (96, 96, 512, [64, 64, 64], 64, 2, 16, 0, 2),
     (500, 512, 2048, [1024], 64, 256, 0, 0, 4),
     (33, 33, 128, [16, 16, 16, 16], 8, 7, 0, 0, 7),
+    # more than 512 token slots: the LDS-staged shrink, every output-group width
+    (600, 640, 72, [8], 8, 1, 0, 0, 1),
+    (700, 700, 264, [40, 136], 16, 3, 8, 16, 3),
+    (600, 600, 200, [32, 32, 32], 16, 4, 0, 0, 1),
+    (1030, 1100, 512, [64, 64, 64], 64, 2, 16, 0, 2),
+    (900, 1024, 320, [64, 64, 64], 32, 9, 8, 8, 5),
+    (777, 800, 1032, [128, 8, 24, 200], 32, 5, 0, 8, 64),
+    (2000, 2048, 2048, [1024], 64, 256, 0, 0, 4),
 ]
 
 
