@@ -5,8 +5,9 @@ one synthetic batch.  Inputs are resident in HBM before timing starts.  To keep
 the 256 MB Infinity Cache from serving repeats, R copies of every buffer (at
 least 1 GiB in total) are rotated: one HIP graph holds R consecutive steps, each
 on its own copy.  Per-kernel launch durations for the roofline figure are
-measured the same way (a graph of R launches of one kernel), with HIP events on
-the stream the graph is replayed on.  The CPU oracle is timed on the host's
+measured the same way (a graph of launches of one kernel, over enough copies
+that the kernel's own buffers span 1 GiB), with HIP events on the stream the
+graph is replayed on.  The CPU oracle is timed on the host's
 cores on the same batch, as a reported baseline.
 
 Prints exactly one JSON line on stdout (progress goes to stderr).
@@ -28,6 +29,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
 CPU_BUDGET_S = 10.0      # the CPU baseline runs full batches for about this long
 ROTATE_BYTES = 1 << 30
+ROTATE_CAP = 48 << 30    # device memory the rotated copies may take in all
+ROTATE_MAX_SETS = 512
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "segmented_rank_gemm_amd", "csrc")
 # sources a kernel's measured traffic depends on
@@ -103,19 +106,29 @@ class Sets:
             a=[to_dev_bf16(a) for a in w.lora_a],
             b=[to_dev_bf16(b) for b in w.lora_b],
         )
+        self.base = base
         self.sets = []
-        for r in range(R):
+        self.T = T
+        self.grow(R)
+
+    def grow(self, R):
+        """Add copies up to R in total; the metadata of new copies is computed."""
+        import torch
+
+        import segmented_rank_gemm_amd as srg
+        w, base, maxT = self.w, self.base, self.w.max_tokens
+        while len(self.sets) < R:
             s = dict(
                 mapping=base["mapping"].clone(), x=base["x"].clone(), y=base["y"].clone(),
                 a=[t.clone() for t in base["a"]], b=[t.clone() for t in base["b"]],
                 meta=srg.LoraMeta(maxT, w.max_loras),
-                buf=torch.zeros((num_splits, w.num_slices, maxT, w.rank), dtype=torch.float32,
-                                device="cuda"),
+                buf=torch.zeros((self.num_splits, w.num_slices, maxT, w.rank),
+                                dtype=torch.float32, device="cuda"),
             )
             self.sets.append(s)
-        del base
+            self.metadata(len(self.sets) - 1)
+        self.R = len(self.sets)
         torch.cuda.synchronize()
-        self.T = T
 
     def metadata(self, r, stream=None):
         import segmented_rank_gemm_amd as srg
@@ -144,6 +157,23 @@ def set_bytes(w, num_splits):
     return (maxT * w.hidden * 2 + maxT * w.n_total * 2 + w.num_tokens * 4 + maxT * 4
             + sum(a.nbytes for a in w.lora_a) + sum(b.nbytes for b in w.lora_b)
             + num_splits * w.num_slices * maxT * w.rank * 4)
+
+
+def kernel_set_bytes(w, num_splits):
+    """Bytes of one buffer copy that each kernel touches (its share of set_bytes)."""
+    maxT = w.max_tokens
+    buf = num_splits * w.num_slices * maxT * w.rank * 4
+    shrink = maxT * w.hidden * 2 + sum(a.nbytes for a in w.lora_a) + buf
+    expand = maxT * w.n_total * 2 + sum(b.nbytes for b in w.lora_b) + buf
+    return {"metadata": w.num_tokens * 4 + maxT * 4, "shrink": shrink, "expand": expand,
+            "pair": shrink + expand - buf}
+
+
+def rotation(nbytes, set_total, floor):
+    """Copies needed for nbytes per copy to span ROTATE_BYTES, within ROTATE_CAP of
+    memory and ROTATE_MAX_SETS launches per graph."""
+    want = max(floor, math.ceil(ROTATE_BYTES / max(nbytes, 1)))
+    return max(floor, min(want, ROTATE_CAP // max(set_total, 1), ROTATE_MAX_SETS))
 
 
 def capture(fn_list):
@@ -251,27 +281,36 @@ def run_config(idx, args):
     gpu_s = start.elapsed_time(end) / 1e3
     step_s = wall / steps
 
-    # single-kernel graphs: average launch duration of each kernel, same rotation
+    # single-kernel graphs: average launch duration of each kernel over enough
+    # copies that the kernel's own buffers span ROTATE_BYTES (so the Infinity
+    # Cache cannot serve a repeat), more copies than the step needs when the
+    # kernel touches only part of a set
     reps = args.kernel_reps
     log("[bench] per-kernel timing")
+    kb = kernel_set_bytes(w, splits)
+    # (the metadata kernel reads a few KB per copy: it is timed over the step's copies)
+    rot = {k: (R if k == "metadata" else rotation(kb[k], sb, R)) for k in kb}
+    sets.grow(max(rot.values()))
     per = {}
-    for name in ("metadata", "shrink", "expand"):
-        g = capture([lambda s, r=r, f=getattr(sets, name): f(r, s) for r in range(R)])
-        per[name] = time_graph(g, reps) / R
+    fns = {"metadata": sets.metadata, "shrink": sets.shrink, "expand": sets.expand,
+           "pair": lambda r, s: (sets.shrink(r, s), sets.expand(r, s))}
+    for name in ("metadata", "shrink", "expand", "pair"):
+        n = rot[name]
+        g = capture([lambda s, r=r, f=fns[name]: f(r, s) for r in range(n)])
+        per[name] = time_graph(g, reps) / n
         del g
-    pair_g = capture([lambda s, r=r: (sets.shrink(r, s), sets.expand(r, s)) for r in range(R)])
-    pair_s = time_graph(pair_g, reps) / R
-    del pair_g
+    pair_s = per.pop("pair")
 
     # practical ceilings for the expand's bytes, same rotation: a copy between
     # two buffers, and an in-place update of one (the expand's access pattern)
     cb = (st["expand_bytes"] // 2) // 16 * 16
-    srcs = [torch.empty(cb, dtype=torch.uint8, device="cuda") for _ in range(R)]
-    dsts = [torch.empty(cb, dtype=torch.uint8, device="cuda") for _ in range(R)]
-    g_copy = capture([lambda s, r=r: srg.lora_stream_copy(srcs[r], dsts[r], s) for r in range(R)])
-    copy_s = time_graph(g_copy, reps) / R
-    g_upd = capture([lambda s, r=r: srg.lora_stream_update(srcs[r], s) for r in range(R)])
-    upd_s = time_graph(g_upd, reps) / R
+    Rc = rot["expand"]
+    srcs = [torch.empty(cb, dtype=torch.uint8, device="cuda") for _ in range(Rc)]
+    dsts = [torch.empty(cb, dtype=torch.uint8, device="cuda") for _ in range(Rc)]
+    g_copy = capture([lambda s, r=r: srg.lora_stream_copy(srcs[r], dsts[r], s) for r in range(Rc)])
+    copy_s = time_graph(g_copy, reps) / Rc
+    g_upd = capture([lambda s, r=r: srg.lora_stream_update(srcs[r], s) for r in range(Rc)])
+    upd_s = time_graph(g_upd, reps) / Rc
     del g_copy, g_upd, srcs, dsts
 
     exp_bytes = st["expand_bytes"]
@@ -295,7 +334,7 @@ def run_config(idx, args):
             "active_tokens": st["active_tokens"], "hidden": w.hidden, "slices": w.slices,
             "rank": w.rank, "max_loras": w.max_loras, "active_adapters": st["active_adapters"],
             "scale": w.scale, "accumulate": "fp32", "shrink_parts": splits,
-            "rotated_sets": R, "parallelism": "single GPU",
+            "rotated_sets": R, "rotated_sets_per_kernel": rot, "parallelism": "single GPU",
         },
         "roofline": {
             "bound": "hbm", "kernel": "lora_expand", "achieved": achieved,

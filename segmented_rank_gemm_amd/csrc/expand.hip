@@ -76,17 +76,28 @@ struct YBlock {
   u32x4 v[4];
 };
 
-// B operand of one 128-column chunk: block b, MFMA step q.
+// One 128-column chunk of B (128 rows of RANK bf16, 256*RANK contiguous
+// bytes) as this lane loads it: 16-byte pieces lane, lane + 64, ... of the
+// chunk, so that every load instruction reads 1 KB of whole cache lines.  The
+// wave then passes the chunk through its own LDS region to reach the MFMA
+// operand layout, in which lane (c, g) needs row 8c + b of every block b: read
+// straight from global memory, each instruction would touch 16 lines for 8 or
+// 16 bytes each.
 template <int RANK>
-struct BChunk;
-template <>
-struct BChunk<8> {
-  u32x2 w[8][1];
+struct BStage {
+  static constexpr int kPieces = RANK / 4;  // 16-byte pieces per lane
+  u32x4 v[kPieces];
 };
+
+// LDS slot of 16-byte piece pr of chunk row `row` (RANK / 8 pieces per row):
+// row-major, with the low three bits XOR-ed by (row / 8) % 8, so that the 16
+// lanes reading rows 8c + b (c = 0..15) of one block spread over the banks.
+// The XOR leaves the bits that hold row / 8 unchanged: a bijection on the
+// region's 16 * RANK slots.
 template <int RANK>
-struct BChunk {
-  u32x4 w[8][RANK / 16];
-};
+__device__ __forceinline__ int bslot(int row, int pr) {
+  return (row * (RANK / 8) + pr) ^ ((row >> 3) & 7);
+}
 
 // MW = 16-token blocks per tile; every block shares the B operand loads.
 //
@@ -106,6 +117,7 @@ void expand_kernel(ExpandParams p) {
   constexpr int kOpWords = RANK == 8 ? 2 : 4;  // 32-bit words per lane per MFMA step
   __shared__ SlotTable tab;
   __shared__ uint32_t a_lds[MW][kSteps][kOpWords][kWave];
+  __shared__ u32x4 b_lds[kExpandWaves][16 * RANK];  // one B chunk per wave
 
   const int lane = lane_id();
   const int wave = wave_index();
@@ -173,23 +185,28 @@ void expand_kernel(ExpandParams p) {
     auto bmat_of = [&](int slot) {
       return bslice + static_cast<int64_t>(tab.lora[slot]) * n_s * RANK;
     };
-    auto load_b = [&](const uint16_t* bmat, int ch, BChunk<RANK>& bc) {
-      const int col = ch * kExpandCols + 8 * c;
-      const int colc = col < n_s ? col : n_s - 8;  // n_s is a multiple of 8
+    // B chunk: piece q = lane + 64 i is piece q % (RANK/8) of chunk row
+    // q / (RANK/8); rows past the slice's end read its last row (their columns
+    // are never stored).
+    constexpr int kRowPieces = RANK / 8;
+    auto load_b = [&](const uint16_t* bmat, int ch, BStage<RANK>& bs) {
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const uint16_t* brow = bmat + static_cast<int64_t>(colc + b) * RANK;
-        if constexpr (RANK == 8) {
-          bc.w[b][0] = load8(brow + 4 * khalf);
-        } else {
+      for (int i = 0; i < BStage<RANK>::kPieces; ++i) {
+        const int q = lane + kWave * i;
+        const int row = ch * kExpandCols + q / kRowPieces;
+        const int rowc = row < n_s ? row : n_s - 1;
+        bs.v[i] = load16(bmat + static_cast<int64_t>(rowc) * RANK + 8 * (q % kRowPieces));
+      }
+    };
+    u32x4* const bw = b_lds[wave];
+    auto stage_b = [&](const BStage<RANK>& bs) {
 #pragma unroll
-          for (int q = 0; q < kSteps; ++q) bc.w[b][q] = load16(brow + 16 * q + 8 * khalf);
-        }
+      for (int i = 0; i < BStage<RANK>::kPieces; ++i) {
+        const int q = lane + kWave * i;
+        bw[bslot<RANK>(q / kRowPieces, q % kRowPieces)] = bs.v[i];
       }
     };
     const uint16_t* bmat0 = bmat_of(sr.first);
-    BChunk<RANK> bcur, bnext;
-    if (ch0 < range_end) load_b(bmat0, ch0, bcur);
 
     // y rows (a row without an adapter reads row 0 and is never stored) and
     // the grouped position of each output row.
@@ -212,8 +229,15 @@ void expand_kernel(ExpandParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) yb[mb].v[j] = load16_stream(p.y + yrow[mb][j] + colc);
     };
+    // First chunk: y, then B, then (below) the shrink's parts, all issued
+    // unconditionally (a wave without a chunk in this range reads the range's
+    // last one and stores nothing), so that the compiler's wait counts stay
+    // exact and no load waits for another.
+    const int chf = ch0 < range_end ? ch0 : range_end - 1;
     YBlock ycur[MW], ynext[MW];
-    if (ch0 < range_end) load_y(ch0, ycur);
+    load_y(chf, ycur);
+    BStage<RANK> bnext;
+    load_b(bmat0, chf, bnext);
 
     // Rank operand, built cooperatively: item (mb, q) is one MFMA step of one
     // block, i.e. one register set of the wave; its lane (c, grp) sums the
@@ -277,9 +301,9 @@ void expand_kernel(ExpandParams p) {
       }
     __syncthreads();  // the next unit may overwrite a_lds
 
-    // One slot's pass over one chunk: acc = y + buf . B^T, stored for the rows
-    // of that slot.
-    auto pass = [&](const BChunk<RANK>& bc, int ch, int s_begin, int s_end) {
+    // One slot's pass over one chunk (its B in this wave's LDS region): acc =
+    // y + buf . B^T, stored for the rows of that slot.
+    auto pass = [&](int ch, int s_begin, int s_end) {
       const int col = ch * kExpandCols + 8 * c;  // first of this lane's 8 columns
       const bool col_ok = col < n_s;
 #pragma unroll
@@ -298,12 +322,15 @@ void expand_kernel(ExpandParams p) {
         for (int b = 0; b < 8; ++b) {
 #pragma unroll
           for (int q = 0; q < kSteps; ++q) {
+            // lane (c, g): row 8c + b, ranks 16q + 8*khalf.. (rank 8: 4*khalf..)
             if constexpr (RANK == 8) {
+              const u32x2 w = reinterpret_cast<const u32x2*>(bw + bslot<RANK>(8 * c + b, 0))[khalf];
               acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                  a[mb].op[q], __builtin_bit_cast(i16x4, bc.w[b][0]), acc[b], 0, 0, 0);
+                  a[mb].op[q], __builtin_bit_cast(i16x4, w), acc[b], 0, 0, 0);
             } else {
+              const u32x4 w = bw[bslot<RANK>(8 * c + b, 2 * q + khalf)];
               acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  a[mb].op[q], __builtin_bit_cast(bf16x8, bc.w[b][q]), acc[b], 0, 0, 0);
+                  a[mb].op[q], __builtin_bit_cast(bf16x8, w), acc[b], 0, 0, 0);
             }
           }
         }
@@ -319,27 +346,33 @@ void expand_kernel(ExpandParams p) {
       }
     };
 
-    for (int ch = ch0; ch < range_end; ch += kExpandWaves) {
-      const bool more = ch + kExpandWaves < range_end;
-      if (more) {
-        load_y(ch + kExpandWaves, ynext);
-        if constexpr (RANK <= 32) load_b(bmat0, ch + kExpandWaves, bnext);
-      }
-      pass(bcur, ch, tab.start[sr.first], tab.end[sr.first]);
-      // Rare: a tile across adapters.  bcur is free after the first pass.
+    // All passes over one chunk: the first slot with its B already in LDS,
+    // then (a tile across adapters) one B load and pass per further slot.  The
+    // wave's own LDS reads and writes stay in program order, so the region can
+    // be refilled right after a pass.
+    auto passes = [&](int ch) {
+      pass(ch, tab.start[sr.first], tab.end[sr.first]);
       for (int slot = sr.first + 1; slot <= sr.last; ++slot) {
-        load_b(bmat_of(slot), ch, bcur);
-        pass(bcur, ch, tab.start[slot], tab.end[slot]);
+        BStage<RANK> bx;
+        load_b(bmat_of(slot), ch, bx);
+        stage_b(bx);
+        pass(ch, tab.start[slot], tab.end[slot]);
       }
-      if (more) {
+    };
+    stage_b(bnext);
+    if (ch0 < range_end) {  // wave-uniform
+      // Steady state: the next chunk's loads are issued unconditionally before
+      // this chunk's passes; the last chunk is peeled off.
+      int ch = ch0;
+      for (; ch + kExpandWaves < range_end; ch += kExpandWaves) {
+        load_y(ch + kExpandWaves, ynext);
+        load_b(bmat0, ch + kExpandWaves, bnext);
+        passes(ch);
 #pragma unroll
         for (int mb = 0; mb < MW; ++mb) ycur[mb] = ynext[mb];
-        if constexpr (RANK <= 32) {
-          bcur = bnext;
-        } else {
-          load_b(bmat0, ch + kExpandWaves, bcur);
-        }
+        stage_b(bnext);
       }
+      passes(ch);
     }
   }
 }

@@ -148,23 +148,27 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
       }
     };
 
-    // The first A chunk does not depend on the gathered token ids: issue it
-    // before waiting for them.
+    // This wave's chunks: kc, kc + kStride, ... below kend.  Every load below
+    // is issued unconditionally (a wave without a chunk reads the part's first
+    // one and adds nothing), so the compiler's wait counts stay exact and no
+    // load waits for a later one.  The token ids go first, then the first A
+    // chunk (which does not depend on them), then the first x chunk.
     constexpr int kStride = kShrinkWaves * kShrinkChunk;
     int kc = kbeg + wave * kShrinkChunk;
-    Chunk c0, c1;
-    if (kc < kend) load_a(kc, c0);
-
+    const int nw = kc < kend ? (kend - kc + kStride - 1) / kStride : 0;  // wave-uniform
+    kc = kc < kend ? kc : kbeg;
     int tok[MW];
 #pragma unroll
     for (int mb = 0; mb < MW; ++mb)
       tok[mb] = tile_token(p.sorted, tile.first, tile.rows, 16 * mb + col, p.max_tokens);
+    Chunk c0, c1;
+    load_a(kc, c0);
 #pragma unroll
     for (int mb = 0; mb < MW; ++mb) {
       xrow[mb] = p.x + static_cast<int64_t>(tok[mb] >= 0 ? tok[mb] : 0) * p.ldx;
       xmask[mb] = opaque_mask(tok[mb] >= 0);
     }
-    if (kc < kend) load_x(kc, c0);
+    load_x(kc, c0);
 
     f32x4 acc[MW][NB];
 #pragma unroll
@@ -190,21 +194,17 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
       }
     };
 
-    // Double-buffered walk over this wave's chunks (every kShrinkWaves-th one).
-    while (kc < kend) {
-      if (kc + kStride < kend) {
+    // Double-buffered walk over this wave's chunks: the next chunk's loads are
+    // issued before this chunk's matrix-core ops; the last chunk is peeled off.
+    if (nw > 0) {
+      for (int i = 1; i < nw; ++i) {
         load_a(kc + kStride, c1);
         load_x(kc + kStride, c1);
+        mma(c0);
+        c0 = c1;
+        kc += kStride;
       }
       mma(c0);
-      kc += kStride;
-      if (kc >= kend) break;
-      if (kc + kStride < kend) {
-        load_a(kc + kStride, c0);
-        load_x(kc + kStride, c0);
-      }
-      mma(c1);
-      kc += kStride;
     }
 
     // Sum the four waves' partial sums in a fixed order, one 16-token block at a
@@ -284,6 +284,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_lds_kernel(ShrinkParams
     if (kbeg >= kend) {
       // an empty part still owes its (zero) contribution
       const int t = tile_token(p.sorted, tile.first, tile.rows, 16 * wave + col, p.max_tokens);
+#pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int o = o0 + 16 * nb + 4 * grp;
         if (t >= 0 && o < nout) {
@@ -295,6 +296,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_lds_kernel(ShrinkParams
       continue;
     }
 
+    const int t = tile_token(p.sorted, tile.first, tile.rows, 16 * wave + col, p.max_tokens);
     // Source row of each piece this thread loads: x rows of the tile's tokens
     // (a row without a token reads row 0: its outputs are never stored), then
     // A rows of the group's outputs (an output past the last reads the last).
@@ -312,38 +314,38 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_lds_kernel(ShrinkParams
                  (static_cast<int64_t>(tile.lora) * p.rank + (o & (p.rank - 1))) * p.hidden;
       }
     }
-    // x pieces past the part's end are zeroed (the A piece beside them stays
-    // finite), so they add nothing.
-    auto gload = [&](int kc, u32x4 (&v)[kJ]) {
-      const int k = kc + 8 * piece;
-      const bool in = k < kend;
-      const int kk = in ? k : kbeg;
-#pragma unroll
-      for (int j = 0; j < kJ; ++j) v[j] = load16(src[j] + kk);
-      if (kc + kShrinkChunk > kend) {  // wave-uniform: tail chunk only
-        const uint32_t mk = opaque_mask(in);
-#pragma unroll
-        for (int j = 0; j < kJ; ++j)
-          if (row0 + 32 * j < kLdsTile) v[j] &= mk;
-      }
+    // Chunk c of the part (clamped to the last, so that every load is issued
+    // unconditionally and the compiler's wait counts stay exact).  A piece
+    // past the part's end reads the part's first piece instead; the x operand
+    // of such a piece is zeroed when it is read from LDS, so it adds nothing.
+    const int nchunks = (kend - kbeg + kShrinkChunk - 1) / kShrinkChunk;
+    struct Staged {
+      u32x4 v[kJ];
     };
-    auto sstore = [&](int b, const u32x4 (&v)[kJ]) {
+    auto gload = [&](int c, Staged& st) {
+      const int k = kbeg + (c < nchunks ? c : nchunks - 1) * kShrinkChunk + 8 * piece;
+      const int kk = k < kend ? k : kbeg;
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) st.v[j] = load16(src[j] + kk);
+    };
+    auto sstore = [&](int b, const Staged& st) {
 #pragma unroll
       for (int j = 0; j < kJ; ++j) {
         const int r = row0 + 32 * j;
-        stage[b][r * 8 + (piece ^ (r & 7))] = v[j];
+        stage[b][r * 8 + (piece ^ (r & 7))] = st.v[j];
       }
     };
 
     f32x4 acc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](int b) {
+    auto compute = [&](int b, int c) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int pc = 4 * i + grp;  // 16-byte piece holding elements [32i + 8*grp, +8)
         const int xr = 16 * wave + col;
-        const u32x4 xv = stage[b][xr * 8 + (pc ^ (xr & 7))];
+        const uint32_t in = kbeg + c * kShrinkChunk + 8 * pc < kend ? 0xFFFFFFFFu : 0u;
+        const u32x4 xv = stage[b][xr * 8 + (pc ^ (xr & 7))] & in;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const int ar = kLdsTile + 16 * nb + col;
@@ -354,34 +356,37 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_lds_kernel(ShrinkParams
       }
     };
 
-    const int nchunks = (kend - kbeg + kShrinkChunk - 1) / kShrinkChunk;
-    u32x4 ra[kJ], rb[kJ];
-    // (the previous unit ended on a barrier after its last read of stage)
-    gload(kbeg, ra);
-    if (nchunks > 1) gload(kbeg + kShrinkChunk, rb);
+    // Two chunks in flight in registers ahead of the one computed.  Chunks go
+    // in pairs (LDS buffer 0, then 1) with one exit test per pair, so that
+    // every path into a wait has the same loads outstanding; loads and LDS
+    // stores past the last chunk repeat it into a buffer no one reads any
+    // more.  An odd last chunk sits in buffer 0.  (The previous unit ended on
+    // a barrier after its last read of stage.)
+    Staged ra, rb;
+    gload(0, ra);
+    gload(1, rb);
     sstore(0, ra);
-    if (nchunks > 2) gload(kbeg + 2 * kShrinkChunk, ra);
+    gload(2, ra);
     __syncthreads();
-    for (int c = 0; c < nchunks; c += 2) {
-      compute(0);
-      if (c + 1 < nchunks) {
-        sstore(1, rb);
-        if (c + 3 < nchunks) gload(kbeg + (c + 3) * kShrinkChunk, rb);
-      }
+    int c = 0;
+    for (; c + 2 <= nchunks; c += 2) {
+      compute(0, c);
+      sstore(1, rb);
+      gload(c + 3, rb);
       __syncthreads();
-      if (c + 1 >= nchunks) break;
-      compute(1);
-      if (c + 2 < nchunks) {
-        sstore(0, ra);
-        if (c + 4 < nchunks) gload(kbeg + (c + 4) * kShrinkChunk, ra);
-      }
+      compute(1, c + 1);
+      sstore(0, ra);
+      gload(c + 4, ra);
+      __syncthreads();
+    }
+    if (c < nchunks) {
+      compute(0, c);
       __syncthreads();
     }
 
     // D^T layout: this lane holds outputs o0 + 16*nb + 4*grp + j (j = 0..3) of
     // token 16*wave + col of the tile; rank is a multiple of 8, so the four
     // share a slice.
-    const int t = tile_token(p.sorted, tile.first, tile.rows, 16 * wave + col, p.max_tokens);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int o = o0 + 16 * nb + 4 * grp;
