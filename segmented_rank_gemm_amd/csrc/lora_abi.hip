@@ -92,9 +92,9 @@ int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t m
     return 0;
   // Enough (tile, part, output group) units for ~1 workgroup per CU of a
   // 256-CU device at the largest batch, with parts of at least 256 hidden
-  // elements.  Small batches (16-token tiles): no more parts than the expand
-  // sums with one batch of loads (16 for rank 8, else 8) and parts * rank <=
-  // 256 (at most 1 KB of parts per token).  Large batches (64-token tiles):
+  // elements.  Small batches (16-token tiles): ~2 units per CU, but no more
+  // parts than the expand sums with one batch of loads (16 for rank 8, else 8)
+  // and parts * rank <= 256 (at most 1 KB of parts per token).  Large batches (64-token tiles):
   // also parts of about 1024 elements, so that several workgroups share each
   // CU, up to 8 parts (a second batch of loads in the expand at rank 64 costs
   // far less than the shrink gains).
@@ -107,6 +107,7 @@ int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t m
   int64_t splits = (256 + tiles * groups - 1) / (tiles * groups);
   const int64_t by_len = hidden / 256 > 0 ? hidden / 256 : 1;
   int64_t cap;
+  if (mw != 4) splits = (512 + tiles * groups - 1) / (tiles * groups);
   if (mw == 4) {
     const int64_t by_work = (hidden + 1023) / 1024;
     splits = splits > by_work ? splits : by_work;

@@ -115,8 +115,11 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
       u32x4 a[NB][2];
       uint32_t kmask[2];  // pieces inside the part (all ones except in a tail chunk)
     };
-    // A chunk that runs past the part's end re-reads its first piece and masks
-    // (kend is a multiple of 8, so a piece is wholly in or out).
+    // A chunk that runs past the part's end re-reads a piece inside the row
+    // and masks (kend is a multiple of 8, so a piece is wholly in or out): the
+    // part's first piece, or for an empty part (kbeg >= hidden, possible when
+    // num_splits * split_len > hidden) the row's first.
+    const int ksafe = kbeg < kend ? kbeg : 0;
     auto piece = [&](int kc, int i, bool full, uint32_t& km) {
       const int k = kc + 32 * i + 8 * grp;
       if (full) {
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
         return k;
       }
       km = opaque_mask(k < kend);
-      return k < kend ? k : kbeg;
+      return k < kend ? k : ksafe;
     };
     auto load_a = [&](int kc, Chunk& c) {
       const bool full = kc + kShrinkChunk <= kend;  // wave-uniform
@@ -149,14 +152,14 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
     };
 
     // This wave's chunks: kc, kc + kStride, ... below kend.  Every load below
-    // is issued unconditionally (a wave without a chunk reads the part's first
-    // one and adds nothing), so the compiler's wait counts stay exact and no
-    // load waits for a later one.  The token ids go first, then the first A
+    // is issued unconditionally (a wave without a chunk reads a chunk at ksafe,
+    // inside every row, and adds nothing), so the compiler's wait counts stay
+    // exact and no load waits for a later one.  The token ids go first, then the first A
     // chunk (which does not depend on them), then the first x chunk.
     constexpr int kStride = kShrinkWaves * kShrinkChunk;
     int kc = kbeg + wave * kShrinkChunk;
     const int nw = kc < kend ? (kend - kc + kStride - 1) / kStride : 0;  // wave-uniform
-    kc = kc < kend ? kc : kbeg;
+    kc = kc < kend ? kc : ksafe;
     int tok[MW];
 #pragma unroll
     for (int mb = 0; mb < MW; ++mb)
@@ -194,17 +197,32 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
       }
     };
 
-    // Double-buffered walk over this wave's chunks: the next chunk's loads are
-    // issued before this chunk's matrix-core ops; the last chunk is peeled off.
+    // Double-buffered walk over this wave's chunks, alternating two register
+    // sets (no copies, which would make the compiler wait for one set's loads
+    // before reusing its registers); the scheduling barriers keep each chunk's
+    // loads ahead of the previous chunk's matrix-core ops, which wait for that
+    // chunk's data.
     if (nw > 0) {
-      for (int i = 1; i < nw; ++i) {
-        load_a(kc + kStride, c1);
-        load_x(kc + kStride, c1);
+      int j = 0;
+      for (; j + 2 < nw; j += 2) {
+        load_a(kc + (j + 1) * kStride, c1);
+        load_x(kc + (j + 1) * kStride, c1);
+        __builtin_amdgcn_sched_barrier(0);
         mma(c0);
-        c0 = c1;
-        kc += kStride;
+        load_a(kc + (j + 2) * kStride, c0);
+        load_x(kc + (j + 2) * kStride, c0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(c1);
       }
-      mma(c0);
+      if (j + 1 < nw) {
+        load_a(kc + (j + 1) * kStride, c1);
+        load_x(kc + (j + 1) * kStride, c1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(c0);
+        mma(c1);
+      } else {
+        mma(c0);
+      }
     }
 
     // Sum the four waves' partial sums in a fixed order, one 16-token block at a

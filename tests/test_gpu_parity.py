@@ -185,6 +185,16 @@ def test_shape_sweep(T, maxT, hidden, slices, rank, L, ldx_pad, ldy_pad, splits)
     _full_check(w, d)
 
 
+def test_empty_parts_decode_shape():
+    # 20 parts of 256 over hidden 4096: parts 16..19 hold no columns, and their
+    # loads must stay inside x and A (both end exactly where the data ends).
+    w = make_workload(1)
+    d = H.upload(w, num_splits=20)
+    H.run_step(d)
+    torch.cuda.synchronize()
+    _full_check(w, d)
+
+
 @pytest.mark.parametrize("kind", ["empty", "all_none", "single", "one_token"])
 def test_degenerate_batches(kind):
     T = {"empty": 0, "all_none": 50, "single": 80, "one_token": 1}[kind]
