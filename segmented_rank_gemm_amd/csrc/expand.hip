@@ -377,15 +377,232 @@ void expand_kernel(ExpandParams p) {
   }
 }
 
+// Ranks 32 and 64: the B operand of a chunk (8 or 16 KB) outweighs the y bytes
+// of a 16-token block, so the four waves of a workgroup work on the same chunk
+// and share its B.  A unit is (tile of up to 64 grouped tokens cut from one
+// adapter's segment, slice s, range of cpr chunks); wave w owns rows 16w..16w+15
+// of the tile.  Per chunk the workgroup loads B once, in whole-line 16-byte
+// pieces, into a double-buffered XOR-swizzled LDS region (two chunks ahead);
+// each wave keeps its y block (one chunk ahead) and its rank operand in
+// registers.  Rows past the tile's end read the tile's first row and are
+// never stored.
+constexpr int kSharedTile = 64;
+
+template <int RANK>
+__global__ __launch_bounds__(kExpandThreads) __attribute__((amdgpu_waves_per_eu(1)))
+void expand_shared_kernel(ExpandParams p) {
+  constexpr int kSteps = RANK / 16;
+  constexpr int kRowPieces = RANK / 8;           // 16-byte pieces per B row
+  constexpr int kPieces = 16 * RANK / kExpandThreads;  // per thread per chunk
+  __shared__ SegmentTable tab;
+  __shared__ u32x4 b_lds[2][16 * RANK];
+
+  build_segment_table<kSharedTile>(tab, p.active_ids, p.counts, p.starts, p.num_active,
+                                   p.max_loras, p.max_tokens);
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = wave_index();
+  const int c = lane & 15;
+  const int grp = lane >> 4;
+  const int khalf = grp & 1;
+  const bool use_lo = grp >= 2;
+  const int cpr = p.chunks_per_range;
+  const int num_tiles = tab.num_tiles;
+  const int units = num_tiles * p.range_end[p.num_slices - 1];
+
+  for (XcdWalk walk = xcd_walk(units, gridDim.x); walk.next < walk.end; walk.next += walk.step) {
+    const int u = walk.next;
+    const int m = u % num_tiles;  // tiles fastest: neighbouring units share B in one L2
+    const int cr = u / num_tiles;
+    const Tile tile = resolve_tile<kSharedTile>(tab, m);
+
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < LORA_MAX_SLICES - 1; ++i) s += (i < p.num_slices - 1 && cr >= p.range_end[i]) ? 1 : 0;
+    int n_s = p.n[0], off_s = p.off[0], r_before = 0;
+    const uint16_t* bslice = p.b[0];
+#pragma unroll
+    for (int i = 1; i < LORA_MAX_SLICES; ++i) {
+      if (s == i) {
+        n_s = p.n[i];
+        off_s = p.off[i];
+        r_before = p.range_end[i - 1];
+        bslice = p.b[i];
+      }
+    }
+    const int chunks_s = (n_s + kExpandCols - 1) / kExpandCols;
+    const int ch0 = (cr - r_before) * cpr;
+    const int nch = min(chunks_s, ch0 + cpr) - ch0;  // >= 1
+    const uint16_t* bmat = bslice + static_cast<int64_t>(tile.lora) * n_s * RANK;
+
+    // Token ids: the rank-operand row c and the output rows 4*grp + j of this
+    // wave's block.
+    const int r0 = 16 * wave;
+    const int tfirst = tile_token(p.sorted, tile.first, tile.rows, 0, p.max_tokens);
+    const int ta = tile_token(p.sorted, tile.first, tile.rows, r0 + c, p.max_tokens);
+    int td[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      td[j] = tile_token(p.sorted, tile.first, tile.rows, r0 + 4 * grp + j, p.max_tokens);
+    const int tsafe = tfirst >= 0 ? tfirst : 0;
+    int64_t yrow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      yrow[j] = static_cast<int64_t>(td[j] >= 0 ? td[j] : tsafe) * p.ldy + off_s;
+
+    auto load_y = [&](int ch, YBlock& yb) {
+      const int col = ch * kExpandCols + 8 * c;
+      const int colc = col < n_s ? col : n_s - 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) yb.v[j] = load16_stream(p.y + yrow[j] + colc);
+    };
+    struct BPieces {
+      u32x4 v[kPieces];
+    };
+    // piece q = tid + 256 i of the chunk: piece q % kRowPieces of row
+    // q / kRowPieces; rows past the slice's end read its last row.
+    auto load_b = [&](int ch, BPieces& bp) {
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) {
+        const int q = tid + kExpandThreads * i;
+        const int row = ch * kExpandCols + q / kRowPieces;
+        const int rowc = row < n_s ? row : n_s - 1;
+        bp.v[i] = load16(bmat + static_cast<int64_t>(rowc) * RANK + 8 * (q % kRowPieces));
+      }
+    };
+    auto stage_b = [&](int b, const BPieces& bp) {
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) {
+        const int q = tid + kExpandThreads * i;
+        b_lds[b][bslot<RANK>(q / kRowPieces, q % kRowPieces)] = bp.v[i];
+      }
+    };
+
+    const int last = ch0 + nch - 1;
+    YBlock ya, yb;
+    BPieces bp;
+    load_y(ch0, ya);
+    load_b(ch0, bp);
+
+    // Rank operand of this wave's rows: step q, lane (c, g) holds ranks
+    // 16q + 8*khalf .. +8 of row c, summed over the parts (loads of a group of
+    // 8 parts issued before the adds, adds in part order), as hi or lo bf16.
+    RankOperand<RANK> a;
+    {
+      const int64_t plane = static_cast<int64_t>(p.num_slices) * p.max_tokens * RANK;
+      const float* src0 =
+          p.buf + (static_cast<int64_t>(s) * p.max_tokens + (ta >= 0 ? ta : tsafe)) * RANK;
+#pragma unroll
+      for (int q = 0; q < kSteps; ++q) {
+        const int k0 = 16 * q + 8 * khalf;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        for (int sp0 = 0; sp0 < p.num_splits; sp0 += 8) {
+          uint32_t pm[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pm[i] = opaque_mask(sp0 + i < p.num_splits);
+          u32x4 w[8][2];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int sp = sp0 + i < p.num_splits ? sp0 + i : sp0;
+            w[i][0] = load16(src0 + sp * plane + k0);
+            w[i][1] = load16(src0 + sp * plane + k0 + 4);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += __uint_as_float(w[i][e >> 2][e & 3] & pm[i]);
+        }
+        uint32_t words[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const uint32_t hi = pack_bf16x2(v[e], v[e + 1]);
+          words[e / 2] = use_lo ? pack_bf16x2(v[e] - bf16_lo(hi), v[e + 1] - bf16_hi(hi)) : hi;
+        }
+        a.op[q] = __builtin_bit_cast(bf16x8, u32x4{words[0], words[1], words[2], words[3]});
+      }
+    }
+
+    // acc = y + buf . B^T for one chunk from LDS buffer b, stored for the
+    // wave's rows that hold a token and columns inside the slice.
+    auto pass = [&](int b, int ch, const YBlock& y) {
+      const int col = ch * kExpandCols + 8 * c;
+      const bool col_ok = col < n_s;
+      f32x4 acc[8];
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = y.v[j][bb >> 1];
+          acc[bb][j] = (bb & 1) ? bf16_hi(w) : bf16_lo(w);
+        }
+      }
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) {
+#pragma unroll
+        for (int q = 0; q < kSteps; ++q) {
+          const u32x4 w = b_lds[b][bslot<RANK>(8 * c + bb, 2 * q + khalf)];
+          acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.op[q], __builtin_bit_cast(bf16x8, w),
+                                                            acc[bb], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (col_ok && td[j] >= 0) {
+          const u32x4 out = {pack_bf16x2(acc[0][j], acc[1][j]), pack_bf16x2(acc[2][j], acc[3][j]),
+                             pack_bf16x2(acc[4][j], acc[5][j]), pack_bf16x2(acc[6][j], acc[7][j])};
+          store16_stream(p.y + yrow[j] + col, out);
+        }
+      }
+    };
+
+    // (The previous unit ended on a barrier after its last read of b_lds.)
+    stage_b(0, bp);
+    load_b(min(ch0 + 1, last), bp);
+    __syncthreads();
+    // Chunk i uses LDS buffer i % 2 and y set ya (even) or yb (odd); its B was
+    // staged one chunk earlier and its y loaded one chunk earlier.  Loads never
+    // run past the range's last chunk for y (B past it repeats the last chunk).
+    int i = 0;
+    for (; i + 2 < nch; i += 2) {
+      load_y(ch0 + i + 1, yb);
+      pass(0, ch0 + i, ya);
+      stage_b(1, bp);
+      load_b(min(ch0 + i + 2, last), bp);
+      __syncthreads();
+      load_y(ch0 + i + 2, ya);
+      pass(1, ch0 + i + 1, yb);
+      stage_b(0, bp);
+      load_b(min(ch0 + i + 3, last), bp);
+      __syncthreads();
+    }
+    if (i + 1 < nch) {
+      load_y(ch0 + i + 1, yb);
+      pass(0, ch0 + i, ya);
+      stage_b(1, bp);
+      __syncthreads();
+      pass(1, ch0 + i + 1, yb);
+      __syncthreads();
+    } else {
+      pass(0, ch0 + i, ya);
+      __syncthreads();
+    }
+  }
+}
+
+template <int RANK>
+hipError_t launch_expand_shared(const ExpandParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((expand_shared_kernel<RANK>), dim3(grid), dim3(kExpandThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int RANK, int MW>
 hipError_t launch_expand_rank(const ExpandParams& p, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((expand_kernel<RANK, MW>), dim3(grid), dim3(kExpandThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-// 16-token blocks per wave unit: two for rank >= 32, where the B operand of a
-// chunk (128 columns x rank) outweighs the y bytes of one block.
-int expand_tile_blocks(int rank) { return rank >= 32 ? 2 : 1; }
 
 hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const* lora_b,
                          const int32_t* slice_sizes, int num_slices, int rank, uint16_t* y,
@@ -410,21 +627,28 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
       p.off[s] = off;
     }
   }
-  // Chunks per wave in a workgroup unit (the unit spans 4x as many): as many as
-  // still give every CU ~16 units at the largest batch, at least 2 for rank >= 32
-  // (building the rank operand reads rank floats per token and part, to be
-  // amortised over the unit's y bytes), at most 8.
-  const int mw = expand_tile_blocks(rank);
-  const int64_t tiles = (static_cast<int64_t>(max_tokens) + kExpandTile * mw - 1) / (kExpandTile * mw);
-  int64_t cpr = tiles * total_chunks / (static_cast<int64_t>(num_cus) * 16);
-  const int64_t by_rank = rank >= 32 ? 2 : 1;
-  cpr = cpr > by_rank ? cpr : by_rank;
-  cpr = cpr > 8 ? 8 : cpr;
+  // Ranks 8 and 16: chunks per wave in a workgroup unit (the unit spans 4x as
+  // many), as many as still give every CU ~16 units at the largest batch, at
+  // most 8.  Ranks 32 and 64 (shared-B kernel, all waves on one chunk):
+  // chunks per unit for ~4 units per CU at the largest batch, from 8 (the
+  // rank operand, rank floats per token and part, is amortised over the
+  // unit's y bytes) to 16.
+  const bool shared = rank >= 32;
+  const int64_t tiles = shared ? (static_cast<int64_t>(max_tokens) + kSharedTile - 1) / kSharedTile + max_loras
+                               : (static_cast<int64_t>(max_tokens) + kExpandTile - 1) / kExpandTile;
+  int64_t cpr;
+  if (shared) {
+    cpr = tiles * total_chunks / (static_cast<int64_t>(num_cus) * 4);
+    cpr = cpr < 8 ? 8 : (cpr > 16 ? 16 : cpr);
+  } else {
+    cpr = tiles * total_chunks / (static_cast<int64_t>(num_cus) * 16);
+    cpr = cpr < 1 ? 1 : (cpr > 8 ? 8 : cpr);
+  }
 #ifdef LORA_TUNING
   if (const char* e = getenv("LORA_EXPAND_CPR")) cpr = atoi(e);
 #endif
   p.chunks_per_range = static_cast<int>(cpr);
-  const int per_unit = p.chunks_per_range * kExpandWaves;
+  const int per_unit = shared ? p.chunks_per_range : p.chunks_per_range * kExpandWaves;
   int ranges = 0;
   for (int s = 0; s < LORA_MAX_SLICES; ++s) {
     if (s < num_slices) {
@@ -444,14 +668,14 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
   p.max_loras = max_loras;
 
   int64_t grid = tiles * ranges;
-  const int64_t cap = static_cast<int64_t>(num_cus) * 8;
+  const int64_t cap = static_cast<int64_t>(num_cus) * (shared ? 4 : 8);
   grid = grid < cap ? grid : cap;
   grid = (grid + kXcds - 1) / kXcds * kXcds;  // whole rounds over the XCDs
   switch (rank) {
     case 8: return launch_expand_rank<8, 1>(p, static_cast<int>(grid), stream);
     case 16: return launch_expand_rank<16, 1>(p, static_cast<int>(grid), stream);
-    case 32: return launch_expand_rank<32, 2>(p, static_cast<int>(grid), stream);
-    default: return launch_expand_rank<64, 2>(p, static_cast<int>(grid), stream);
+    case 32: return launch_expand_shared<32>(p, static_cast<int>(grid), stream);
+    default: return launch_expand_shared<64>(p, static_cast<int>(grid), stream);
   }
 }
 
