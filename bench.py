@@ -289,7 +289,8 @@ def run_config(idx, args):
     log("[bench] per-kernel timing")
     kb = kernel_set_bytes(w, splits)
     # (the metadata kernel reads a few KB per copy: it is timed over the step's copies)
-    rot = {k: (R if k == "metadata" else rotation(kb[k], sb, R)) for k in kb}
+    # (--rotate fixes the copies for every kernel, e.g. for short counter runs)
+    rot = {k: (R if k == "metadata" or args.rotate else rotation(kb[k], sb, R)) for k in kb}
     sets.grow(max(rot.values()))
     per = {}
     fns = {"metadata": sets.metadata, "shrink": sets.shrink, "expand": sets.expand,
