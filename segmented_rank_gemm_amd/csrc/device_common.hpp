@@ -284,6 +284,24 @@ __device__ __forceinline__ SlotRange tile_slots(const SlotTable& tab, int pos0, 
 // xcd * per_xcd + slot, + slots_per_xcd, ... within its XCD's run.
 constexpr int kXcds = 8;
 
+// Clamp a persistent grid to the workgroups the device holds at once, so that
+// every launched workgroup runs from the start: one queued behind the resident
+// ones would begin its share of the units only when another ends, and a share
+// of large units then finishes far behind the rest.  Whole rounds over the
+// XCDs.  Host only.
+template <typename Kernel>
+inline int resident_grid(Kernel kernel, int threads, int grid) {
+  int per_cu = 0, dev = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+      per_cu < 1 || hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return grid;
+  int64_t cap = static_cast<int64_t>(per_cu) * cus / kXcds * kXcds;
+  cap = cap < kXcds ? kXcds : cap;
+  return grid < cap ? grid : static_cast<int>(cap);
+}
+
 struct XcdWalk {
   int next;  // next unit index, or >= end when done
   int end;

@@ -593,12 +593,14 @@ void expand_shared_kernel(ExpandParams p) {
 
 template <int RANK>
 hipError_t launch_expand_shared(const ExpandParams& p, int grid, hipStream_t stream) {
+  grid = resident_grid(expand_shared_kernel<RANK>, kExpandThreads, grid);
   hipLaunchKernelGGL((expand_shared_kernel<RANK>), dim3(grid), dim3(kExpandThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int RANK, int MW>
 hipError_t launch_expand_rank(const ExpandParams& p, int grid, hipStream_t stream) {
+  grid = resident_grid(expand_kernel<RANK, MW>, kExpandThreads, grid);
   hipLaunchKernelGGL((expand_kernel<RANK, MW>), dim3(grid), dim3(kExpandThreads), 0, stream, p);
   return hipGetLastError();
 }

@@ -266,8 +266,11 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
 // cross-wave reduction is needed.
 constexpr int kLdsTile = 64;  // tokens per tile (4 waves x 16)
 
+// Three workgroups per CU (registers and LDS allow it up to NB = 6), so that a
+// batch's units all run in one round.
 template <int NB>
-__global__ __launch_bounds__(kShrinkThreads) void shrink_lds_kernel(ShrinkParams p) {
+__global__ __launch_bounds__(kShrinkThreads) __attribute__((amdgpu_waves_per_eu(NB <= 6 ? 3 : 2)))
+void shrink_lds_kernel(ShrinkParams p) {
   constexpr int kRows = kLdsTile + 16 * NB;       // x rows, then A rows
   constexpr int kJ = (kRows * 8 + kShrinkThreads - 1) / kShrinkThreads;  // pieces per thread
   constexpr int kLdsRows = kJ * (kShrinkThreads / 8);
@@ -420,12 +423,14 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_lds_kernel(ShrinkParams
 
 template <int NB>
 hipError_t launch_shrink_lds_nb(const ShrinkParams& p, int grid, hipStream_t stream) {
+  grid = resident_grid(shrink_lds_kernel<NB>, kShrinkThreads, grid);
   hipLaunchKernelGGL((shrink_lds_kernel<NB>), dim3(grid), dim3(kShrinkThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int NB, int MW>
 hipError_t launch_shrink_nb(const ShrinkParams& p, int grid, hipStream_t stream) {
+  grid = resident_grid(shrink_kernel<NB, MW>, kShrinkThreads, grid);
   hipLaunchKernelGGL((shrink_kernel<NB, MW>), dim3(grid), dim3(kShrinkThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -501,7 +506,7 @@ hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint1
   const int mw = shrink_tile_blocks(max_tokens, nb);
   if (mw == 4) {
     // large batch: LDS-staged kernel, 64-token tiles, at most 3 workgroups per
-    // CU (LDS), in whole rounds over the XCDs
+    // CU, in whole rounds over the XCDs (and no more than are resident)
     const int64_t tiles = (static_cast<int64_t>(max_tokens) + kLdsTile - 1) / kLdsTile + max_loras;
     int64_t g = tiles * num_splits * p.num_groups;
     const int64_t cap = static_cast<int64_t>(num_cus) * 3;
