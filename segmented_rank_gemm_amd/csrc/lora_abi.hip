@@ -94,10 +94,11 @@ int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t m
   // 256-CU device at the largest batch, with parts of at least 256 hidden
   // elements.  Small batches (16-token tiles): ~2 units per CU, but no more
   // parts than the expand sums with one batch of loads (16 for rank 8, else 8)
-  // and parts * rank <= 256 (at most 1 KB of parts per token).  Large batches (64-token tiles):
-  // also parts of about 1024 elements, so that several workgroups share each
-  // CU, up to 8 parts (a second batch of loads in the expand at rank 64 costs
-  // far less than the shrink gains).
+  // and parts * rank <= 256 (at most 1 KB of parts per token).  Large batches
+  // (64-token tiles): also parts of about 1400 elements (at least 4), so that
+  // several workgroups share each CU, up to 8 parts (measured on the prefill,
+  // down_proj and 70B shapes; a second batch of loads in the expand at rank 64
+  // costs far less than the shrink gains).
   const int nb_total = (num_slices * rank + 15) / 16;
   const int nb = lora::shrink_group_blocks(nb_total);
   const int64_t groups = (nb_total + nb - 1) / nb;
@@ -109,7 +110,8 @@ int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t m
   int64_t cap;
   if (mw != 4) splits = (512 + tiles * groups - 1) / (tiles * groups);
   if (mw == 4) {
-    const int64_t by_work = (hidden + 1023) / 1024;
+    int64_t by_work = (hidden + 700) / 1400;  // parts of about 1400 elements, 4 to 8
+    by_work = by_work < 4 ? 4 : by_work;
     splits = splits > by_work ? splits : by_work;
     cap = 8;
   } else {
