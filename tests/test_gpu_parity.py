@@ -69,7 +69,8 @@ FUZZ = [(0, 1, 1, "wild"), (0, 64, 8, "wild"), (1, 1, 1, "single"), (1, 5, 256, 
         (63, 64, 3, "runs"), (64, 64, 2, "wild"), (65, 100, 4, "extreme"), (1023, 1024, 16, "wild"),
         (1024, 1024, 64, "all_none"), (1025, 3000, 64, "runs"), (3000, 3000, 1, "wild"),
         (4097, 5000, 256, "wild"), (8192, 8192, 4, "runs"), (20000, 20000, 256, "extreme"),
-        (65536, 70000, 33, "wild"), (777, 777, 255, "single")]
+        (65536, 70000, 33, "wild"), (777, 777, 255, "single"),
+        (1 << 20, (1 << 20) + 3, 256, "wild")]  # many blocks, every adapter slot
 
 
 @pytest.mark.parametrize("T,maxT,L,kind", FUZZ)
@@ -171,6 +172,13 @@ SHAPES = [
     (900, 1024, 320, [64, 64, 64], 32, 9, 8, 8, 5),
     (777, 800, 1032, [128, 8, 24, 200], 32, 5, 0, 8, 64),
     (2000, 2048, 2048, [1024], 64, 256, 0, 0, 4),
+    # extremes: one token slot; the widest hidden dimension; four rank-64 slices
+    # (two output groups of eight blocks) in both shrink kernels
+    (1, 1, 64, [8], 8, 1, 0, 0, 1),
+    (40, 48, 65536, [64], 8, 2, 8, 0, 16),
+    (600, 640, 65536, [16], 16, 3, 0, 8, 8),
+    (300, 320, 384, [64, 32, 16, 8], 64, 3, 8, 8, 3),
+    (700, 700, 384, [64, 32, 16, 8], 64, 3, 8, 8, 3),
 ]
 
 
@@ -193,6 +201,21 @@ def test_empty_parts_decode_shape():
     H.run_step(d)
     torch.cuda.synchronize()
     _full_check(w, d)
+
+
+@pytest.mark.parametrize("scale", [-1.5, 0.0])
+@pytest.mark.parametrize("T", [200, 900])
+def test_scale_values(scale, T):
+    # a negative scale flips every product; zero leaves y exactly as it was
+    rng = np.random.default_rng(int(T + 10 * scale))
+    mapping = rng.integers(-1, 4, size=T)
+    w = make_custom_workload(T + 3, T, 512, [96, 32], 16, 4, scale, mapping)
+    d = H.upload(w, num_splits=3)
+    H.run_step(d)
+    torch.cuda.synchronize()
+    _full_check(w, d)
+    if scale == 0.0:
+        assert np.array_equal(H.from_dev_bf16(d.y)[:T, :w.n_total], w.y0[:T])
 
 
 @pytest.mark.parametrize("kind", ["empty", "all_none", "single", "one_token"])
