@@ -413,8 +413,10 @@ void expand_shared_kernel(ExpandParams p) {
 
   for (XcdWalk walk = xcd_walk(units, gridDim.x); walk.next < walk.end; walk.next += walk.step) {
     const int u = walk.next;
-    const int m = u % num_tiles;  // tiles fastest: neighbouring units share B in one L2
-    const int cr = u / num_tiles;
+    // (large batches: a tile's column ranges consecutive, as in the kernel above)
+    const int nranges = p.range_end[p.num_slices - 1];
+    const int m = p.order_range_fastest ? u / nranges : u % num_tiles;
+    const int cr = p.order_range_fastest ? u % nranges : u / num_tiles;
     const Tile tile = resolve_tile<kSharedTile>(tab, m);
 
     int s = 0;
