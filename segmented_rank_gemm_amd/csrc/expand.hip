@@ -130,14 +130,29 @@ void expand_kernel(ExpandParams p) {
 
   const int tiles = (p.max_tokens + kTile - 1) / kTile;
   const int ranges = p.range_end[p.num_slices - 1];
-  const int units = tiles * ranges;
+  // Large batches walk only the tiles that hold positions with an adapter:
+  // the tokens without one come first in the grouped order, and tiles of theirs
+  // in the units would leave the first XCDs' runs without work.  The slot table
+  // is then read before the first unit's token ids; small batches load both
+  // together and skip empty tiles as they meet them.
+  int tile0 = 0;
+  int units = tiles * ranges;
+  if (p.order_range_fastest) {
+    if (wave == 0)
+      load_slot_table(tab, p.active_ids, p.counts, p.starts, p.num_active, p.max_loras,
+                      p.max_tokens);
+    __syncthreads();
+    tile0 = tab.act_begin < tab.act_end ? tab.act_begin / kTile : 0;
+    const int tile1 = tab.act_begin < tab.act_end ? (tab.act_end + kTile - 1) / kTile : 0;
+    units = (tile1 - tile0) * ranges;
+  }
   XcdWalk walk = xcd_walk(units, gridDim.x);
 
   // Token ids of a unit's rows: the rank-operand row c and the output rows
   // 4*grp + j of every 16-token block.
   int ta[MW], td[MW][4];
   auto load_tokens = [&](int u) {
-    const int pos0 = (p.order_range_fastest ? u / ranges : u % tiles) * kTile;
+    const int pos0 = (p.order_range_fastest ? tile0 + u / ranges : u % tiles) * kTile;
 #pragma unroll
     for (int mb = 0; mb < MW; ++mb) {
       ta[mb] = token_at_clamped(p.sorted, pos0 + 16 * mb + c, p.max_tokens);
@@ -147,14 +162,17 @@ void expand_kernel(ExpandParams p) {
     }
   };
   if (walk.next < walk.end) load_tokens(walk.next);
-  if (wave == 0)
-    load_slot_table(tab, p.active_ids, p.counts, p.starts, p.num_active, p.max_loras, p.max_tokens);
-  __syncthreads();
+  if (!p.order_range_fastest) {
+    if (wave == 0)
+      load_slot_table(tab, p.active_ids, p.counts, p.starts, p.num_active, p.max_loras,
+                      p.max_tokens);
+    __syncthreads();
+  }
 
   for (bool first = true; walk.next < walk.end; walk.next += walk.step, first = false) {
     const int u = walk.next;
     if (!first) load_tokens(u);
-    const int m = p.order_range_fastest ? u / ranges : u % tiles;
+    const int m = p.order_range_fastest ? tile0 + u / ranges : u % tiles;
     const int cr = p.order_range_fastest ? u % ranges : u / tiles;
     const int pos0 = m * kTile;
     const SlotRange sr = tile_slots(tab, pos0, kTile);

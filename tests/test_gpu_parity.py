@@ -182,6 +182,29 @@ SHAPES = [
 ]
 
 
+LARGE_BATCH_PARTS = [
+    # (T, hidden, slices, rank, L, splits): batches of more than 512 tokens
+    # (the LDS-staged shrink) on the down_proj, gate_up and 70B qkv shapes, from
+    # two parts to the most parts the hidden dimension has 64-element chunks for
+    (520, 11008, [4096], 64, 16, 2),
+    (520, 11008, [4096], 64, 16, 64),
+    (1500, 4096, [2048, 2048], 16, 4, 8),
+    (3000, 8192, [8192, 1024, 1024], 32, 64, 6),
+    (2048, 1024, [512], 8, 1, 3),
+]
+
+
+@pytest.mark.parametrize("T,hidden,slices,rank,L,splits", LARGE_BATCH_PARTS)
+def test_large_batch_parts(T, hidden, slices, rank, L, splits):
+    rng = np.random.default_rng(T + splits)
+    mapping = rng.integers(-1, L, size=T)
+    w = make_custom_workload(T, T, hidden, slices, rank, L, 1.0, mapping, max_tokens=T + 3)
+    d = H.upload(w, num_splits=splits)
+    H.run_step(d)
+    torch.cuda.synchronize()
+    _full_check(w, d)
+
+
 @pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,ldx_pad,ldy_pad,splits", SHAPES)
 def test_shape_sweep(T, maxT, hidden, slices, rank, L, ldx_pad, ldy_pad, splits):
     rng = np.random.default_rng(T + hidden)
