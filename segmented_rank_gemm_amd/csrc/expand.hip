@@ -34,6 +34,7 @@ constexpr int kExpandThreads = 256;
 constexpr int kExpandWaves = kExpandThreads / kWave;
 constexpr int kExpandTile = 16;    // tokens per wave unit (the MFMA M dimension)
 constexpr int kExpandCols = 128;   // columns per chunk: 8 MFMA blocks of 16
+constexpr int kMaxSharedCpr = 16;  // longest column range (chunks) of the shared-B kernel
 
 struct ExpandParams {
   const float* buf;
@@ -42,8 +43,11 @@ struct ExpandParams {
   int n[LORA_MAX_SLICES];
   int off[LORA_MAX_SLICES];
   int range_end[LORA_MAX_SLICES];  // running count of column ranges through slice s
+                                   // (ranks 8, 16; the shared-B kernel derives its own)
   int num_slices;
-  int chunks_per_range;
+  int chunks_per_range;            // 0: the shared-B kernel chooses it
+  int num_cus;
+  int ranges_by_cpr[kMaxSharedCpr + 1];  // shared-B: column ranges for c chunks per range
   int order_range_fastest;  // unit order: the column ranges of a tile consecutive
   uint16_t* y;
   int64_t ldy;
@@ -407,6 +411,32 @@ void expand_kernel(ExpandParams p) {
 // never stored.
 constexpr int kSharedTile = 64;
 
+// Chunks per column range of the shared-B kernel, chosen for the batch at
+// hand (its tile count is known only on the device).  Each XCD's workgroups
+// take its run of units in rounds; a unit costs its chunks plus a start-up of
+// about three chunks' time (token ids, rank operand, first B chunk), so the
+// choice minimises rounds * (chunks + 3), ties to the longer range (measured
+// on the down_proj and 70B qkv batches: this cost orders all lengths from 2
+// to 16 as their times do).  Every lane computes the same value.
+// (The search runs at every workgroup's start, so it avoids integer division:
+// the range counts come from the host, and the rounds, integers below 2^20,
+// are exact enough in fp32 less a margin well above its rounding error.)
+__device__ int shared_chunks_per_range(const ExpandParams& p, int tiles, int grid) {
+  const int slots = (grid < p.num_cus ? grid : p.num_cus) / kXcds;  // CUs per XCD at work
+  const float inv_slots = 1.0f / static_cast<float>(slots > 0 ? slots : 1);
+  int best = 8;
+  float best_cost = 3.0e38f;
+  for (int cpr = kMaxSharedCpr; cpr >= 2; --cpr) {
+    const int per_xcd = (tiles * p.ranges_by_cpr[cpr] + kXcds - 1) / kXcds;
+    const float cost = ceilf(static_cast<float>(per_xcd) * inv_slots - 1e-3f) * (cpr + 3);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = cpr;
+    }
+  }
+  return best;
+}
+
 template <int RANK>
 __global__ __launch_bounds__(kExpandThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void expand_shared_kernel(ExpandParams p) {
@@ -425,21 +455,32 @@ void expand_shared_kernel(ExpandParams p) {
   const int grp = lane >> 4;
   const int khalf = grp & 1;
   const bool use_lo = grp >= 2;
-  const int cpr = p.chunks_per_range;
-  const int num_tiles = tab.num_tiles;
-  const int units = num_tiles * p.range_end[p.num_slices - 1];
+  // (the table's values are the same in every lane: read them as scalars)
+  const int num_tiles = __builtin_amdgcn_readfirstlane(tab.num_tiles);
+  const int cpr = p.chunks_per_range > 0 ? p.chunks_per_range
+                                         : shared_chunks_per_range(p, num_tiles, gridDim.x);
+  int range_end[LORA_MAX_SLICES];  // running count of column ranges through slice s
+  {
+    int ranges = 0;
+#pragma unroll
+    for (int s = 0; s < LORA_MAX_SLICES; ++s) {
+      if (s < p.num_slices) ranges += ((p.n[s] + kExpandCols - 1) / kExpandCols + cpr - 1) / cpr;
+      range_end[s] = ranges;
+    }
+  }
+  const int nranges = range_end[p.num_slices - 1];
+  const int units = num_tiles * nranges;
 
   for (XcdWalk walk = xcd_walk(units, gridDim.x); walk.next < walk.end; walk.next += walk.step) {
     const int u = walk.next;
     // (large batches: a tile's column ranges consecutive, as in the kernel above)
-    const int nranges = p.range_end[p.num_slices - 1];
     const int m = p.order_range_fastest ? u / nranges : u % num_tiles;
     const int cr = p.order_range_fastest ? u % nranges : u / num_tiles;
     const Tile tile = resolve_tile<kSharedTile>(tab, m);
 
     int s = 0;
 #pragma unroll
-    for (int i = 0; i < LORA_MAX_SLICES - 1; ++i) s += (i < p.num_slices - 1 && cr >= p.range_end[i]) ? 1 : 0;
+    for (int i = 0; i < LORA_MAX_SLICES - 1; ++i) s += (i < p.num_slices - 1 && cr >= range_end[i]) ? 1 : 0;
     int n_s = p.n[0], off_s = p.off[0], r_before = 0;
     const uint16_t* bslice = p.b[0];
 #pragma unroll
@@ -447,7 +488,7 @@ void expand_shared_kernel(ExpandParams p) {
       if (s == i) {
         n_s = p.n[i];
         off_s = p.off[i];
-        r_before = p.range_end[i - 1];
+        r_before = range_end[i - 1];
         bslice = p.b[i];
       }
     }
@@ -652,18 +693,13 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
   }
   // Ranks 8 and 16: chunks per wave in a workgroup unit (the unit spans 4x as
   // many), as many as still give every CU ~16 units at the largest batch, at
-  // most 8.  Ranks 32 and 64 (shared-B kernel, all waves on one chunk):
-  // chunks per unit for ~4 units per CU at the largest batch, from 8 (the
-  // rank operand, rank floats per token and part, is amortised over the
-  // unit's y bytes) to 16.
+  // most 8.  Ranks 32 and 64 (shared-B kernel, all waves on one chunk): the
+  // kernel chooses the range length from the batch's tile count (0 here).
   const bool shared = rank >= 32;
   const int64_t tiles = shared ? (static_cast<int64_t>(max_tokens) + kSharedTile - 1) / kSharedTile + max_loras
                                : (static_cast<int64_t>(max_tokens) + kExpandTile - 1) / kExpandTile;
-  int64_t cpr;
-  if (shared) {
-    cpr = tiles * total_chunks / (static_cast<int64_t>(num_cus) * 4);
-    cpr = cpr < 8 ? 8 : (cpr > 16 ? 16 : cpr);
-  } else {
+  int64_t cpr = 0;
+  if (!shared) {
     cpr = tiles * total_chunks / (static_cast<int64_t>(num_cus) * 16);
     cpr = cpr < 1 ? 1 : (cpr > 8 ? 8 : cpr);
   }
@@ -679,7 +715,9 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
 #ifdef LORA_TUNING
   if (const char* e = getenv("LORA_EXPAND_ORDER")) p.order_range_fastest = atoi(e);
 #endif
-  const int per_unit = shared ? p.chunks_per_range : p.chunks_per_range * kExpandWaves;
+  // (shared-B kernel: the shortest range it may choose bounds the units)
+  const int per_unit = shared ? (p.chunks_per_range > 0 ? p.chunks_per_range : 2)
+                              : p.chunks_per_range * kExpandWaves;
   int ranges = 0;
   for (int s = 0; s < LORA_MAX_SLICES; ++s) {
     if (s < num_slices) {
@@ -698,8 +736,20 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
   p.max_tokens = max_tokens;
   p.max_loras = max_loras;
 
+  p.num_cus = num_cus;
+  for (int c = 2; c <= kMaxSharedCpr; ++c) {
+    int r = 0;
+    for (int s = 0; s < num_slices; ++s) r += ((slice_sizes[s] + kExpandCols - 1) / kExpandCols + c - 1) / c;
+    p.ranges_by_cpr[c] = r;
+  }
   int64_t grid = tiles * ranges;
-  const int64_t cap = static_cast<int64_t>(num_cus) * (shared ? 4 : 8);
+  // shared-B: two workgroups per CU (one hides the other's unit start-up; the
+  // range choice counts rounds per CU, whose fetch rate bounds both)
+  int64_t wg_per_cu = shared ? 2 : 8;
+#ifdef LORA_TUNING
+  if (const char* e = getenv("LORA_EXPAND_SHARED_WPC")) if (shared) wg_per_cu = atoi(e);
+#endif
+  const int64_t cap = static_cast<int64_t>(num_cus) * wg_per_cu;
   grid = grid < cap ? grid : cap;
   grid = (grid + kXcds - 1) / kXcds * kXcds;  // whole rounds over the XCDs
   switch (rank) {
