@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=None, help="buffer copies (default: >= 1 GiB)")
     ap.add_argument("--kernel-reps", type=int, default=50,
                     help="graph replays per single-kernel timing")
+    ap.add_argument("--layers", type=int, default=32,
+                    help="layers of the layer-stack timing (one metadata step, then shrink + "
+                    "expand per layer on its own weights and activations; 0 skips it)")
     return ap.parse_args()
 
 
@@ -145,6 +148,14 @@ class Sets:
         import segmented_rank_gemm_amd as srg
         s = self.sets[r]
         srg.lora_expand(s["buf"], self.num_splits, s["b"], s["y"], s["meta"], stream)
+
+    def layer(self, r, meta_r, stream=None):
+        """Shrink + expand on copy r (one layer's weights and activations) with the
+        metadata computed on copy meta_r."""
+        import segmented_rank_gemm_amd as srg
+        s, m = self.sets[r], self.sets[meta_r]["meta"]
+        srg.lora_shrink(s["x"], s["a"], float(self.w.scale), s["buf"], self.num_splits, m, stream)
+        srg.lora_expand(s["buf"], self.num_splits, s["b"], s["y"], m, stream)
 
     def step(self, r, stream=None):
         self.metadata(r, stream)
@@ -302,6 +313,30 @@ def run_config(idx, args):
         del g
     pair_s = per.pop("pair")
 
+    # layer stack: one metadata step serves a model's L LoRA layers of this
+    # shape, each with its own weights, activations and outputs.  Stacks are
+    # rotated like the steps (each stack takes L copies and computes its
+    # metadata on its first), so that the buffers span ROTATE_BYTES.
+    stack = None
+    L = args.layers
+    if L > 0:
+        K = max(1, math.ceil(max(R, rot["expand"]) / L))
+        log(f"[bench] layer stack: {K} stacks of {L} layers")
+        sets.grow(K * L)
+        calls = []
+        for k in range(K):
+            m = k * L
+            calls.append(lambda s, m=m: sets.metadata(m, s))
+            calls += [lambda s, r=m + l, m=m: sets.layer(r, m, s) for l in range(L)]
+        g = capture(calls)
+        t_stack = time_graph(g, max(2, reps // 10)) / K
+        del g
+        stack = {
+            "layers": L, "rotated_stacks": K, "us": t_stack * 1e6, "us_per_layer": t_stack / L * 1e6,
+            "metadata_share": per["metadata"] / t_stack,
+            "layer_tokens_per_s": w.num_tokens * L / t_stack,
+        }
+
     # practical ceilings for the expand's bytes, same rotation: a copy between
     # two buffers, and an in-place update of one (the expand's access pattern)
     cb = (st["expand_bytes"] // 2) // 16 * 16
@@ -358,6 +393,7 @@ def run_config(idx, args):
             "achieved_GBs": (st["shrink_bytes"] + st["expand_bytes"]) / pair_s / 1e9,
             "frac_of_peak": (st["shrink_bytes"] + st["expand_bytes"]) / pair_s / 1e9 / HBM_PEAK_GBS,
         },
+        "layer_stack": stack,
         "copy_ceiling": {"bytes_read_plus_written": 2 * cb, "us": copy_s * 1e6,
                          "GBs": 2 * cb / copy_s / 1e9},
         "update_ceiling": {"bytes_read_plus_written": 2 * cb, "us": upd_s * 1e6,
