@@ -296,6 +296,43 @@ def test_token_permutation_permutes_rows():
     assert np.array_equal(H.from_dev_bf16(d2.y), H.from_dev_bf16(d.y)[perm])
 
 
+@pytest.mark.parametrize("T,hidden,slices,rank,L", [
+    (300, 1024, [512, 256, 256], 8, 4),      # up to 512 token slots: register shrink
+    (900, 2048, [1024], 64, 16),             # LDS shrink, shared-B expand
+    (1200, 1024, [2048, 2048], 16, 6),       # LDS shrink, position-tile expand
+])
+def test_graph_replays_new_batches(T, hidden, slices, rank, L):
+    # One capture, then batches of the same size with new adapter maps and
+    # activations copied into the captured buffers before each replay (static
+    # buffers, as a graph-captured serving loop uses them): every replay must
+    # match the oracle for its own batch, however many adapters it has.
+    rng = np.random.default_rng(T + rank)
+    kinds = [rng.integers(-1, L, size=T), np.full(T, L - 1), np.full(T, -1),
+             np.sort(rng.integers(0, 2, size=T)), rng.integers(-3, L + 3, size=T)]
+    batches = [make_custom_workload(T + i, T, hidden, slices, rank, L, 0.75, m)
+               for i, m in enumerate(kinds)]
+    d = H.upload(batches[0])
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        H.run_step(d, stream=torch.cuda.current_stream())
+    for w in batches:
+        fresh = H.upload(w, num_splits=d.num_splits)
+        d.w = w
+        d.mapping.copy_(fresh.mapping)
+        d.x.copy_(fresh.x)
+        d.y.copy_(fresh.y)
+        for dst, src in zip(d.lora_a + d.lora_b, fresh.lora_a + fresh.lora_b):
+            dst.copy_(src)
+        d.buf.fill_(float("nan"))
+        d.meta.sorted_token_ids.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _full_check(w, d)
+
+
 def test_graph_replay_matches_eager():
     w = make_workload(1, num_tokens=256)
     d = H.upload(w)
