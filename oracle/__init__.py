@@ -107,6 +107,42 @@ def prepare_metadata(mapping: np.ndarray, max_loras: int) -> Dict[str, np.ndarra
     return out
 
 
+TILE = 16  # positions per tile of the padded grouped order
+
+
+def prepare_tiles(mapping: np.ndarray, max_loras: int) -> Dict[str, np.ndarray]:
+    """The padded grouped order the kernels read tiles of: for the k-th
+    adapter present (ascending id), its tokens in batch order from position
+    P_k = round_up(S_k + (TILE - 1) * k, TILE), S_k being the number of tokens of the
+    adapters before it; -1 everywhere else below num_tiles * TILE.  Returns
+    tile_token_ids [num_tiles * TILE], tile_lora [num_tiles] (the adapter of
+    each tile, -1 for a tile of -1 entries) and num_tiles [1].
+
+    A layout of this library's own (the pages fix only the grouping itself:
+    vLLM PR #13096, "Why do we need a new set of kernels"); written out here
+    from its definition, adapter by adapter, independently of the sort above.
+    """
+    m = np.asarray(mapping, dtype=np.int64).reshape(-1)
+    ids = np.where((m >= -1) & (m < max_loras), m, -1)
+    runs = []  # (start position, adapter, tokens)
+    s_k = 0
+    for k, l in enumerate(sorted(set(int(v) for v in ids if v >= 0))):
+        toks = [t for t in range(ids.shape[0]) if ids[t] == l] if ids.shape[0] <= 4096 \
+            else np.nonzero(ids == l)[0].tolist()
+        p_k = -(-(s_k + (TILE - 1) * k) // TILE) * TILE
+        runs.append((p_k, l, toks))
+        s_k += len(toks)
+    end = runs[-1][0] + len(runs[-1][2]) if runs else 0
+    num_tiles = -(-end // TILE)
+    tile_token_ids = np.full(num_tiles * TILE, -1, dtype=np.int32)
+    tile_lora = np.full(num_tiles, -1, dtype=np.int32)
+    for p_k, l, toks in runs:
+        tile_token_ids[p_k:p_k + len(toks)] = toks
+        tile_lora[p_k // TILE:-(-(p_k + len(toks)) // TILE)] = l
+    return dict(tile_token_ids=tile_token_ids, tile_lora=tile_lora,
+                num_tiles=np.array([num_tiles], dtype=np.int32))
+
+
 def shrink(x: np.ndarray, lora_a: List[np.ndarray], mapping: np.ndarray, max_loras: int,
            rank: int, scale: float, num_threads: int = 0) -> np.ndarray:
     """fp64 buf [S, T, rank]; rows of tokens without an adapter stay NaN."""

@@ -143,6 +143,60 @@ def test_metadata_matches_selection_brute_force(seed):
         assert meta[k].tolist() == v, k
 
 
+# ------------------------------------------------ padded tiles of the order --
+
+def test_tiles_worked_example():
+    # adapters 0 (tokens 2, 6), 1 (token 4), 2 (tokens 0, 3); S = 0, 2, 3 and
+    # k = 0, 1, 2 give starts round_up(S + 15k, 16) = 0, 32, 48 by hand, so
+    # tile 1 is the empty gap between adapters 0 and 1
+    t = oracle.prepare_tiles(np.array([2, -1, 0, 2, 1, -1, 0, 7]), 3)
+    want = np.full(64, -1)
+    want[[0, 1, 32, 48, 49]] = [2, 6, 4, 0, 3]
+    assert t["tile_token_ids"].tolist() == want.tolist()
+    assert t["tile_lora"].tolist() == [0, -1, 1, 2]
+    assert t["num_tiles"].tolist() == [4]
+
+
+def test_tiles_empty_and_no_adapter():
+    for mapping in (np.zeros(0, dtype=np.int32), np.full(40, -1)):
+        t = oracle.prepare_tiles(mapping, 4)
+        assert t["num_tiles"].tolist() == [0]
+        assert t["tile_token_ids"].size == 0 and t["tile_lora"].size == 0
+
+
+@pytest.mark.parametrize("kind", FUZZ_KINDS)
+@pytest.mark.parametrize("T,L", [(1, 1), (37, 3), (1000, 16), (4096, 64), (5000, 256)])
+def test_tiles_are_the_grouping_padded(kind, T, L):
+    rng = np.random.default_rng(T * 1000 + L + 7)
+    mapping = make_fuzz_mapping(rng, T, L, kind)
+    ids = _sanitize(mapping, L)
+    t = oracle.prepare_tiles(mapping, L)
+    tok, lora, nt = t["tile_token_ids"], t["tile_lora"], int(t["num_tiles"][0])
+    assert tok.shape == (nt * 16,) and lora.shape == (nt,)
+    # without the -1 entries: the tokens that have an adapter, in the library's
+    # stable argsort order
+    order = np.argsort(ids, kind="stable")
+    assert np.array_equal(tok[tok >= 0], order[ids[order] >= 0])
+    # every tile holds one adapter's tokens (or none, with adapter -1)
+    tiles = tok.reshape(nt, 16)
+    for m in range(nt):
+        members = tiles[m][tiles[m] >= 0]
+        if lora[m] < 0:
+            assert members.size == 0
+        else:
+            assert members.size > 0 and np.all(ids[members] == lora[m])
+    # each adapter's run starts at round_up(S_k + 15 k, 16) and is contiguous
+    uniq, counts = np.unique(ids[ids >= 0], return_counts=True)
+    s = 0
+    for k, (l, c) in enumerate(zip(uniq, counts)):
+        p = -(-(s + 15 * k) // 16) * 16
+        assert np.all(ids[tok[p:p + c]] == l) and np.all(np.diff(tok[p:p + c]) > 0)
+        s += c
+    assert nt <= -(-T // 16) + L + 1
+    if nt:
+        assert lora[-1] >= 0  # no trailing empty tile
+
+
 # ------------------------------------------------------- shrink and expand --
 
 def _dense_reference(w, rows, lid, scale):
