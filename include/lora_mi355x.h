@@ -63,6 +63,12 @@ typedef enum lora_status {
 #define LORA_MAX_SLICES 4      /* output slices per call (qkv: 3, gate_up: 2) */
 #define LORA_MAX_SPLITS 64     /* hidden-dimension partitions of the shrink */
 
+/* Tiles of the padded grouped order (see lora_meta_t): LORA_TILE positions
+ * each, at most LORA_MAX_TILES(max_tokens, max_loras) of them. */
+#define LORA_TILE 16
+#define LORA_MAX_TILES(max_tokens, max_loras) \
+  (((max_tokens) + LORA_TILE - 1) / LORA_TILE + (max_loras) + 1)
+
 /*
  * Per-batch grouping of the tokens by adapter: the segment description that
  * shrink and expand read.  A host struct holding device pointers; the struct
@@ -79,6 +85,24 @@ typedef enum lora_status {
  *   lora_token_start    int32 [max_loras]: offset of the slot's first token in
  *                       sorted_token_ids; unused slots hold num_tokens.
  *   num_active          int32 [1]: number of active slots.
+ *
+ * The same grouping of the tokens that have an adapter, padded so that every
+ * tile of LORA_TILE positions belongs to one adapter (the kernels read a
+ * tile's token ids and its adapter at fixed addresses, in one round trip):
+ *
+ *   tile_token_ids      int32 [LORA_MAX_TILES * LORA_TILE]: the k-th active
+ *                       slot's tokens (in sorted_token_ids order) from
+ *                       position P_k = round_up(S_k + (LORA_TILE - 1) * k,
+ *                       LORA_TILE), where S_k counts the tokens of the slots
+ *                       before it; every other position below
+ *                       num_tiles * LORA_TILE holds -1.  (The slack term makes
+ *                       P_k a function of S_k and k alone, so each slot's
+ *                       start is known without the other slots' sizes; it
+ *                       leaves at most one empty tile between two slots.)
+ *   tile_lora           int32 [LORA_MAX_TILES]: the adapter id of each tile
+ *                       below num_tiles, or -1 for a tile of -1 entries.
+ *   num_tiles           int32 [1]: tiles in use.
+ *   Entries at or past num_tiles are never written.
  */
 typedef struct lora_meta {
   int32_t *sorted_token_ids;
@@ -86,6 +110,9 @@ typedef struct lora_meta {
   int32_t *num_tokens_per_lora;
   int32_t *lora_token_start;
   int32_t *num_active;
+  int32_t *tile_token_ids;
+  int32_t *tile_lora;
+  int32_t *num_tiles;
 } lora_meta_t;
 
 /*
@@ -104,9 +131,11 @@ typedef struct lora_meta {
  *   max_loras           adapter slots, 1 <= max_loras <= LORA_MAX_LORAS.
  *   meta                host pointer to the output buffers (all non-null).
  *
- * Writes sorted_token_ids[0:num_tokens] and all max_loras entries of the three
- * per-slot arrays, plus num_active.  A stable counting sort: bit-for-bit
- * deterministic, no atomics on global memory.  Grid: max_loras + 1 workgroups (of 64, 256 or 1024 threads by max_tokens).
+ * Writes sorted_token_ids[0:num_tokens], all max_loras entries of the three
+ * per-slot arrays, num_active, and the padded tiles below num_tiles with
+ * num_tiles.  A stable counting sort: bit-for-bit deterministic, no atomics on
+ * global memory.  Grid: max_loras + 1 workgroups (of 64, 256 or 1024 threads
+ * by max_tokens).
  */
 lora_status_t lora_prepare_metadata(const int32_t *token_lora_mapping, int32_t num_tokens,
                                     int32_t max_tokens, int32_t max_loras,

@@ -47,7 +47,15 @@ class LoraError(RuntimeError):
 class _MetaStruct(ctypes.Structure):
     _fields_ = [("sorted_token_ids", ctypes.c_void_p), ("active_lora_ids", ctypes.c_void_p),
                 ("num_tokens_per_lora", ctypes.c_void_p), ("lora_token_start", ctypes.c_void_p),
-                ("num_active", ctypes.c_void_p)]
+                ("num_active", ctypes.c_void_p), ("tile_token_ids", ctypes.c_void_p),
+                ("tile_lora", ctypes.c_void_p), ("num_tiles", ctypes.c_void_p)]
+
+TILE = 16  # positions per tile of the padded grouped order (LORA_TILE)
+
+
+def max_tiles(max_tokens: int, max_loras: int) -> int:
+    """LORA_MAX_TILES: tiles the padded grouped order may use."""
+    return (int(max_tokens) + TILE - 1) // TILE + int(max_loras) + 1
 
 
 _VP = ctypes.c_void_p
@@ -126,11 +134,16 @@ class LoraMeta:
         self.num_tokens_per_lora = torch.empty(self.max_loras, **opts)
         self.lora_token_start = torch.empty(self.max_loras, **opts)
         self.num_active = torch.empty(1, **opts)
+        nt = max_tiles(max_tokens, max_loras)
+        self.tile_token_ids = torch.empty(nt * TILE, **opts)
+        self.tile_lora = torch.empty(nt, **opts)
+        self.num_tiles = torch.empty(1, **opts)
         self._struct = _MetaStruct(*(int(t.data_ptr()) for t in self.tensors()))
 
     def tensors(self):
         return (self.sorted_token_ids, self.active_lora_ids, self.num_tokens_per_lora,
-                self.lora_token_start, self.num_active)
+                self.lora_token_start, self.num_active, self.tile_token_ids, self.tile_lora,
+                self.num_tiles)
 
     @property
     def struct_ref(self):

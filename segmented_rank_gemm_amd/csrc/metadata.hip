@@ -17,6 +17,11 @@
 // from per-thread tallies summed in a fixed order, occurrence from an LDS flag
 // per group, ranks from a block-wide exclusive scan of the per-thread member
 // counts; no global atomics, so the result is the same bits on every run.
+//
+// The same workgroup also writes its adapter's run of the padded grouped order
+// (16-token tiles of one adapter each, read by the kernels at fixed
+// addresses): the run starts at round_up(S + 15 * k, 16), S being the tokens
+// of lower adapters and k the group's slot, so it needs no other group's size.
 
 #include "device_common.hpp"
 
@@ -47,19 +52,35 @@ __device__ __forceinline__ void load_groups(const int32_t* __restrict__ mapping,
   }
 }
 
+struct MetaOut {
+  int32_t* sorted;
+  int32_t* active_ids;
+  int32_t* counts;
+  int32_t* starts;
+  int32_t* num_active;
+  int32_t* tile_ids;
+  int32_t* tile_lora;
+  int32_t* num_tiles;
+};
+
+constexpr int kMetaTile = LORA_TILE;
+
+__device__ __forceinline__ int round_up_tile(int v) {
+  return (v + kMetaTile - 1) / kMetaTile * kMetaTile;
+}
+
 // THREADS threads per workgroup (64, a single wave, for batches up to 512
 // tokens, 256 up to 2048, else 1024: fewer waves to synchronise on small
 // batches); a block of the map is THREADS * 8 tokens.
 template <int THREADS>
-__global__ __launch_bounds__(THREADS) void metadata_kernel(
-    const int32_t* __restrict__ mapping, int num_tokens, int max_loras,
-    int32_t* __restrict__ sorted, int32_t* __restrict__ active_ids,
-    int32_t* __restrict__ counts, int32_t* __restrict__ starts,
-    int32_t* __restrict__ num_active) {
+__global__ __launch_bounds__(THREADS) void metadata_kernel(const int32_t* __restrict__ mapping,
+                                                           int num_tokens, int max_loras,
+                                                           MetaOut out) {
   constexpr int kWaves = THREADS / kWave;
   constexpr int kBlock = THREADS * kPerThread;
   __shared__ int present[LORA_MAX_LORAS + 1];
-  __shared__ int wave_below[kWaves], wave_members[kWaves], wave_scan[kWaves];
+  __shared__ int wave_below[kWaves], wave_members[kWaves], wave_none[kWaves], wave_scan[kWaves];
+  __shared__ int group_slot, groups_present;
 
   const int g = blockIdx.x;
   const int groups = max_loras + 1;
@@ -71,7 +92,7 @@ __global__ __launch_bounds__(THREADS) void metadata_kernel(
 
   // Count pass: tokens in lower groups, members of g, occurring groups.
   int grp[kPerThread];
-  int below = 0, members = 0;
+  int below = 0, members = 0, none = 0;
   for (int b0 = 0; b0 < num_tokens; b0 += kBlock) {
     load_groups(mapping, num_tokens, max_loras, b0 + tid * kPerThread, grp);
 #pragma unroll
@@ -79,19 +100,22 @@ __global__ __launch_bounds__(THREADS) void metadata_kernel(
       if (grp[e] >= 0) present[grp[e]] = 1;  // benign: every writer stores 1
       below += (grp[e] >= 0 && grp[e] < g) ? 1 : 0;
       members += grp[e] == g ? 1 : 0;
+      none += grp[e] == 0 ? 1 : 0;
     }
   }
-  const int wb = wave_sum(below), wm = wave_sum(members);
+  const int wb = wave_sum(below), wm = wave_sum(members), wn = wave_sum(none);
   if (lane == 0) {
     wave_below[wave] = wb;
     wave_members[wave] = wm;
+    wave_none[wave] = wn;
   }
   __syncthreads();
-  int start = 0, total = 0;
+  int start = 0, total = 0, n_none = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     start += wave_below[w];
     total += wave_members[w];
+    n_none += wave_none[w];
   }
 
   // Wave 0: slot of g among the adapters present, how many are present, and
@@ -106,18 +130,42 @@ __global__ __launch_bounds__(THREADS) void metadata_kernel(
     }
     if (g == 0) {
       for (int i = npresent + lane; i < max_loras; i += kWave) {
-        active_ids[i] = -1;
-        counts[i] = 0;
-        starts[i] = num_tokens;
+        out.active_ids[i] = -1;
+        out.counts[i] = 0;
+        out.starts[i] = num_tokens;
       }
-      if (lane == 0) *num_active = npresent;
+      if (lane == 0) *out.num_active = npresent;
+      if (lane == 0 && npresent == 0) *out.num_tiles = 0;
     } else if (total > 0 && lane == 0) {
-      active_ids[slot] = g - 1;
-      counts[slot] = total;
-      starts[slot] = start;
+      out.active_ids[slot] = g - 1;
+      out.counts[slot] = total;
+      out.starts[slot] = start;
+    }
+    if (lane == 0) {
+      group_slot = slot;
+      groups_present = npresent;
     }
   }
   if (total == 0) return;  // uniform across the workgroup
+  __syncthreads();
+
+  // An adapter's run of the padded order: [pstart, pstart + total), then -1 up
+  // to the next run's start (or, for the last run, to the end of its tile),
+  // and the tiles' adapter ids (-1 for a gap tile of -1 entries).  Group 0
+  // (no adapter) has no run.
+  const bool has_run = g > 0;
+  const int k = group_slot;
+  const int s_k = start - n_none;  // tokens of lower adapters
+  const int pstart = round_up_tile(s_k + (kMetaTile - 1) * k);
+  if (has_run) {
+    const int run_end = round_up_tile(pstart + total);
+    const bool last = k == groups_present - 1;
+    const int pnext = last ? run_end : round_up_tile(s_k + total + (kMetaTile - 1) * (k + 1));
+    for (int i = pstart + total + tid; i < pnext; i += THREADS) out.tile_ids[i] = -1;
+    for (int m = pstart / kMetaTile + tid; m < pnext / kMetaTile; m += THREADS)
+      out.tile_lora[m] = m < run_end / kMetaTile ? g - 1 : -1;
+    if (last && tid == 0) *out.num_tiles = run_end / kMetaTile;
+  }
 
   // Place pass: member rank = members in earlier blocks + exclusive scan of the
   // per-thread member counts (thread order is token order within a block).  A
@@ -139,11 +187,14 @@ __global__ __launch_bounds__(THREADS) void metadata_kernel(
       before += w < wave ? n : 0;
       block_total += n;
     }
-    int pos = start + placed + before + incl - mine;
+    int pos = placed + before + incl - mine;  // rank of this thread's first member
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
       if (grp[e] == g) {
-        if (pos < num_tokens) sorted[pos] = t0 + e;
+        if (start + pos < num_tokens) {
+          out.sorted[start + pos] = t0 + e;
+          if (has_run) out.tile_ids[pstart + pos] = t0 + e;
+        }
         ++pos;
       }
     }
@@ -154,18 +205,18 @@ __global__ __launch_bounds__(THREADS) void metadata_kernel(
 
 hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_tokens, int max_loras,
                            const lora_meta_t& meta, hipStream_t stream) {
+  const MetaOut out{meta.sorted_token_ids, meta.active_lora_ids, meta.num_tokens_per_lora,
+                    meta.lora_token_start, meta.num_active, meta.tile_token_ids,
+                    meta.tile_lora, meta.num_tiles};
   if (max_tokens <= 64 * kPerThread) {
     hipLaunchKernelGGL(metadata_kernel<64>, dim3(max_loras + 1), dim3(64), 0, stream, mapping,
-                       num_tokens, max_loras, meta.sorted_token_ids, meta.active_lora_ids,
-                       meta.num_tokens_per_lora, meta.lora_token_start, meta.num_active);
+                       num_tokens, max_loras, out);
   } else if (max_tokens <= 256 * kPerThread) {
     hipLaunchKernelGGL(metadata_kernel<256>, dim3(max_loras + 1), dim3(256), 0, stream, mapping,
-                       num_tokens, max_loras, meta.sorted_token_ids, meta.active_lora_ids,
-                       meta.num_tokens_per_lora, meta.lora_token_start, meta.num_active);
+                       num_tokens, max_loras, out);
   } else {
     hipLaunchKernelGGL(metadata_kernel<1024>, dim3(max_loras + 1), dim3(1024), 0, stream, mapping,
-                       num_tokens, max_loras, meta.sorted_token_ids, meta.active_lora_ids,
-                       meta.num_tokens_per_lora, meta.lora_token_start, meta.num_active);
+                       num_tokens, max_loras, out);
   }
   return hipGetLastError();
 }

@@ -68,10 +68,12 @@ def run_step(d: DeviceWorkload, stream=None) -> None:
     srg.lora_expand(d.buf, d.num_splits, d.lora_b, d.y, d.meta, stream)
 
 
+META_KEYS = ["sorted_token_ids", "active_lora_ids", "num_tokens_per_lora", "lora_token_start",
+             "num_active", "tile_token_ids", "tile_lora", "num_tiles"]
+
+
 def meta_host(d: DeviceWorkload) -> dict:
-    return {k: v.cpu().numpy() for k, v in zip(
-        ["sorted_token_ids", "active_lora_ids", "num_tokens_per_lora", "lora_token_start",
-         "num_active"], d.meta.tensors())}
+    return {k: v.cpu().numpy() for k, v in zip(META_KEYS, d.meta.tensors())}
 
 
 def ulp_bf16(v: np.ndarray) -> np.ndarray:

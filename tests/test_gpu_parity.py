@@ -18,8 +18,7 @@ from workloads import (CONFIGS, make_custom_workload, make_fuzz_mapping,
 
 pytestmark = pytest.mark.gpu
 
-META_KEYS = ["sorted_token_ids", "active_lora_ids", "num_tokens_per_lora", "lora_token_start",
-             "num_active"]
+META_KEYS = H.META_KEYS
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -36,11 +35,18 @@ def _sanitize(mapping, L):
     return np.where((m >= -1) & (m < L), m, -1)
 
 
-def _check_meta(meta_gpu, ref, T, max_tokens, sorted_fill=-7):
+def _check_meta(meta_gpu, ref, T, max_tokens, sorted_fill=-7, mapping=None, L=None):
     assert np.array_equal(meta_gpu["sorted_token_ids"][:T], ref["sorted_token_ids"])
     assert np.all(meta_gpu["sorted_token_ids"][T:max_tokens] == sorted_fill)
-    for k in META_KEYS[1:]:
+    for k in META_KEYS[1:5]:
         assert np.array_equal(meta_gpu[k], ref[k]), k
+    if mapping is not None:
+        # the padded tiles, bit for bit below num_tiles
+        tiles = oracle.prepare_tiles(mapping, L)
+        nt = int(tiles["num_tiles"][0])
+        assert int(meta_gpu["num_tiles"][0]) == nt
+        assert np.array_equal(meta_gpu["tile_token_ids"][:nt * 16], tiles["tile_token_ids"])
+        assert np.array_equal(meta_gpu["tile_lora"][:nt], tiles["tile_lora"])
 
 
 def _run_metadata(mapping, T, max_tokens, L):
@@ -62,7 +68,7 @@ def test_metadata_bit_exact_full_size(cfg):
     T = mapping.shape[0]
     L = CONFIGS[cfg]["max_loras"]
     got = _run_metadata(mapping, T, T + 37, L)
-    _check_meta(got, oracle.prepare_metadata(mapping, L), T, T + 37)
+    _check_meta(got, oracle.prepare_metadata(mapping, L), T, T + 37, mapping=mapping, L=L)
 
 
 FUZZ = [(0, 1, 1, "wild"), (0, 64, 8, "wild"), (1, 1, 1, "single"), (1, 5, 256, "wild"),
@@ -78,7 +84,7 @@ def test_metadata_bit_exact_fuzz(T, maxT, L, kind):
     rng = np.random.default_rng(T * 7 + L)
     mapping = make_fuzz_mapping(rng, T, L, kind)
     got = _run_metadata(mapping, T, maxT, L)
-    _check_meta(got, oracle.prepare_metadata(mapping, L), T, maxT)
+    _check_meta(got, oracle.prepare_metadata(mapping, L), T, maxT, mapping=mapping, L=L)
 
 
 # --------------------------------------------------------- shrink + expand
@@ -86,7 +92,7 @@ def test_metadata_bit_exact_fuzz(T, maxT, L, kind):
 def _full_check(w, d, literal=False):
     T = w.num_tokens
     ref = oracle.run_step(w)
-    _check_meta(H.meta_host(d), ref, T, w.max_tokens)
+    _check_meta(H.meta_host(d), ref, T, w.max_tokens, mapping=w.mapping[:T], L=w.max_loras)
     ids = _sanitize(w.mapping, w.max_loras)
     act = ids >= 0
     # shrink: sum of the parts against the fp64 projection (rows with an adapter)
