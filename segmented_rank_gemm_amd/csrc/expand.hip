@@ -32,7 +32,6 @@ namespace lora {
 
 constexpr int kExpandThreads = 256;
 constexpr int kExpandWaves = kExpandThreads / kWave;
-constexpr int kExpandTile = 16;    // tokens per wave unit (the MFMA M dimension)
 constexpr int kExpandCols = 128;   // columns per chunk: 8 MFMA blocks of 16
 constexpr int kMaxSharedCpr = 16;  // longest column range (chunks) of the shared-B kernel
 
@@ -56,6 +55,10 @@ struct ExpandParams {
   const int32_t* counts;
   const int32_t* starts;
   const int32_t* num_active;
+  const int32_t* tile_ids;   // the padded grouped order (16-token tiles of one adapter)
+  const int32_t* tile_lora;
+  const int32_t* num_tiles;
+  int max_tiles;             // tiles the padded order may use
   int max_tokens;
   int max_loras;
 };
@@ -106,21 +109,20 @@ __device__ __forceinline__ int bslot(int row, int pr) {
 
 // MW = 16-token blocks per tile; every block shares the B operand loads.
 //
-// A workgroup unit is (fixed tile of 16*MW consecutive grouped positions,
-// slice s, column range of 4*cpr chunks); wave w takes chunks w, w+4, ... of the
-// range, so the four waves stream neighbouring columns together.  The unit's
-// token ids load together with the slot table.  The rank operand of the tile
-// (sum over the shrink's parts, split hi/lo, already in MFMA operand layout) is
-// built once per unit into LDS and shared by the four waves.  A tile that
-// straddles two adapters loads y once per chunk and runs one B pass per
-// adapter, each storing its own rows.
+// A workgroup unit is (tile of 16 positions of the padded grouped order, all
+// of one adapter, slice s, column range of 4*cpr chunks); wave w takes chunks
+// w, w+4, ... of the range, so the four waves stream neighbouring columns
+// together.  The unit's token ids, its adapter and the tile count load in one
+// round trip.  The rank operand of the tile (sum over the shrink's parts,
+// split hi/lo, already in MFMA operand layout) is built once per unit into LDS
+// and shared by the four waves.
 template <int RANK, int MW>
 __global__ __launch_bounds__(kExpandThreads) __attribute__((amdgpu_waves_per_eu(RANK <= 16 ? 2 : 1)))
 void expand_kernel(ExpandParams p) {
+  static_assert(MW == 1, "a tile of the padded grouped order holds 16 tokens");
   constexpr int kTile = 16 * MW;
   constexpr int kSteps = RankOperand<RANK>::kSteps;
   constexpr int kOpWords = RANK == 8 ? 2 : 4;  // 32-bit words per lane per MFMA step
-  __shared__ SlotTable tab;
   __shared__ uint32_t a_lds[MW][kSteps][kOpWords][kWave];
   __shared__ u32x4 b_lds[kExpandWaves][16 * RANK];  // one B chunk per wave
 
@@ -132,55 +134,42 @@ void expand_kernel(ExpandParams p) {
   const bool use_lo = grp >= 2;
   const int cpr = p.chunks_per_range;
 
-  const int tiles = (p.max_tokens + kTile - 1) / kTile;
+  // Units are (tile of the padded grouped order, column range).  Small batches
+  // take every tile the order may use, so that a unit's token ids, its tile's
+  // adapter and the batch's tile count load together in one round trip
+  // (units of tiles past the count do nothing).  Large batches read the tile
+  // count first (one round trip for the whole walk) and take only the tiles in
+  // use, so that every XCD's run of units has work.
   const int ranges = p.range_end[p.num_slices - 1];
-  // Large batches walk only the tiles that hold positions with an adapter:
-  // the tokens without one come first in the grouped order, and tiles of theirs
-  // in the units would leave the first XCDs' runs without work.  The slot table
-  // is then read before the first unit's token ids; small batches load both
-  // together and skip empty tiles as they meet them.
-  int tile0 = 0;
-  int units = tiles * ranges;
-  if (p.order_range_fastest) {
-    if (wave == 0)
-      load_slot_table(tab, p.active_ids, p.counts, p.starts, p.num_active, p.max_loras,
-                      p.max_tokens);
-    __syncthreads();
-    tile0 = tab.act_begin < tab.act_end ? tab.act_begin / kTile : 0;
-    const int tile1 = tab.act_begin < tab.act_end ? (tab.act_end + kTile - 1) / kTile : 0;
-    units = (tile1 - tile0) * ranges;
-  }
+  const int tiles = p.order_range_fastest ? __builtin_amdgcn_readfirstlane(*p.num_tiles)
+                                          : p.max_tiles;
+  const int units = tiles * ranges;
   XcdWalk walk = xcd_walk(units, gridDim.x);
 
-  // Token ids of a unit's rows: the rank-operand row c and the output rows
-  // 4*grp + j of every 16-token block.
-  int ta[MW], td[MW][4];
+  // Token ids of a unit's rows (the rank-operand row c and the output rows
+  // 4*grp + j; -1 for a pad entry), its tile's adapter and the tile count.
+  int ta[MW], td[MW][4], tlora = 0, tcount = 0;
   auto load_tokens = [&](int u) {
-    const int pos0 = (p.order_range_fastest ? tile0 + u / ranges : u % tiles) * kTile;
+    const int m = p.order_range_fastest ? u / ranges : u % tiles;
+    const int* ids = p.tile_ids + m * kTile;
+    ta[0] = ids[c];
 #pragma unroll
-    for (int mb = 0; mb < MW; ++mb) {
-      ta[mb] = token_at_clamped(p.sorted, pos0 + 16 * mb + c, p.max_tokens);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        td[mb][j] = token_at_clamped(p.sorted, pos0 + 16 * mb + 4 * grp + j, p.max_tokens);
-    }
+    for (int j = 0; j < 4; ++j) td[0][j] = ids[4 * grp + j];
+    tlora = p.tile_lora[m];
+    tcount = *p.num_tiles;
   };
   if (walk.next < walk.end) load_tokens(walk.next);
-  if (!p.order_range_fastest) {
-    if (wave == 0)
-      load_slot_table(tab, p.active_ids, p.counts, p.starts, p.num_active, p.max_loras,
-                      p.max_tokens);
-    __syncthreads();
-  }
 
   for (bool first = true; walk.next < walk.end; walk.next += walk.step, first = false) {
     const int u = walk.next;
     if (!first) load_tokens(u);
-    const int m = p.order_range_fastest ? tile0 + u / ranges : u % tiles;
+    const int m = p.order_range_fastest ? u / ranges : u % tiles;
     const int cr = p.order_range_fastest ? u % ranges : u / tiles;
-    const int pos0 = m * kTile;
-    const SlotRange sr = tile_slots(tab, pos0, kTile);
-    if (sr.first > sr.last) continue;  // wave-uniform: no row of this tile has an adapter
+    // (every load of the unit's first round trip goes out before the test: the
+    // compiler would otherwise sink some below it)
+    asm volatile("" : : "v"(ta[0]), "v"(td[0][0]), "v"(td[0][1]), "v"(td[0][2]), "v"(td[0][3]),
+                 "v"(tlora), "v"(tcount));
+    if (m >= tcount || tlora < 0 || tlora >= p.max_loras) continue;  // unused or gap tile
 
     int s = 0;
 #pragma unroll
@@ -205,9 +194,6 @@ void expand_kernel(ExpandParams p) {
     // adapter (or whose column is past the slice) reads a clamped, valid
     // location, and its results are simply not stored; the matrix-core rows
     // of such a token, and the columns of such a column, touch nothing else.
-    auto bmat_of = [&](int slot) {
-      return bslice + static_cast<int64_t>(tab.lora[slot]) * n_s * RANK;
-    };
     // B chunk: piece q = lane + 64 i is piece q % (RANK/8) of chunk row
     // q / (RANK/8); rows past the slice's end read its last row (their columns
     // are never stored).
@@ -229,18 +215,16 @@ void expand_kernel(ExpandParams p) {
         bw[bslot<RANK>(q / kRowPieces, q % kRowPieces)] = bs.v[i];
       }
     };
-    const uint16_t* bmat0 = bmat_of(sr.first);
+    const uint16_t* bmat0 = bslice + static_cast<int64_t>(tlora) * n_s * RANK;
 
-    // y rows (a row without an adapter reads row 0 and is never stored) and
-    // the grouped position of each output row.
+    // y rows (a pad entry reads row 0 and is never stored)
     int64_t yrow[MW][4];
     bool dval[MW][4];
 #pragma unroll
     for (int mb = 0; mb < MW; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int q = pos0 + 16 * mb + 4 * grp + j;
-        dval[mb][j] = row_valid(tab, q, td[mb][j], p.max_tokens);
+        dval[mb][j] = td[mb][j] >= 0 && td[mb][j] < p.max_tokens;
         yrow[mb][j] = static_cast<int64_t>(dval[mb][j] ? td[mb][j] : 0) * p.ldy + off_s;
       }
 
@@ -276,7 +260,7 @@ void expand_kernel(ExpandParams p) {
         const int mb = item / kSteps;
         const int q = item - mb * kSteps;
         const int k0 = RANK == 8 ? 4 * khalf : 16 * q + 8 * khalf;
-        const bool aval = row_valid(tab, pos0 + 16 * mb + c, ta[mb], p.max_tokens);
+        const bool aval = ta[mb] >= 0 && ta[mb] < p.max_tokens;
         const float* src0 =
             p.buf + (static_cast<int64_t>(s) * p.max_tokens + (aval ? ta[mb] : 0)) * RANK + k0;
         float v[kPer];
@@ -324,14 +308,13 @@ void expand_kernel(ExpandParams p) {
       }
     __syncthreads();  // the next unit may overwrite a_lds
 
-    // One slot's pass over one chunk (its B in this wave's LDS region): acc =
-    // y + buf . B^T, stored for the rows of that slot.
-    auto pass = [&](int ch, int s_begin, int s_end) {
+    // One pass over one chunk (its B in this wave's LDS region): acc =
+    // y + buf . B^T, stored for the tile's rows.
+    auto pass = [&](int ch) {
       const int col = ch * kExpandCols + 8 * c;  // first of this lane's 8 columns
       const bool col_ok = col < n_s;
 #pragma unroll
       for (int mb = 0; mb < MW; ++mb) {
-        if (pos0 + 16 * mb >= s_end || pos0 + 16 * mb + 16 <= s_begin) continue;  // wave-uniform
         f32x4 acc[8];
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
@@ -359,8 +342,7 @@ void expand_kernel(ExpandParams p) {
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int q = pos0 + 16 * mb + 4 * grp + j;
-          if (col_ok && dval[mb][j] && q >= s_begin && q < s_end) {
+          if (col_ok && dval[mb][j]) {
             const u32x4 out = {pack_bf16x2(acc[0][j], acc[1][j]), pack_bf16x2(acc[2][j], acc[3][j]),
                                pack_bf16x2(acc[4][j], acc[5][j]), pack_bf16x2(acc[6][j], acc[7][j])};
             store16_stream(p.y + yrow[mb][j] + col, out);
@@ -369,19 +351,8 @@ void expand_kernel(ExpandParams p) {
       }
     };
 
-    // All passes over one chunk: the first slot with its B already in LDS,
-    // then (a tile across adapters) one B load and pass per further slot.  The
-    // wave's own LDS reads and writes stay in program order, so the region can
-    // be refilled right after a pass.
-    auto passes = [&](int ch) {
-      pass(ch, tab.start[sr.first], tab.end[sr.first]);
-      for (int slot = sr.first + 1; slot <= sr.last; ++slot) {
-        BStage<RANK> bx;
-        load_b(bmat_of(slot), ch, bx);
-        stage_b(bx);
-        pass(ch, tab.start[slot], tab.end[slot]);
-      }
-    };
+    // (The wave's own LDS reads and writes stay in program order, so its B
+    // region can be refilled right after a pass.)
     stage_b(bnext);
     if (ch0 < range_end) {  // wave-uniform
       // Steady state: the next chunk's loads are issued unconditionally before
@@ -390,12 +361,12 @@ void expand_kernel(ExpandParams p) {
       for (; ch + kExpandWaves < range_end; ch += kExpandWaves) {
         load_y(ch + kExpandWaves, ynext);
         load_b(bmat0, ch + kExpandWaves, bnext);
-        passes(ch);
+        pass(ch);
 #pragma unroll
         for (int mb = 0; mb < MW; ++mb) ycur[mb] = ynext[mb];
         stage_b(bnext);
       }
-      passes(ch);
+      pass(ch);
     }
   }
 }
@@ -697,7 +668,7 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
   // kernel chooses the range length from the batch's tile count (0 here).
   const bool shared = rank >= 32;
   const int64_t tiles = shared ? (static_cast<int64_t>(max_tokens) + kSharedTile - 1) / kSharedTile + max_loras
-                               : (static_cast<int64_t>(max_tokens) + kExpandTile - 1) / kExpandTile;
+                               : LORA_MAX_TILES(static_cast<int64_t>(max_tokens), max_loras);
   int64_t cpr = 0;
   if (!shared) {
     cpr = tiles * total_chunks / (static_cast<int64_t>(num_cus) * 16);
@@ -733,6 +704,10 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
   p.counts = meta.num_tokens_per_lora;
   p.starts = meta.lora_token_start;
   p.num_active = meta.num_active;
+  p.tile_ids = meta.tile_token_ids;
+  p.tile_lora = meta.tile_lora;
+  p.num_tiles = meta.num_tiles;
+  p.max_tiles = LORA_MAX_TILES(max_tokens, max_loras);
   p.max_tokens = max_tokens;
   p.max_loras = max_loras;
 

@@ -53,6 +53,10 @@ struct ShrinkParams {
   const int32_t* counts;
   const int32_t* starts;
   const int32_t* num_active;
+  const int32_t* tile_ids;   // the padded grouped order (16-token tiles)
+  const int32_t* tile_lora;
+  const int32_t* num_tiles;
+  int max_tiles;             // tiles the padded order may use
   int max_tokens;
   int max_loras;
 };
@@ -62,16 +66,19 @@ struct ShrinkParams {
 // fetched feeds MW matrix-core ops.
 template <int NB, int MW>
 __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) {
+  static_assert(MW == 1, "a tile of the padded grouped order holds 16 tokens");
   constexpr int kTile = 16 * MW;
-  __shared__ SegmentTable tab;
   __shared__ f32x4 red[kShrinkWaves][NB][kWave];
   __shared__ const uint16_t* slice_a[LORA_MAX_SLICES];  // per-lane slice lookup without
                                                         // indexing the argument block
   if (threadIdx.x < LORA_MAX_SLICES) slice_a[threadIdx.x] = p.a[threadIdx.x];
+  __syncthreads();
 
-  build_segment_table<kTile>(tab, p.active_ids, p.counts, p.starts, p.num_active, p.max_loras,
-                             p.max_tokens);
-  const int num_tiles = tab.num_tiles;
+  // Units over every tile the padded order may use (tile fastest), so that a
+  // unit's tile is known before the batch's tile count arrives: the unit's
+  // token ids, its adapter and the count load in one round trip, and units of
+  // tiles past the count do nothing.
+  const int num_tiles = p.max_tiles;
   const int units = num_tiles * p.num_splits * p.num_groups;
 
   const int lane = lane_id();
@@ -86,7 +93,15 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
     const int m = u - pg * num_tiles;
     const int part = pg / p.num_groups;
     const int o0 = (pg - part * p.num_groups) * 16 * NB;  // first output of the group
-    const Tile tile = resolve_tile<kTile>(tab, m);
+    const int tiles_used = *p.num_tiles;
+    const int tile_lora = p.tile_lora[m];
+    const int tile_id = p.tile_ids[kTile * m + col];  // this lane's token column
+    // (the three loads go out together: the compiler would otherwise sink the
+    // tile's two below the test, a second round trip)
+    asm volatile("" : : "v"(tile_id), "v"(tile_lora), "v"(tiles_used));
+    if (m >= tiles_used) continue;  // wave-uniform
+    Tile tile;
+    tile.lora = tile_lora >= 0 && tile_lora < p.max_loras ? tile_lora : 0;
     const int kbeg = part * p.split_len;
     const int kend = min(p.hidden, kbeg + p.split_len);
 
@@ -161,9 +176,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
     const int nw = kc < kend ? (kend - kc + kStride - 1) / kStride : 0;  // wave-uniform
     kc = kc < kend ? kc : ksafe;
     int tok[MW];
-#pragma unroll
-    for (int mb = 0; mb < MW; ++mb)
-      tok[mb] = tile_token(p.sorted, tile.first, tile.rows, 16 * mb + col, p.max_tokens);
+    tok[0] = tile_id >= 0 && tile_id < p.max_tokens ? tile_id : -1;  // -1: a pad entry
     Chunk c0, c1;
     load_a(kc, c0);
 #pragma unroll
@@ -456,7 +469,7 @@ int shrink_group_blocks(int nb_total) { return nb_total <= 8 ? nb_total : 8; }
 // LDS-staged kernel) for larger ones.
 int shrink_tile_blocks(int max_tokens, int nb) {
 #ifdef LORA_TUNING
-  if (const char* e = getenv("LORA_SHRINK_MW")) return atoi(e);
+  if (const char* e = getenv("LORA_SHRINK_MW")) return atoi(e) >= 4 ? 4 : 1;
 #endif
   if (max_tokens <= 512) return 1;
   return 4;  // the LDS-staged kernel (64-token tiles)
@@ -467,11 +480,8 @@ int shrink_split_len(int hidden, int num_splits) {
   return (per + kShrinkChunk - 1) / kShrinkChunk * kShrinkChunk;
 }
 
-int shrink_grid(int max_tokens, int max_loras, int num_splits, int num_groups, int mw,
-                int num_cus) {
-  const int tile = kShrinkTile * mw;
-  const int64_t tiles = (static_cast<int64_t>(max_tokens) + tile - 1) / tile + max_loras;
-  const int64_t units = tiles * num_splits * num_groups;
+int shrink_grid(int max_tiles, int num_splits, int num_groups, int num_cus) {
+  const int64_t units = static_cast<int64_t>(max_tiles) * num_splits * num_groups;
   const int64_t cap = static_cast<int64_t>(num_cus) * 8;
   const int64_t g = units < cap ? units : cap;
   return static_cast<int>((g + kXcds - 1) / kXcds * kXcds);  // whole rounds over the XCDs
@@ -498,6 +508,10 @@ hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint1
   p.counts = meta.num_tokens_per_lora;
   p.starts = meta.lora_token_start;
   p.num_active = meta.num_active;
+  p.tile_ids = meta.tile_token_ids;
+  p.tile_lora = meta.tile_lora;
+  p.num_tiles = meta.num_tiles;
+  p.max_tiles = LORA_MAX_TILES(max_tokens, max_loras);
   p.max_tokens = max_tokens;
   p.max_loras = max_loras;
   const int nb_total = (num_slices * rank + 15) / 16;
@@ -522,11 +536,8 @@ hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint1
       default: return launch_shrink_lds_nb<8>(p, grid, stream);
     }
   }
-  const int grid = shrink_grid(max_tokens, max_loras, num_splits, p.num_groups, mw, num_cus);
-  switch (mw) {
-    case 1: return launch_shrink_mw<1>(p, nb, grid, stream);
-    default: return launch_shrink_mw<2>(p, nb, grid, stream);
-  }
+  const int grid = shrink_grid(p.max_tiles, num_splits, p.num_groups, num_cus);
+  return launch_shrink_mw<1>(p, nb, grid, stream);
 }
 
 }  // namespace lora
