@@ -80,7 +80,7 @@ __global__ __launch_bounds__(THREADS) void metadata_kernel(const int32_t* __rest
   constexpr int kBlock = THREADS * kPerThread;
   __shared__ int present[LORA_MAX_LORAS + 1];
   __shared__ int wave_below[kWaves], wave_members[kWaves], wave_none[kWaves], wave_scan[kWaves];
-  __shared__ int group_slot, groups_present;
+  __shared__ int32_t staged[kBlock];  // one block's members of g, in rank order
 
   const int g = blockIdx.x;
   const int groups = max_loras + 1;
@@ -118,48 +118,44 @@ __global__ __launch_bounds__(THREADS) void metadata_kernel(const int32_t* __rest
     n_none += wave_none[w];
   }
 
-  // Wave 0: slot of g among the adapters present, how many are present, and
-  // the slot entries (group 0 writes the unused slots and the count).
-  if (wave == 0) {
-    int slot = 0, npresent = 0;
-    for (int base = 0; base < groups; base += kWave) {
-      const int i = base + lane;
-      const bool p = i >= 1 && i < groups && present[i] != 0;
-      slot += __popcll(__ballot(p && i < g));
-      npresent += __popcll(__ballot(p));
-    }
-    if (g == 0) {
-      for (int i = npresent + lane; i < max_loras; i += kWave) {
-        out.active_ids[i] = -1;
-        out.counts[i] = 0;
-        out.starts[i] = num_tokens;
-      }
-      if (lane == 0) *out.num_active = npresent;
-      if (lane == 0 && npresent == 0) *out.num_tiles = 0;
-    } else if (total > 0 && lane == 0) {
-      out.active_ids[slot] = g - 1;
-      out.counts[slot] = total;
-      out.starts[slot] = start;
-    }
-    if (lane == 0) {
-      group_slot = slot;
-      groups_present = npresent;
-    }
-  }
-  if (total == 0) return;  // uniform across the workgroup
-  __syncthreads();
+  if (g > 0 && total == 0) return;  // an adapter absent from the batch (uniform)
 
-  // An adapter's run of the padded order: [pstart, pstart + total), then -1 up
-  // to the next run's start (or, for the last run, to the end of its tile),
-  // and the tiles' adapter ids (-1 for a gap tile of -1 entries).  Group 0
-  // (no adapter) has no run.
+  // Every wave: g's slot among the adapters present and how many are present
+  // (a few ballots; no barrier to share them).
+  int k = 0, npresent = 0;
+  for (int base = 0; base < groups; base += kWave) {
+    const int i = base + lane;
+    const bool p = i >= 1 && i < groups && present[i] != 0;
+    k += __popcll(__ballot(p && i < g));
+    npresent += __popcll(__ballot(p));
+  }
+
+  // An adapter's run of the padded order starts at pstart (group 0, no
+  // adapter, has none).
   const bool has_run = g > 0;
-  const int k = group_slot;
   const int s_k = start - n_none;  // tokens of lower adapters
   const int pstart = round_up_tile(s_k + (kMetaTile - 1) * k);
-  if (has_run) {
+
+  // The slot entries (group 0: the unused slots and the counts) and, past the
+  // run's members, -1 up to the next run's start (for the last run, to the end
+  // of its tile) and the tiles' adapter ids (-1 for a gap tile).  These depend
+  // on the counts only, so they go out before the placing.
+  if (g == 0) {
+    for (int i = npresent + tid; i < max_loras; i += THREADS) {
+      out.active_ids[i] = -1;
+      out.counts[i] = 0;
+      out.starts[i] = num_tokens;
+    }
+    if (tid == 0) *out.num_active = npresent;
+    if (tid == 0 && npresent == 0) *out.num_tiles = 0;
+  } else {
+    if (tid == 0) {
+      out.active_ids[k] = g - 1;
+      out.counts[k] = total;
+      out.starts[k] = start;
+    }
     const int run_end = round_up_tile(pstart + total);
-    const bool last = k == groups_present - 1;
+    const bool last = k == npresent - 1;
     const int pnext = last ? run_end : round_up_tile(s_k + total + (kMetaTile - 1) * (k + 1));
     for (int i = pstart + total + tid; i < pnext; i += THREADS) out.tile_ids[i] = -1;
     for (int m = pstart / kMetaTile + tid; m < pnext / kMetaTile; m += THREADS)
@@ -171,7 +167,7 @@ __global__ __launch_bounds__(THREADS) void metadata_kernel(const int32_t* __rest
   // per-thread member counts (thread order is token order within a block).  A
   // batch of one block reuses the groups already in registers.
   int placed = 0;
-  for (int b0 = 0; b0 < num_tokens; b0 += kBlock) {
+  for (int b0 = 0; total > 0 && b0 < num_tokens; b0 += kBlock) {
     const int t0 = b0 + tid * kPerThread;
     if (num_tokens > kBlock) load_groups(mapping, num_tokens, max_loras, t0, grp);
     int mine = 0;
@@ -187,19 +183,24 @@ __global__ __launch_bounds__(THREADS) void metadata_kernel(const int32_t* __rest
       before += w < wave ? n : 0;
       block_total += n;
     }
-    int pos = placed + before + incl - mine;  // rank of this thread's first member
+    // The block's members go to LDS in rank order, then out to both orders as
+    // contiguous runs (consecutive lanes, consecutive words: whole lines rather
+    // than one scattered word per member).
+    int r = before + incl - mine;  // rank within the block of this thread's first member
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
-      if (grp[e] == g) {
-        if (start + pos < num_tokens) {
-          out.sorted[start + pos] = t0 + e;
-          if (has_run) out.tile_ids[pstart + pos] = t0 + e;
-        }
-        ++pos;
+      if (grp[e] == g) staged[r++] = t0 + e;
+    }
+    __syncthreads();
+    for (int i = tid; i < block_total; i += THREADS) {
+      const int32_t t = staged[i];
+      if (start + placed + i < num_tokens) {
+        out.sorted[start + placed + i] = t;
+        if (has_run) out.tile_ids[pstart + placed + i] = t;
       }
     }
     placed += block_total;
-    if (b0 + kBlock < num_tokens) __syncthreads();  // wave_scan is reused by the next block
+    if (b0 + kBlock < num_tokens) __syncthreads();  // wave_scan and staged are reused
   }
 }
 
