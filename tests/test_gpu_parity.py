@@ -185,6 +185,11 @@ SHAPES = [
     (600, 640, 65536, [16], 16, 3, 0, 8, 8),
     (300, 320, 384, [64, 32, 16, 8], 64, 3, 8, 8, 3),
     (700, 700, 384, [64, 32, 16, 8], 64, 3, 8, 8, 3),
+    # every adapter slot in play with few tokens each: most tiles of the padded
+    # order are single-token runs or gaps, and most of the walked tiles unused
+    (100, 100, 256, [64, 64], 16, 256, 0, 0, 2),
+    (300, 333, 512, [128], 8, 256, 8, 8, 5),
+    (2000, 2040, 256, [96, 32], 16, 256, 0, 0, 3),
 ]
 
 
