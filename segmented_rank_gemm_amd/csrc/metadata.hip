@@ -14,7 +14,7 @@
 // tokens sit in lower groups (its start), which groups occur at all (its slot
 // among the adapters present and, for group 0, how many there are), and, per
 // member, how many members precede it in token order (its rank).  Counts come
-// from per-thread tallies summed in a fixed order, occurrence from an LDS flag
+// from wave ballots summed in a fixed order, occurrence from an LDS flag
 // per group, ranks from a block-wide exclusive scan of the per-thread member
 // counts; no global atomics, so the result is the same bits on every run.
 //
@@ -91,19 +91,19 @@ __global__ __launch_bounds__(THREADS) void metadata_kernel(const int32_t* __rest
   __syncthreads();
 
   // Count pass: tokens in lower groups, members of g, occurring groups.
+  // Wave totals come straight from ballots (no cross-lane reduction).
   int grp[kPerThread];
-  int below = 0, members = 0, none = 0;
+  int wb = 0, wm = 0, wn = 0;
   for (int b0 = 0; b0 < num_tokens; b0 += kBlock) {
     load_groups(mapping, num_tokens, max_loras, b0 + tid * kPerThread, grp);
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
       if (grp[e] >= 0) present[grp[e]] = 1;  // benign: every writer stores 1
-      below += (grp[e] >= 0 && grp[e] < g) ? 1 : 0;
-      members += grp[e] == g ? 1 : 0;
-      none += grp[e] == 0 ? 1 : 0;
+      wb += __popcll(__ballot(grp[e] >= 0 && grp[e] < g));
+      wm += __popcll(__ballot(grp[e] == g));
+      wn += __popcll(__ballot(grp[e] == 0));
     }
   }
-  const int wb = wave_sum(below), wm = wave_sum(members), wn = wave_sum(none);
   if (lane == 0) {
     wave_below[wave] = wb;
     wave_members[wave] = wm;
