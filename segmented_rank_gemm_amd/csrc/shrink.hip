@@ -32,7 +32,6 @@ namespace lora {
 
 constexpr int kShrinkThreads = 256;
 constexpr int kShrinkWaves = kShrinkThreads / kWave;
-constexpr int kShrinkTile = 16;   // tokens per unit (the MFMA N dimension)
 constexpr int kShrinkChunk = 64;  // hidden elements per wave step (two MFMA K-steps)
 
 struct ShrinkParams {
