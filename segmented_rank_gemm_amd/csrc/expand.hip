@@ -236,15 +236,15 @@ void expand_kernel(ExpandParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) yb[mb].v[j] = load16_stream(p.y + yrow[mb][j] + colc);
     };
-    // First chunk: y, then B, then (below) the shrink's parts, all issued
+    // First chunk: B, then y, then (below) the shrink's parts, all issued
     // unconditionally (a wave without a chunk in this range reads the range's
     // last one and stores nothing), so that the compiler's wait counts stay
     // exact and no load waits for another.
     const int chf = ch0 < range_end ? ch0 : range_end - 1;
     YBlock ycur[MW], ynext[MW];
-    load_y(chf, ycur);
     BStage<RANK> bnext;
     load_b(bmat0, chf, bnext);
+    load_y(chf, ycur);
 
     // Rank operand, built cooperatively: item (mb, q) is one MFMA step of one
     // block, i.e. one register set of the wave; its lane (c, grp) sums the
@@ -663,16 +663,23 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
     }
   }
   // Ranks 8 and 16: chunks per wave in a workgroup unit (the unit spans 4x as
-  // many), as many as still give every CU ~16 units at the largest batch, at
-  // most 8.  Ranks 32 and 64 (shared-B kernel, all waves on one chunk): the
-  // kernel chooses the range length from the batch's tile count (0 here).
+  // many).  Small batches: as many as still give every CU ~16 units, at most 8.
+  // Large batches: 2, i.e. 1024-column ranges taken one after another along a
+  // tile's row (see the unit order below), so that the workgroups in flight
+  // hold few distinct y rows at a time (measured on the gate_up shape at 1-16 K
+  // tokens and the qkv shape at 1-4 K: 2 was the fastest of 1, 2, 3, 4, 8
+  // everywhere, 5% ahead of 8 on the 8 K-token prefill batch).  Ranks 32 and 64
+  // (shared-B kernel, all waves on one chunk): the kernel chooses the range
+  // length from the batch's tile count (0 here).
   const bool shared = rank >= 32;
+  const bool large = max_tokens > 512;
   const int64_t tiles = shared ? (static_cast<int64_t>(max_tokens) + kSharedTile - 1) / kSharedTile + max_loras
                                : LORA_MAX_TILES(static_cast<int64_t>(max_tokens), max_loras);
   int64_t cpr = 0;
   if (!shared) {
     cpr = tiles * total_chunks / (static_cast<int64_t>(num_cus) * 16);
     cpr = cpr < 1 ? 1 : (cpr > 8 ? 8 : cpr);
+    if (large) cpr = 2;
   }
 #ifdef LORA_TUNING
   if (const char* e = getenv("LORA_EXPAND_CPR")) cpr = atoi(e);
@@ -682,7 +689,7 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
   // XCD's workgroups sweep whole y rows of a few tiles at a time (better DRAM
   // page locality: measured 125 vs 128 us on the prefill batch); small ones
   // keep tiles next to each other (their few rows fit a single sweep anyway).
-  p.order_range_fastest = max_tokens > 512 ? 1 : 0;
+  p.order_range_fastest = large ? 1 : 0;
 #ifdef LORA_TUNING
   if (const char* e = getenv("LORA_EXPAND_ORDER")) p.order_range_fastest = atoi(e);
 #endif
