@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=None, help="buffer copies (default: >= 1 GiB)")
     ap.add_argument("--kernel-reps", type=int, default=50,
                     help="graph replays per single-kernel timing")
+    ap.add_argument("--tune", action="store_true",
+                    help="choose the shrink's part count by timing the candidates on this batch "
+                    "(segmented_rank_gemm_amd.tuning) instead of the size rule")
     ap.add_argument("--layers", type=int, default=32,
                     help="layers of the layer-stack timing (one metadata step, then shrink + "
                     "expand per layer on its own weights and activations; 0 skips it)")
@@ -253,6 +256,18 @@ def run_config(idx, args):
     st = workload_stats(w)
     splits = srg.lora_shrink_default_splits(w.hidden, w.max_tokens, w.max_loras, w.num_slices,
                                             w.rank)
+    tuning = None
+    if args.tune:
+        from segmented_rank_gemm_amd.tuning import tune_shrink_splits
+        log("[bench] tuning the shrink's part count")
+        one = Sets(w, 1, splits)
+        s0 = one.sets[0]
+        tuning = tune_shrink_splits(s0["x"], s0["a"], s0["b"], s0["y"], float(w.scale), s0["meta"])
+        del one, s0
+        torch.cuda.empty_cache()
+        splits = tuning["best"]
+        tuning = {"rule": tuning["default"], "best": tuning["best"],
+                  "pair_us": {str(k): round(v, 3) for k, v in tuning["us"].items()}}
     sb = set_bytes(w, splits)
     R = args.rotate or max(2, math.ceil(ROTATE_BYTES / sb))
     log(f"[bench] {R} rotated buffer sets of {sb / 1e6:.1f} MB, {splits} shrink parts")
@@ -370,6 +385,7 @@ def run_config(idx, args):
             "active_tokens": st["active_tokens"], "hidden": w.hidden, "slices": w.slices,
             "rank": w.rank, "max_loras": w.max_loras, "active_adapters": st["active_adapters"],
             "scale": w.scale, "accumulate": "fp32", "shrink_parts": splits,
+            "shrink_parts_from": "measured" if tuning else "size rule", "tuning": tuning,
             "rotated_sets": R, "rotated_sets_per_kernel": rot, "parallelism": "single GPU",
         },
         "roofline": {

@@ -147,3 +147,16 @@ def test_binding_rejects_host_tensors():
         srg.lora_shrink(torch.zeros(4, 8, dtype=torch.bfloat16),
                         [torch.zeros(2, 8, 8, dtype=torch.bfloat16)], 1.0,
                         torch.zeros(1, 1, 4, 8), 1, meta_like)
+
+
+def test_tuning_candidates():
+    from segmented_rank_gemm_amd.tuning import candidate_splits
+    for hidden, maxT, L, S, r in [(4096, 256, 4, 3, 8), (11008, 2048, 16, 1, 64), (128, 16, 2, 1, 8),
+                                  (256, 16, 2, 1, 8), (8192, 4096, 64, 3, 32), (65536, 1, 1, 4, 16)]:
+        c = candidate_splits(hidden, maxT, L, S, r)
+        d = srg.lora_shrink_default_splits(hidden, maxT, L, S, r)
+        chunks = -(-hidden // 64)
+        assert c == sorted(set(c)) and c[0] == 1
+        assert d in c
+        assert all(1 <= v <= srg.LORA_MAX_SPLITS for v in c)
+        assert all(v <= chunks for v in c if v != d)

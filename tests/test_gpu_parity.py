@@ -364,3 +364,24 @@ def test_graph_replay_matches_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert np.array_equal(H.from_dev_bf16(d.y), eager)
+
+
+def test_tuned_splits_give_parity():
+    """The tuner times each candidate on copies of the operands, leaves the
+    caller's tensors untouched, and its choice passes the parity check."""
+    from segmented_rank_gemm_amd.tuning import tune_shrink_splits
+    mapping = np.random.default_rng(11).integers(-1, 4, size=600).astype(np.int32)
+    w = make_custom_workload(7, 600, 1024, [512, 256], 16, 4, 1.25, mapping)
+    d = H.upload(w)
+    srg.lora_prepare_metadata(d.mapping, w.num_tokens, d.meta)
+    y_before = d.y.clone()
+    res = tune_shrink_splits(d.x, d.lora_a, d.lora_b, d.y, float(w.scale), d.meta,
+                             candidates=[1, 2, 4], rotate_bytes=1 << 24, reps=3)
+    torch.cuda.synchronize()
+    assert set(res["us"]) == {1, 2, 4} and res["best"] in (1, 2, 4)
+    assert all(t > 0 for t in res["us"].values())
+    assert torch.equal(d.y.view(torch.int16), y_before.view(torch.int16))
+    d2 = H.upload(w, num_splits=res["best"])
+    H.run_step(d2)
+    torch.cuda.synchronize()
+    _full_check(w, d2)
