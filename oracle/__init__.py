@@ -143,6 +143,28 @@ def prepare_tiles(mapping: np.ndarray, max_loras: int) -> Dict[str, np.ndarray]:
                 num_tiles=np.array([num_tiles], dtype=np.int32))
 
 
+def count_runs(mapping: np.ndarray, max_loras: int) -> np.ndarray:
+    """num_runs [1]: the number of maximal runs of consecutive tokens (batch
+    order) that share one adapter id >= 0, after ids outside [-1, max_loras)
+    are read as -1.  Tokens without an adapter belong to no run and separate
+    the runs around them.
+
+    This is the batch's segment count in the sense of the MLC-LLM issue's
+    Overview (Punica's segment vector: consecutive rows multiplied by the same
+    adapter) for the batch as given, before any grouping.  Written from that
+    definition, token by token.
+    """
+    m = np.asarray(mapping, dtype=np.int64).reshape(-1)
+    ids = [int(v) if -1 <= v < max_loras else -1 for v in m.tolist()]
+    runs = 0
+    prev = -1
+    for l in ids:
+        if l >= 0 and l != prev:
+            runs += 1
+        prev = l
+    return np.array([runs], dtype=np.int32)
+
+
 def shrink(x: np.ndarray, lora_a: List[np.ndarray], mapping: np.ndarray, max_loras: int,
            rank: int, scale: float, num_threads: int = 0) -> np.ndarray:
     """fp64 buf [S, T, rank]; rows of tokens without an adapter stay NaN."""

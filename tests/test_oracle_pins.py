@@ -143,6 +143,39 @@ def test_metadata_matches_selection_brute_force(seed):
         assert meta[k].tolist() == v, k
 
 
+# ------------------------------------------------ runs in batch order -------
+
+def test_runs_worked_examples():
+    # by hand: [2, -1, 0, 2, 1, -1, 0, 7] with 3 slots reads 7 as -1, leaving
+    # the runs {0}, {2}, {3}, {4}, {6}
+    assert oracle.count_runs(np.array([2, -1, 0, 2, 1, -1, 0, 7]), 3).tolist() == [5]
+    # 0 0 0 | 1 1 | (-1) | 1 1 | 0: the -1 splits the ones
+    assert oracle.count_runs(np.array([0, 0, 0, 1, 1, -1, 1, 1, 0]), 2).tolist() == [4]
+    assert oracle.count_runs(np.array([5, 5, 5]), 4).tolist() == [0]
+    assert oracle.count_runs(np.zeros(0, dtype=np.int32), 4).tolist() == [0]
+
+
+@pytest.mark.parametrize("kind", FUZZ_KINDS)
+@pytest.mark.parametrize("T,L", [(1, 1), (37, 3), (1000, 16), (4096, 64)])
+def test_runs_properties(kind, T, L):
+    import itertools
+    rng = np.random.default_rng(T * 7 + L)
+    mapping = make_fuzz_mapping(rng, T, L, kind)
+    ids = _sanitize(mapping, L)
+    n = int(oracle.count_runs(mapping, L)[0])
+    # the library's run-length grouping, keeping the groups of an adapter
+    assert n == sum(1 for k, _ in itertools.groupby(ids.tolist()) if k >= 0)
+    # bounds: at least one run per adapter present, at most one per token
+    assert len(set(ids[ids >= 0].tolist())) <= n <= int(np.sum(ids >= 0))
+    # a grouped batch (the stable sort of itself) has exactly one run per adapter
+    assert int(oracle.count_runs(np.sort(ids), L)[0]) == len(set(ids[ids >= 0].tolist()))
+    # splitting the batch: the halves' runs add up, less one where a run straddles the cut
+    c = T // 2
+    a, b = ids[:c], ids[c:]
+    join = 1 if c > 0 and c < T and a[-1] >= 0 and a[-1] == b[0] else 0
+    assert n == int(oracle.count_runs(a, L)[0]) + int(oracle.count_runs(b, L)[0]) - join
+
+
 # ------------------------------------------------ padded tiles of the order --
 
 def test_tiles_worked_example():
