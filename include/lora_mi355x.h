@@ -103,6 +103,17 @@ typedef enum lora_status {
  *                       below num_tiles, or -1 for a tile of -1 entries.
  *   num_tiles           int32 [1]: tiles in use.
  *   Entries at or past num_tiles are never written.
+ *
+ * And one count of the batch as given (before grouping):
+ *
+ *   num_runs            int32 [1]: the number of maximal runs of consecutive
+ *                       tokens (batch order) sharing one adapter id >= 0;
+ *                       tokens without an adapter belong to no run.  Punica's
+ *                       segment count for the batch as it arrives (MLC-LLM
+ *                       issue, Overview).  Runs of at least a few tokens mean
+ *                       that a tile of the grouped order holds neighbouring
+ *                       rows of x and y; the expand picks its walk over the
+ *                       tiles by it.
  */
 typedef struct lora_meta {
   int32_t *sorted_token_ids;
@@ -113,6 +124,7 @@ typedef struct lora_meta {
   int32_t *tile_token_ids;
   int32_t *tile_lora;
   int32_t *num_tiles;
+  int32_t *num_runs;
 } lora_meta_t;
 
 /*
@@ -132,8 +144,8 @@ typedef struct lora_meta {
  *   meta                host pointer to the output buffers (all non-null).
  *
  * Writes sorted_token_ids[0:num_tokens], all max_loras entries of the three
- * per-slot arrays, num_active, and the padded tiles below num_tiles with
- * num_tiles.  A stable counting sort: bit-for-bit deterministic, no atomics on
+ * per-slot arrays, num_active, the padded tiles below num_tiles with
+ * num_tiles, and num_runs.  A stable counting sort: bit-for-bit deterministic, no atomics on
  * global memory.  Grid: max_loras + 1 workgroups (of 64, 256 or 1024 threads
  * by max_tokens).
  */

@@ -48,7 +48,8 @@ class _MetaStruct(ctypes.Structure):
     _fields_ = [("sorted_token_ids", ctypes.c_void_p), ("active_lora_ids", ctypes.c_void_p),
                 ("num_tokens_per_lora", ctypes.c_void_p), ("lora_token_start", ctypes.c_void_p),
                 ("num_active", ctypes.c_void_p), ("tile_token_ids", ctypes.c_void_p),
-                ("tile_lora", ctypes.c_void_p), ("num_tiles", ctypes.c_void_p)]
+                ("tile_lora", ctypes.c_void_p), ("num_tiles", ctypes.c_void_p),
+                ("num_runs", ctypes.c_void_p)]
 
 TILE = 16  # positions per tile of the padded grouped order (LORA_TILE)
 
@@ -138,12 +139,13 @@ class LoraMeta:
         self.tile_token_ids = torch.empty(nt * TILE, **opts)
         self.tile_lora = torch.empty(nt, **opts)
         self.num_tiles = torch.empty(1, **opts)
+        self.num_runs = torch.empty(1, **opts)
         self._struct = _MetaStruct(*(int(t.data_ptr()) for t in self.tensors()))
 
     def tensors(self):
         return (self.sorted_token_ids, self.active_lora_ids, self.num_tokens_per_lora,
                 self.lora_token_start, self.num_active, self.tile_token_ids, self.tile_lora,
-                self.num_tiles)
+                self.num_tiles, self.num_runs)
 
     @property
     def struct_ref(self):

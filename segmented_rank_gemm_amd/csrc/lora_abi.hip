@@ -38,7 +38,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool meta_ok(const lora_meta_t* m) {
   return m && m->sorted_token_ids && m->active_lora_ids && m->num_tokens_per_lora &&
          m->lora_token_start && m->num_active && m->tile_token_ids && m->tile_lora &&
-         m->num_tiles;
+         m->num_tiles && m->num_runs;
 }
 
 bool sizes_ok(int32_t max_tokens, int32_t max_loras) {

@@ -61,6 +61,7 @@ struct MetaOut {
   int32_t* tile_ids;
   int32_t* tile_lora;
   int32_t* num_tiles;
+  int32_t* num_runs;
 };
 
 constexpr int kMetaTile = LORA_TILE;
@@ -80,6 +81,7 @@ __global__ __launch_bounds__(THREADS) void metadata_kernel(const int32_t* __rest
   constexpr int kBlock = THREADS * kPerThread;
   __shared__ int present[LORA_MAX_LORAS + 1];
   __shared__ int wave_below[kWaves], wave_members[kWaves], wave_none[kWaves], wave_scan[kWaves];
+  __shared__ int wave_runs[kWaves];
   __shared__ int32_t staged[kBlock];  // one block's members of g, in rank order
 
   const int g = blockIdx.x;
@@ -90,32 +92,43 @@ __global__ __launch_bounds__(THREADS) void metadata_kernel(const int32_t* __rest
   for (int i = tid; i < groups; i += THREADS) present[i] = 0;
   __syncthreads();
 
-  // Count pass: tokens in lower groups, members of g, occurring groups.
+  // Count pass: tokens in lower groups, members of g, occurring groups, and
+  // (workgroup 0 only) the tokens that start a run of one adapter in batch
+  // order: an adapter other than the previous token's.
   // Wave totals come straight from ballots (no cross-lane reduction).
   int grp[kPerThread];
-  int wb = 0, wm = 0, wn = 0;
+  int wb = 0, wm = 0, wn = 0, wr = 0;
   for (int b0 = 0; b0 < num_tokens; b0 += kBlock) {
-    load_groups(mapping, num_tokens, max_loras, b0 + tid * kPerThread, grp);
+    const int t0 = b0 + tid * kPerThread;
+    load_groups(mapping, num_tokens, max_loras, t0, grp);
+    int prev = 0;  // group of token t0 - 1 (0: none, or no such token)
+    if (g == 0 && t0 > 0 && t0 <= num_tokens) prev = group_of(mapping[t0 - 1], max_loras);
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
       if (grp[e] >= 0) present[grp[e]] = 1;  // benign: every writer stores 1
       wb += __popcll(__ballot(grp[e] >= 0 && grp[e] < g));
       wm += __popcll(__ballot(grp[e] == g));
       wn += __popcll(__ballot(grp[e] == 0));
+      if (g == 0) {
+        wr += __popcll(__ballot(grp[e] > 0 && grp[e] != prev));
+        prev = grp[e];
+      }
     }
   }
   if (lane == 0) {
     wave_below[wave] = wb;
     wave_members[wave] = wm;
     wave_none[wave] = wn;
+    wave_runs[wave] = wr;
   }
   __syncthreads();
-  int start = 0, total = 0, n_none = 0;
+  int start = 0, total = 0, n_none = 0, runs = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     start += wave_below[w];
     total += wave_members[w];
     n_none += wave_none[w];
+    runs += wave_runs[w];
   }
 
   if (g > 0 && total == 0) return;  // an adapter absent from the batch (uniform)
@@ -147,6 +160,7 @@ __global__ __launch_bounds__(THREADS) void metadata_kernel(const int32_t* __rest
       out.starts[i] = num_tokens;
     }
     if (tid == 0) *out.num_active = npresent;
+    if (tid == 0) *out.num_runs = runs;
     if (tid == 0 && npresent == 0) *out.num_tiles = 0;
   } else {
     if (tid == 0) {
@@ -208,7 +222,7 @@ hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_token
                            const lora_meta_t& meta, hipStream_t stream) {
   const MetaOut out{meta.sorted_token_ids, meta.active_lora_ids, meta.num_tokens_per_lora,
                     meta.lora_token_start, meta.num_active, meta.tile_token_ids,
-                    meta.tile_lora, meta.num_tiles};
+                    meta.tile_lora, meta.num_tiles, meta.num_runs};
   if (max_tokens <= 64 * kPerThread) {
     hipLaunchKernelGGL(metadata_kernel<64>, dim3(max_loras + 1), dim3(64), 0, stream, mapping,
                        num_tokens, max_loras, out);

@@ -69,7 +69,7 @@ def run_step(d: DeviceWorkload, stream=None) -> None:
 
 
 META_KEYS = ["sorted_token_ids", "active_lora_ids", "num_tokens_per_lora", "lora_token_start",
-             "num_active", "tile_token_ids", "tile_lora", "num_tiles"]
+             "num_active", "tile_token_ids", "tile_lora", "num_tiles", "num_runs"]
 
 
 def meta_host(d: DeviceWorkload) -> dict:

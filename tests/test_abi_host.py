@@ -46,7 +46,7 @@ def test_status_strings():
 def _meta(**null):
     fields = dict(sorted_token_ids=FAKE, active_lora_ids=FAKE, num_tokens_per_lora=FAKE,
                   lora_token_start=FAKE, num_active=FAKE, tile_token_ids=FAKE, tile_lora=FAKE,
-                  num_tiles=FAKE)
+                  num_tiles=FAKE, num_runs=FAKE)
     fields.update(null)
     return ctypes.byref(srg._MetaStruct(**fields))
 
@@ -59,7 +59,7 @@ def _ptrs(n, value=FAKE):
     (-1, 16, 4, None), (17, 16, 4, None), (4, 0, 4, None), (4, 16, 0, None), (4, 16, 257, None),
     (4, 1 << 25, 4, None), (4, 16, 4, dict(num_active=None)), (4, 16, 4, dict(sorted_token_ids=None)),
     (4, 16, 4, dict(tile_token_ids=None)), (4, 16, 4, dict(tile_lora=None)),
-    (4, 16, 4, dict(num_tiles=None)),
+    (4, 16, 4, dict(num_tiles=None)), (4, 16, 4, dict(num_runs=None)),
 ])
 def test_prepare_metadata_rejects(num_tokens, max_tokens, max_loras, meta):
     m = _meta(**(meta or {}))

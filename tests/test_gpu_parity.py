@@ -47,6 +47,7 @@ def _check_meta(meta_gpu, ref, T, max_tokens, sorted_fill=-7, mapping=None, L=No
         assert int(meta_gpu["num_tiles"][0]) == nt
         assert np.array_equal(meta_gpu["tile_token_ids"][:nt * 16], tiles["tile_token_ids"])
         assert np.array_equal(meta_gpu["tile_lora"][:nt], tiles["tile_lora"])
+        assert np.array_equal(meta_gpu["num_runs"], oracle.count_runs(mapping, L))
 
 
 def _run_metadata(mapping, T, max_tokens, L):
