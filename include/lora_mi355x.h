@@ -28,9 +28,10 @@
  *   - Every pointer is a DEVICE pointer unless marked "host".  All memory is
  *     owned by the caller.  No call allocates, frees, synchronises or keeps
  *     state between calls; host arrays are read only during the call.
- *   - Every call enqueues exactly one kernel on `stream` and returns without
- *     waiting.  Launch grids depend only on the size arguments (max_tokens,
- *     max_loras, shapes), never on device data, so a sequence of calls can be
+ *   - Every call enqueues one kernel on `stream` (lora_prepare_and_shrink: one
+ *     or two, see there) and returns without waiting.  Launch grids depend
+ *     only on the size arguments (max_tokens, max_loras, shapes), never on
+ *     device data, so a sequence of calls can be
  *     captured once into a HIP graph and replayed.
  *   - Arguments are validated on the host before anything is enqueued; an
  *     invalid one returns LORA_ERR_INVALID_ARGUMENT and enqueues nothing.
@@ -195,6 +196,36 @@ lora_status_t lora_shrink(const uint16_t *x, int64_t ldx, int32_t hidden,
                           const uint16_t *const *lora_a, int32_t num_slices, int32_t rank,
                           float scale, float *buf, int32_t num_splits, const lora_meta_t *meta,
                           int32_t max_tokens, int32_t max_loras, hipStream_t stream);
+
+/*
+ * lora_prepare_and_shrink - lora_prepare_metadata followed by lora_shrink for
+ * the same batch, in one launch where the sizes allow it.
+ *
+ * Defined by: the two passages cited above (the grouping of an ungrouped
+ * batch, vLLM PR #13096 "Why do we need a new set of kernels"; the shrink
+ * kernel, its summary and "Kernel Code Change" item 2).  The fusion is this
+ * library's: a V1 step computes the grouping and the first layer's shrink back
+ * to back, and a launch boundary costs about as much as either kernel on a
+ * small batch.
+ *
+ * Arguments: those of lora_prepare_metadata (token_lora_mapping, num_tokens,
+ * max_tokens, max_loras, meta) and of lora_shrink (x, ldx, hidden, lora_a,
+ * num_slices, rank, scale, buf, num_splits), with the same meanings and
+ * checks.  Writes exactly what the two calls write, bit for bit (meta in
+ * full, buf rows of tokens with an adapter).
+ *
+ * With max_tokens <= 512 one kernel is enqueued: its first workgroups do the
+ * shrink, finding each tile's tokens from the map themselves, and the last
+ * max_loras + 1 workgroups compute the metadata.  Larger batches enqueue the
+ * metadata kernel and the shrink one after the other.  The grid still depends
+ * only on the sizes, so the call can be captured in a graph.
+ */
+lora_status_t lora_prepare_and_shrink(const int32_t *token_lora_mapping, int32_t num_tokens,
+                                      const uint16_t *x, int64_t ldx, int32_t hidden,
+                                      const uint16_t *const *lora_a, int32_t num_slices,
+                                      int32_t rank, float scale, float *buf, int32_t num_splits,
+                                      const lora_meta_t *meta, int32_t max_tokens,
+                                      int32_t max_loras, hipStream_t stream);
 
 /*
  * lora_expand - project each grouped token's rank-r vector up through its

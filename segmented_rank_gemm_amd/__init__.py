@@ -21,6 +21,7 @@ import torch  # noqa: F401  (must precede loading the library, see above)
 
 __all__ = [
     "LIB_PATH", "LoraError", "LoraMeta", "lib", "lora_prepare_metadata", "lora_shrink",
+    "lora_prepare_and_shrink",
     "lora_shrink_default_splits", "lora_expand", "lora_stream_copy", "lora_stream_update",
     "lora_status_string",
     "LORA_MAX_LORAS", "LORA_MAX_SLICES", "LORA_MAX_SPLITS", "SUPPORTED_RANKS",
@@ -83,6 +84,9 @@ def lib() -> ctypes.CDLL:
         L.lora_shrink.argtypes = [_VP, _I64, _I32, ctypes.POINTER(_VP), _I32, _I32, ctypes.c_float,
                                   _VP, _I32, MP, _I32, _I32, _VP]
         L.lora_shrink.restype = ctypes.c_int
+        L.lora_prepare_and_shrink.argtypes = [_VP, _I32, _VP, _I64, _I32, ctypes.POINTER(_VP), _I32,
+                                              _I32, ctypes.c_float, _VP, _I32, MP, _I32, _I32, _VP]
+        L.lora_prepare_and_shrink.restype = ctypes.c_int
         L.lora_expand.argtypes = [_VP, _I32, ctypes.POINTER(_VP), ctypes.POINTER(_I32), _I32, _I32,
                                   _VP, _I64, MP, _I32, _I32, _VP]
         L.lora_expand.restype = ctypes.c_int
@@ -167,11 +171,8 @@ def lora_shrink_default_splits(hidden: int, max_tokens: int, max_loras: int, num
     return int(lib().lora_shrink_default_splits(hidden, max_tokens, max_loras, num_slices, rank))
 
 
-def lora_shrink(x: torch.Tensor, lora_a: Sequence[torch.Tensor], scale: float, buf: torch.Tensor,
-                num_splits: int, meta: LoraMeta,
-                stream: Optional[torch.cuda.Stream] = None) -> None:
-    """x: bf16 [max_tokens, >=hidden] (row stride x.stride(0)); lora_a[s]: bf16
-    [max_loras, rank, hidden]; buf: fp32 [num_splits, S, max_tokens, rank]."""
+def _shrink_args(x: torch.Tensor, lora_a: Sequence[torch.Tensor], buf: torch.Tensor,
+                 num_splits: int, meta: LoraMeta):
     S = len(lora_a)
     _, rank, hidden = lora_a[0].shape
     if x.dim() != 2 or x.stride(1) != 1 or x.shape[0] < meta.max_tokens:
@@ -182,10 +183,35 @@ def lora_shrink(x: torch.Tensor, lora_a: Sequence[torch.Tensor], scale: float, b
         if tuple(a.shape) != (meta.max_loras, rank, hidden) or not a.is_contiguous():
             raise ValueError("lora_a[s] must be contiguous [max_loras, rank, hidden]")
     aptrs = (_VP * S)(*[_dev_ptr(a, torch.bfloat16, "lora_a") for a in lora_a])
+    return S, int(rank), int(hidden), aptrs
+
+
+def lora_shrink(x: torch.Tensor, lora_a: Sequence[torch.Tensor], scale: float, buf: torch.Tensor,
+                num_splits: int, meta: LoraMeta,
+                stream: Optional[torch.cuda.Stream] = None) -> None:
+    """x: bf16 [max_tokens, >=hidden] (row stride x.stride(0)); lora_a[s]: bf16
+    [max_loras, rank, hidden]; buf: fp32 [num_splits, S, max_tokens, rank]."""
+    S, rank, hidden, aptrs = _shrink_args(x, lora_a, buf, num_splits, meta)
     _check("lora_shrink", lib().lora_shrink(
-        _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), int(hidden), aptrs, S, int(rank),
+        _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), hidden, aptrs, S, rank,
         float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits), meta.struct_ref,
         meta.max_tokens, meta.max_loras, _stream_handle(stream)))
+
+
+def lora_prepare_and_shrink(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.Tensor,
+                            lora_a: Sequence[torch.Tensor], scale: float, buf: torch.Tensor,
+                            num_splits: int, meta: LoraMeta,
+                            stream: Optional[torch.cuda.Stream] = None) -> None:
+    """lora_prepare_metadata then lora_shrink on the same batch (one launch up to
+    512 token slots); arguments as for those two."""
+    ptr = _dev_ptr(token_lora_mapping, torch.int32, "token_lora_mapping") if num_tokens else 0
+    if num_tokens and token_lora_mapping.numel() < num_tokens:
+        raise ValueError("token_lora_mapping is shorter than num_tokens")
+    S, rank, hidden, aptrs = _shrink_args(x, lora_a, buf, num_splits, meta)
+    _check("lora_prepare_and_shrink", lib().lora_prepare_and_shrink(
+        ptr, int(num_tokens), _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), hidden, aptrs,
+        S, rank, float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits),
+        meta.struct_ref, meta.max_tokens, meta.max_loras, _stream_handle(stream)))
 
 
 def lora_expand(buf: torch.Tensor, num_splits: int, lora_b: Sequence[torch.Tensor], y: torch.Tensor,

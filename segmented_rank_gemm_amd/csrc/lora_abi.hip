@@ -24,6 +24,11 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int num_cus,
                               hipStream_t stream);
 hipError_t launch_stream_update(void* buf, int64_t bytes, int num_cus, hipStream_t stream);
+hipError_t launch_prep_shrink(const int32_t* mapping, int num_tokens, const uint16_t* x,
+                              int64_t ldx, int hidden, const uint16_t* const* lora_a,
+                              int num_slices, int rank, float scale, float* buf, int num_splits,
+                              const lora_meta_t& meta, int max_tokens, int max_loras,
+                              int num_cus, hipStream_t stream);
 int shrink_group_blocks(int nb_total);
 int shrink_tile_blocks(int max_tokens, int nb);
 }  // namespace lora
@@ -125,10 +130,11 @@ int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t m
   return static_cast<int32_t>(splits);
 }
 
-lora_status_t lora_shrink(const uint16_t* x, int64_t ldx, int32_t hidden,
+// Checks of lora_shrink's arguments (meta and sizes included).
+static lora_status_t shrink_args(const uint16_t* x, int64_t ldx, int32_t hidden,
                           const uint16_t* const* lora_a, int32_t num_slices, int32_t rank,
-                          float scale, float* buf, int32_t num_splits, const lora_meta_t* meta,
-                          int32_t max_tokens, int32_t max_loras, hipStream_t stream) {
+                          const float* buf, int32_t num_splits, const lora_meta_t* meta,
+                          int32_t max_tokens, int32_t max_loras) {
   if (!meta_ok(meta) || !sizes_ok(max_tokens, max_loras)) return LORA_ERR_INVALID_ARGUMENT;
   if (!x || !lora_a || !buf || !aligned16(x) || !aligned16(buf)) return LORA_ERR_INVALID_ARGUMENT;
   if (hidden < 8 || hidden > kMaxHidden || hidden % 8 != 0) return LORA_ERR_INVALID_ARGUMENT;
@@ -139,9 +145,37 @@ lora_status_t lora_shrink(const uint16_t* x, int64_t ldx, int32_t hidden,
   for (int32_t s = 0; s < num_slices; ++s)
     if (!lora_a[s] || !aligned16(lora_a[s])) return LORA_ERR_INVALID_ARGUMENT;
   if (!rank_supported(rank)) return LORA_ERR_UNSUPPORTED;
+  return LORA_OK;
+}
+
+lora_status_t lora_shrink(const uint16_t* x, int64_t ldx, int32_t hidden,
+                          const uint16_t* const* lora_a, int32_t num_slices, int32_t rank,
+                          float scale, float* buf, int32_t num_splits, const lora_meta_t* meta,
+                          int32_t max_tokens, int32_t max_loras, hipStream_t stream) {
+  const lora_status_t st = shrink_args(x, ldx, hidden, lora_a, num_slices, rank, buf, num_splits,
+                                       meta, max_tokens, max_loras);
+  if (st != LORA_OK) return st;
   return launch_status(lora::launch_shrink(x, ldx, hidden, lora_a, num_slices, rank, scale, buf,
                                            num_splits, *meta, max_tokens, max_loras,
                                            current_cus(), stream));
+}
+
+lora_status_t lora_prepare_and_shrink(const int32_t* token_lora_mapping, int32_t num_tokens,
+                                      const uint16_t* x, int64_t ldx, int32_t hidden,
+                                      const uint16_t* const* lora_a, int32_t num_slices,
+                                      int32_t rank, float scale, float* buf, int32_t num_splits,
+                                      const lora_meta_t* meta, int32_t max_tokens,
+                                      int32_t max_loras, hipStream_t stream) {
+  if (!meta_ok(meta) || !sizes_ok(max_tokens, max_loras)) return LORA_ERR_INVALID_ARGUMENT;
+  if (num_tokens < 0 || num_tokens > max_tokens) return LORA_ERR_INVALID_ARGUMENT;
+  if (num_tokens > 0 && !token_lora_mapping) return LORA_ERR_INVALID_ARGUMENT;
+  const lora_status_t st = shrink_args(x, ldx, hidden, lora_a, num_slices, rank, buf, num_splits,
+                                       meta, max_tokens, max_loras);
+  if (st != LORA_OK) return st;
+  return launch_status(lora::launch_prep_shrink(token_lora_mapping, num_tokens, x, ldx, hidden,
+                                                lora_a, num_slices, rank, scale, buf, num_splits,
+                                                *meta, max_tokens, max_loras, current_cus(),
+                                                stream));
 }
 
 lora_status_t lora_expand(const float* buf, int32_t num_splits, const uint16_t* const* lora_b,

@@ -23,6 +23,7 @@
 // the size arguments; workgroups stride over the units of the actual batch.
 
 #include "device_common.hpp"
+#include "metadata_group.hpp"
 
 #ifdef LORA_TUNING
 #include <cstdlib>
@@ -58,15 +59,39 @@ struct ShrinkParams {
   int max_tiles;             // tiles the padded order may use
   int max_tokens;
   int max_loras;
+  // fused prepare + shrink only: the map, the batch size, the metadata outputs
+  // (written by the workgroups past shrink_grid), the shrink's own grid
+  const int32_t* mapping;
+  int num_tokens;
+  int shrink_grid;
+  MetaOut meta_out;
 };
 
 // NB = number of 16-output blocks covering num_slices * rank outputs;
 // MW = 16-token blocks per tile, all held by every wave so that each A operand
 // fetched feeds MW matrix-core ops.
-template <int NB, int MW>
+//
+// SELF: the fused prepare + shrink launch for batches of at most 512 token
+// slots.  The workgroups past shrink_grid compute the metadata (one group
+// each, the metadata kernel's code); the others do not wait for it: wave 0
+// reads the whole map once (8 ids per lane), counts the adapters in LDS and
+// places each adapter's run of the padded grouped order (start round_up(S_k +
+// 15 k, 16), as the metadata step does), and per unit finds the adapter whose
+// run covers the unit's tile and that adapter's members of the tile by their
+// rank in token order.  So the shrink learns its tile from the map in the
+// round trip that would otherwise fetch it from the metadata, and the two
+// steps share one launch.
+template <int NB, int MW, bool SELF = false>
 __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) {
   static_assert(MW == 1, "a tile of the padded grouped order holds 16 tokens");
   constexpr int kTile = 16 * MW;
+  if constexpr (SELF) {
+    if (static_cast<int>(blockIdx.x) >= p.shrink_grid) {  // workgroup-uniform
+      metadata_group<kShrinkThreads>(p.mapping, p.num_tokens, p.max_loras, p.meta_out,
+                                     static_cast<int>(blockIdx.x) - p.shrink_grid);
+      return;
+    }
+  }
   __shared__ f32x4 red[kShrinkWaves][NB][kWave];
   __shared__ const uint16_t* slice_a[LORA_MAX_SLICES];  // per-lane slice lookup without
                                                         // indexing the argument block
@@ -86,18 +111,100 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
   const int grp = lane >> 4;  // lane group: K sub-range, and output rows 4*grp..4*grp+3
   const int nout = p.num_slices * p.rank;
 
-  for (XcdWalk walk = xcd_walk(units, gridDim.x); walk.next < walk.end; walk.next += walk.step) {
+  // SELF: the batch's adapter counts, the start of each adapter's run of the
+  // padded order (-1: absent), and the current unit's tile (token ids, then
+  // its adapter, then the tile count).
+  constexpr int kGroups = SELF ? LORA_MAX_LORAS + 1 : 1;
+  __shared__ int g_count[kGroups];
+  __shared__ int g_start[kGroups];
+  __shared__ int g_tile[SELF ? kTile + 2 : 1];
+  const int groups = p.max_loras + 1;
+  int mgrp[kPerThread];  // wave 0: groups of tokens 8 * lane + e (-1 past the batch)
+  if constexpr (SELF) {
+    for (int i = threadIdx.x; i < groups; i += kShrinkThreads) g_count[i] = 0;
+    __syncthreads();
+    if (wave == 0) {
+      load_groups(p.mapping, p.num_tokens, p.max_loras, lane * kPerThread, mgrp);
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e)
+        if (mgrp[e] > 0) atomicAdd(&g_count[mgrp[e]], 1);  // exact counts, any order
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int carry_s = 0, carry_k = 0, end = 0;
+      for (int base = 1; base < groups; base += kWave) {
+        const int i = base + lane;
+        const int c = i < groups ? g_count[i] : 0;
+        const unsigned long long present = __ballot(c > 0);
+        const int incl = wave_inclusive_scan(c);
+        const int k = carry_k + __popcll(present & ((1ull << lane) - 1ull));
+        const int start = round_up_tile(carry_s + incl - c + (kTile - 1) * k);
+        if (i < groups) g_start[i] = c > 0 ? start : -1;
+        if (c > 0) end = max(end, round_up_tile(start + c));
+        carry_s += __shfl(incl, kWave - 1, kWave);
+        carry_k += __popcll(present);
+      }
+      end = wave_max(end);
+      if (lane == 0) g_tile[kTile + 1] = end / kTile;
+    }
+  }
+
+  for (XcdWalk walk = xcd_walk(units, SELF ? p.shrink_grid : static_cast<int>(gridDim.x));
+       walk.next < walk.end; walk.next += walk.step) {
     const int u = walk.next;
     const int pg = u / num_tiles;  // (part, output group), group fastest
     const int m = u - pg * num_tiles;
     const int part = pg / p.num_groups;
     const int o0 = (pg - part * p.num_groups) * 16 * NB;  // first output of the group
-    const int tiles_used = *p.num_tiles;
-    const int tile_lora = p.tile_lora[m];
-    const int tile_id = p.tile_ids[kTile * m + col];  // this lane's token column
-    // (the three loads go out together: the compiler would otherwise sink the
-    // tile's two below the test, a second round trip)
-    asm volatile("" : : "v"(tile_id), "v"(tile_lora), "v"(tiles_used));
+    int tiles_used, tile_lora, tile_id;
+    if constexpr (SELF) {
+      __syncthreads();  // every wave has read the previous unit's tile
+      if (wave == 0) {
+        // the adapter group whose run covers tile m (runs start on tile
+        // boundaries, so the tile overlaps run i iff start_i <= 16 m < start_i + count_i)
+        int hit = -1, hit_start = 0;
+        for (int base = 1; base < groups; base += kWave) {
+          const int i = base + lane;
+          const int st = i < groups ? g_start[i] : -1;
+          const int c = i < groups ? g_count[i] : 0;
+          const unsigned long long b = __ballot(st >= 0 && kTile * m >= st && kTile * m < st + c);
+          if (b) {
+            const int src = __ffsll(static_cast<long long>(b)) - 1;
+            hit = __shfl(i, src, kWave);
+            hit_start = __shfl(st, src, kWave);
+            break;
+          }
+        }
+        if (lane < kTile) g_tile[lane] = -1;
+        if (hit > 0) {
+          // its members of rank j0 .. j0 + 15 in token order
+          const int j0 = kTile * m - hit_start;
+          int mine = 0;
+#pragma unroll
+          for (int e = 0; e < kPerThread; ++e) mine += mgrp[e] == hit ? 1 : 0;
+          int r = wave_inclusive_scan(mine) - mine;
+#pragma unroll
+          for (int e = 0; e < kPerThread; ++e) {
+            if (mgrp[e] == hit) {
+              if (r >= j0 && r < j0 + kTile) g_tile[r - j0] = lane * kPerThread + e;
+              ++r;
+            }
+          }
+        }
+        if (lane == 0) g_tile[kTile] = hit > 0 ? hit - 1 : -1;  // the adapter, -1 for none
+      }
+      __syncthreads();
+      tiles_used = g_tile[kTile + 1];
+      tile_lora = g_tile[kTile];
+      tile_id = g_tile[col];
+    } else {
+      tiles_used = *p.num_tiles;
+      tile_lora = p.tile_lora[m];
+      tile_id = p.tile_ids[kTile * m + col];  // this lane's token column
+      // (the three loads go out together: the compiler would otherwise sink the
+      // tile's two below the test, a second round trip)
+      asm volatile("" : : "v"(tile_id), "v"(tile_lora), "v"(tiles_used));
+    }
     if (m >= tiles_used) continue;  // wave-uniform
     Tile tile;
     tile.lora = tile_lora >= 0 && tile_lora < p.max_loras ? tile_lora : 0;
@@ -447,6 +554,17 @@ hipError_t launch_shrink_nb(const ShrinkParams& p, int grid, hipStream_t stream)
   return hipGetLastError();
 }
 
+// Fused prepare + shrink: the shrink's grid (as resident as the kernel allows),
+// then one workgroup per metadata group.
+template <int NB>
+hipError_t launch_prep_shrink_nb(ShrinkParams p, int grid, hipStream_t stream) {
+  grid = resident_grid(shrink_kernel<NB, 1, true>, kShrinkThreads, grid);
+  p.shrink_grid = grid;
+  const int total = grid + p.max_loras + 1;
+  hipLaunchKernelGGL((shrink_kernel<NB, 1, true>), dim3(total), dim3(kShrinkThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int MW>
 hipError_t launch_shrink_mw(const ShrinkParams& p, int nb, int grid, hipStream_t stream) {
   switch (nb) {
@@ -486,10 +604,10 @@ int shrink_grid(int max_tiles, int num_splits, int num_groups, int num_cus) {
   return static_cast<int>((g + kXcds - 1) / kXcds * kXcds);  // whole rounds over the XCDs
 }
 
-hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint16_t* const* lora_a,
-                         int num_slices, int rank, float scale, float* buf, int num_splits,
-                         const lora_meta_t& meta, int max_tokens, int max_loras, int num_cus,
-                         hipStream_t stream) {
+static ShrinkParams shrink_params(const uint16_t* x, int64_t ldx, int hidden,
+                                  const uint16_t* const* lora_a, int num_slices, int rank,
+                                  float scale, float* buf, int num_splits, const lora_meta_t& meta,
+                                  int max_tokens, int max_loras) {
   ShrinkParams p{};
   p.x = x;
   p.ldx = ldx;
@@ -516,6 +634,20 @@ hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint1
   const int nb_total = (num_slices * rank + 15) / 16;
   const int nb = shrink_group_blocks(nb_total);
   p.num_groups = (nb_total + nb - 1) / nb;
+  return p;
+}
+
+static int shrink_nb(int num_slices, int rank) {
+  return shrink_group_blocks((num_slices * rank + 15) / 16);
+}
+
+hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint16_t* const* lora_a,
+                         int num_slices, int rank, float scale, float* buf, int num_splits,
+                         const lora_meta_t& meta, int max_tokens, int max_loras, int num_cus,
+                         hipStream_t stream) {
+  const ShrinkParams p = shrink_params(x, ldx, hidden, lora_a, num_slices, rank, scale, buf,
+                                       num_splits, meta, max_tokens, max_loras);
+  const int nb = shrink_nb(num_slices, rank);
   const int mw = shrink_tile_blocks(max_tokens, nb);
   if (mw == 4) {
     // large batch: LDS-staged kernel, 64-token tiles, at most 3 workgroups per
@@ -537,6 +669,43 @@ hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint1
   }
   const int grid = shrink_grid(p.max_tiles, num_splits, p.num_groups, num_cus);
   return launch_shrink_mw<1>(p, nb, grid, stream);
+}
+
+hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_tokens, int max_loras,
+                           const lora_meta_t& meta, hipStream_t stream);
+
+// Metadata and shrink of one batch.  Up to 512 token slots (the register
+// kernel's sizes, one wave holding the whole map): one fused launch.  Larger
+// batches: the metadata kernel, then the shrink.
+hipError_t launch_prep_shrink(const int32_t* mapping, int num_tokens, const uint16_t* x,
+                              int64_t ldx, int hidden, const uint16_t* const* lora_a,
+                              int num_slices, int rank, float scale, float* buf, int num_splits,
+                              const lora_meta_t& meta, int max_tokens, int max_loras,
+                              int num_cus, hipStream_t stream) {
+  const int nb = shrink_nb(num_slices, rank);
+  if (shrink_tile_blocks(max_tokens, nb) != 1 || max_tokens > kWave * kPerThread) {
+    const hipError_t e = launch_metadata(mapping, num_tokens, max_tokens, max_loras, meta, stream);
+    if (e != hipSuccess) return e;
+    return launch_shrink(x, ldx, hidden, lora_a, num_slices, rank, scale, buf, num_splits, meta,
+                         max_tokens, max_loras, num_cus, stream);
+  }
+  ShrinkParams p = shrink_params(x, ldx, hidden, lora_a, num_slices, rank, scale, buf, num_splits,
+                                 meta, max_tokens, max_loras);
+  p.mapping = mapping;
+  p.num_tokens = num_tokens;
+  p.meta_out = MetaOut{meta.sorted_token_ids, meta.active_lora_ids, meta.num_tokens_per_lora,
+                       meta.lora_token_start, meta.num_active, meta.tile_token_ids,
+                       meta.tile_lora, meta.num_tiles, meta.num_runs};
+  const int grid = shrink_grid(p.max_tiles, num_splits, p.num_groups, num_cus);
+  switch (nb) {
+    case 1: return launch_prep_shrink_nb<1>(p, grid, stream);
+    case 2: return launch_prep_shrink_nb<2>(p, grid, stream);
+    case 3: return launch_prep_shrink_nb<3>(p, grid, stream);
+    case 4: return launch_prep_shrink_nb<4>(p, grid, stream);
+    case 5:
+    case 6: return launch_prep_shrink_nb<6>(p, grid, stream);
+    default: return launch_prep_shrink_nb<8>(p, grid, stream);
+  }
 }
 
 }  // namespace lora

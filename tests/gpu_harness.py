@@ -68,6 +68,14 @@ def run_step(d: DeviceWorkload, stream=None) -> None:
     srg.lora_expand(d.buf, d.num_splits, d.lora_b, d.y, d.meta, stream)
 
 
+def run_step_fused(d: DeviceWorkload, stream=None) -> None:
+    """The same step through lora_prepare_and_shrink (metadata and shrink in one
+    call) and lora_expand."""
+    srg.lora_prepare_and_shrink(d.mapping, d.w.num_tokens, d.x, d.lora_a, float(d.w.scale), d.buf,
+                                d.num_splits, d.meta, stream)
+    srg.lora_expand(d.buf, d.num_splits, d.lora_b, d.y, d.meta, stream)
+
+
 META_KEYS = ["sorted_token_ids", "active_lora_ids", "num_tokens_per_lora", "lora_token_start",
              "num_active", "tile_token_ids", "tile_lora", "num_tiles", "num_runs"]
 

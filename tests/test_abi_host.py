@@ -25,6 +25,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["lora_prepare_metadata", "lora_shrink", "lora_expand", "lora_status_string",
+              "lora_prepare_and_shrink",
               "lora_shrink_default_splits", "lora_stream_copy", "lora_stream_update"]:
         assert n in names
 
@@ -93,6 +94,27 @@ def _shrink(**kw):
 ])
 def test_shrink_rejects(kw, status):
     assert _shrink(**kw) == status
+
+
+def _prep_shrink(mapping=FAKE, T=4, maxT=256, meta=None, **kw):
+    a = dict(SHRINK_OK)
+    a.update(kw)
+    a["maxT"] = maxT
+    aptr = a["a"] if not isinstance(a["a"], int) else _ptrs(a["a"])
+    return srg.lib().lora_prepare_and_shrink(mapping, T, a["x"], a["ldx"], a["hidden"], aptr,
+                                             a["S"], a["rank"], a["scale"], a["buf"],
+                                             a["splits"], _meta(**(meta or {})), a["maxT"],
+                                             a["L"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), 1), (dict(T=257), 1), (dict(mapping=None), 1), (dict(maxT=0, T=0), 1),
+    (dict(meta=dict(num_runs=None)), 1), (dict(meta=dict(tile_lora=None)), 1), (dict(L=0), 1),
+    (dict(L=257), 1), (dict(x=None), 1), (dict(buf=FAKE + 4), 1), (dict(hidden=4092), 1),
+    (dict(splits=0), 1), (dict(S=5), 1), (dict(a=_ptrs(3, None)), 1), (dict(rank=12), 2),
+])
+def test_prepare_and_shrink_rejects(kw, status):
+    assert _prep_shrink(**kw) == status
 
 
 EXPAND_OK = dict(buf=FAKE, splits=4, b=3, sizes=(4096, 4096, 4096), S=3, rank=8, y=FAKE,

@@ -386,3 +386,85 @@ def test_tuned_splits_give_parity():
     H.run_step(d2)
     torch.cuda.synchronize()
     _full_check(w, d2)
+
+
+# ------------------------------------------------ fused prepare + shrink ----
+
+PREP_CASES = [  # T, maxT, hidden, slices, rank, L, kind, splits
+    (0, 16, 256, [256], 8, 2, "wild", 1),
+    (1, 1, 256, [256], 8, 1, "single", 1),
+    (16, 16, 256, [256], 8, 2, "wild", 2),
+    (100, 128, 512, [96, 32], 16, 8, "wild", 3),
+    (200, 256, 1024, [256, 256], 8, 4, "all_none", 2),
+    (300, 300, 1024, [512, 256], 32, 64, "runs", 5),
+    (511, 512, 256, [256, 256, 256, 256], 8, 3, "extreme", 1),
+    (512, 512, 2048, [1024], 64, 256, "wild", 16),
+    (512, 512, 1024, [256, 256, 256, 256], 64, 16, "runs", 4),  # 16 output blocks: 2 groups
+    (700, 720, 1024, [512, 512], 16, 4, "wild", 3),             # larger: two launches
+]
+
+
+@pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,kind,splits", PREP_CASES)
+def test_prepare_and_shrink_matches_two_calls(T, maxT, hidden, slices, rank, L, kind, splits):
+    """Metadata and parts from the fused call equal those of lora_prepare_metadata
+    + lora_shrink bit for bit (buf compared as raw words, its NaN fill included)."""
+    rng = np.random.default_rng(T * 31 + L)
+    mapping = make_fuzz_mapping(rng, T, L, kind)
+    w = make_custom_workload(T + 5, T, hidden, slices, rank, L, 1.5, mapping, max_tokens=maxT)
+    d1 = H.upload(w, num_splits=splits)
+    d2 = H.upload(w, num_splits=splits)
+    srg.lora_prepare_metadata(d1.mapping, T, d1.meta)
+    srg.lora_shrink(d1.x, d1.lora_a, float(w.scale), d1.buf, splits, d1.meta)
+    srg.lora_prepare_and_shrink(d2.mapping, T, d2.x, d2.lora_a, float(w.scale), d2.buf, splits,
+                                d2.meta)
+    torch.cuda.synchronize()
+    m1, m2 = H.meta_host(d1), H.meta_host(d2)
+    _check_meta(m2, oracle.prepare_metadata(mapping, L), T, maxT, mapping=mapping, L=L)
+    nt = int(m1["num_tiles"][0])
+    assert np.array_equal(m1["sorted_token_ids"], m2["sorted_token_ids"])
+    for k in ["active_lora_ids", "num_tokens_per_lora", "lora_token_start", "num_active",
+              "num_tiles", "num_runs"]:
+        assert np.array_equal(m1[k], m2[k]), k
+    assert np.array_equal(m1["tile_token_ids"][:16 * nt], m2["tile_token_ids"][:16 * nt])
+    assert np.array_equal(m1["tile_lora"][:nt], m2["tile_lora"][:nt])
+    assert np.array_equal(d1.buf.view(torch.int32).cpu().numpy(),
+                          d2.buf.view(torch.int32).cpu().numpy())
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_fused_step_parity_full_size(cfg):
+    # the launch configuration the benchmark times for the decode step
+    w = make_workload(cfg)
+    d = H.upload(w)
+    H.run_step_fused(d)
+    torch.cuda.synchronize()
+    _full_check(w, d, literal=True)
+
+
+def test_fused_graph_replays_new_batches():
+    T, hidden, slices, rank, L = 256, 1024, [512, 256, 256], 8, 6
+    rng = np.random.default_rng(99)
+    kinds = [rng.integers(-1, L, size=T), np.full(T, L - 1), np.full(T, -1),
+             np.sort(rng.integers(0, 2, size=T)), rng.integers(-3, L + 3, size=T)]
+    batches = [make_custom_workload(T + i, T, hidden, slices, rank, L, 0.75, m)
+               for i, m in enumerate(kinds)]
+    d = H.upload(batches[0])
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        H.run_step_fused(d, stream=torch.cuda.current_stream())
+    for w in batches:
+        fresh = H.upload(w, num_splits=d.num_splits)
+        d.w = w
+        d.mapping.copy_(fresh.mapping)
+        d.x.copy_(fresh.x)
+        d.y.copy_(fresh.y)
+        for dst, src in zip(d.lora_a + d.lora_b, fresh.lora_a + fresh.lora_b):
+            dst.copy_(src)
+        d.buf.fill_(float("nan"))
+        d.meta.sorted_token_ids.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _full_check(w, d)
