@@ -1,7 +1,9 @@
 """Throughput of the multi-LoRA metadata + shrink + expand step on one MI355X.
 
 A step is one pass of the whole path (grouping metadata, shrink, expand) over
-one synthetic batch.  Inputs are resident in HBM before timing starts.  To keep
+one synthetic batch, as two calls: lora_prepare_and_shrink (metadata and shrink,
+one launch up to 512 token slots) and lora_expand; the same step as three calls
+is reported next to it.  Inputs are resident in HBM before timing starts.  To keep
 the 256 MB Infinity Cache from serving repeats, R copies of every buffer (at
 least 1 GiB in total) are rotated: one HIP graph holds R consecutive steps, each
 on its own copy.  Per-kernel launch durations for the roofline figure are
@@ -147,6 +149,13 @@ class Sets:
         srg.lora_shrink(s["x"], s["a"], float(self.w.scale), s["buf"], self.num_splits, s["meta"],
                         stream)
 
+    def prep_shrink(self, r, stream=None):
+        """Metadata and shrink of copy r in one call (lora_prepare_and_shrink)."""
+        import segmented_rank_gemm_amd as srg
+        s = self.sets[r]
+        srg.lora_prepare_and_shrink(s["mapping"], self.T, s["x"], s["a"], float(self.w.scale),
+                                    s["buf"], self.num_splits, s["meta"], stream)
+
     def expand(self, r, stream=None):
         import segmented_rank_gemm_amd as srg
         s = self.sets[r]
@@ -161,6 +170,12 @@ class Sets:
         srg.lora_expand(s["buf"], self.num_splits, s["b"], s["y"], m, stream)
 
     def step(self, r, stream=None):
+        """The whole path: metadata + shrink (one call) and expand."""
+        self.prep_shrink(r, stream)
+        self.expand(r, stream)
+
+    def step3(self, r, stream=None):
+        """The whole path as three calls: metadata, shrink, expand."""
         self.metadata(r, stream)
         self.shrink(r, stream)
         self.expand(r, stream)
@@ -316,17 +331,22 @@ def run_config(idx, args):
     kb = kernel_set_bytes(w, splits)
     # (the metadata kernel reads a few KB per copy: it is timed over the step's copies)
     # (--rotate fixes the copies for every kernel, e.g. for short counter runs)
-    rot = {k: (R if k == "metadata" or args.rotate else rotation(kb[k], sb, R)) for k in kb}
+    kb["prepare_and_shrink"] = kb["shrink"] + kb["metadata"]
+    kb["step3"] = sb
+    rot = {k: (R if k in ("metadata", "step3") or args.rotate else rotation(kb[k], sb, R))
+           for k in kb}
     sets.grow(max(rot.values()))
     per = {}
     fns = {"metadata": sets.metadata, "shrink": sets.shrink, "expand": sets.expand,
-           "pair": lambda r, s: (sets.shrink(r, s), sets.expand(r, s))}
-    for name in ("metadata", "shrink", "expand", "pair"):
+           "prepare_and_shrink": sets.prep_shrink,
+           "pair": lambda r, s: (sets.shrink(r, s), sets.expand(r, s)), "step3": sets.step3}
+    for name in ("metadata", "shrink", "prepare_and_shrink", "expand", "pair", "step3"):
         n = rot[name]
         g = capture([lambda s, r=r, f=fns[name]: f(r, s) for r in range(n)])
         per[name] = time_graph(g, reps) / n
         del g
     pair_s = per.pop("pair")
+    step3_s = per.pop("step3")
 
     # layer stack: one metadata step serves a model's L LoRA layers of this
     # shape, each with its own weights, activations and outputs.  Stacks are
@@ -341,8 +361,9 @@ def run_config(idx, args):
         calls = []
         for k in range(K):
             m = k * L
-            calls.append(lambda s, m=m: sets.metadata(m, s))
-            calls += [lambda s, r=m + l, m=m: sets.layer(r, m, s) for l in range(L)]
+            # the first layer groups the batch in its shrink call; the others reuse it
+            calls.append(lambda s, m=m: (sets.prep_shrink(m, s), sets.expand(m, s)))
+            calls += [lambda s, r=m + l, m=m: sets.layer(r, m, s) for l in range(1, L)]
         g = capture(calls)
         t_stack = time_graph(g, max(2, reps // 10)) / K
         del g
@@ -397,12 +418,17 @@ def run_config(idx, args):
             "frac_of_update_ceiling": achieved / (2 * cb / upd_s / 1e9),
         },
         "step": {
+            "calls": "lora_prepare_and_shrink + lora_expand",
             "gpu_event_ms_per_step": gpu_s / steps * 1e3,
             "algorithmic_bytes": st["total_bytes"],
             "achieved_GBs": st["total_bytes"] / step_s / 1e9,
             "frac_of_peak": st["total_bytes"] / step_s / 1e9 / HBM_PEAK_GBS,
         },
         "kernels_us": {k: v * 1e6 for k, v in per.items()},
+        "step_three_calls": {
+            "calls": "lora_prepare_metadata + lora_shrink + lora_expand",
+            "us": step3_s * 1e6, "tokens_per_s": w.num_tokens / step3_s,
+        },
         "shrink_expand_pair": {
             "us": pair_s * 1e6,
             "tokens_per_s": w.num_tokens / pair_s,

@@ -214,10 +214,10 @@ lora_status_t lora_shrink(const uint16_t *x, int64_t ldx, int32_t hidden,
  * checks.  Writes exactly what the two calls write, bit for bit (meta in
  * full, buf rows of tokens with an adapter).
  *
- * With max_tokens <= 512 one kernel is enqueued: its first workgroups do the
- * shrink, finding each tile's tokens from the map themselves, and the last
- * max_loras + 1 workgroups compute the metadata.  Larger batches enqueue the
- * metadata kernel and the shrink one after the other.  The grid still depends
+ * With max_tokens <= 512 and max_loras <= 16 one kernel is enqueued: its
+ * first workgroups do the shrink, finding each tile's tokens from the map
+ * themselves, and the last max_loras + 1 workgroups compute the metadata.
+ * Other sizes enqueue the metadata kernel and the shrink one after the other.  The grid still depends
  * only on the sizes, so the call can be captured in a graph.
  */
 lora_status_t lora_prepare_and_shrink(const int32_t *token_lora_mapping, int32_t num_tokens,

@@ -72,13 +72,13 @@ struct ShrinkParams {
 // fetched feeds MW matrix-core ops.
 //
 // SELF: the fused prepare + shrink launch for batches of at most 512 token
-// slots.  The workgroups past shrink_grid compute the metadata (one group
-// each, the metadata kernel's code); the others do not wait for it: wave 0
-// reads the whole map once (8 ids per lane), counts the adapters in LDS and
-// places each adapter's run of the padded grouped order (start round_up(S_k +
-// 15 k, 16), as the metadata step does), and per unit finds the adapter whose
-// run covers the unit's tile and that adapter's members of the tile by their
-// rank in token order.  So the shrink learns its tile from the map in the
+// slots and 16 adapter slots.  The workgroups past shrink_grid compute the
+// metadata (one group each, the metadata kernel's code); the others do not
+// wait for it: wave 0 reads the whole map once (8 ids per lane), counts each
+// adapter's tokens with ballots and places its run of the padded grouped order
+// (start round_up(S_k + 15 k, 16), as the metadata step does), and per unit
+// finds the adapter whose run covers the unit's tile and that adapter's
+// members of the tile by their rank in token order.  So the shrink learns its tile from the map in the
 // round trip that would otherwise fetch it from the metadata, and the two
 // steps share one launch.
 template <int NB, int MW, bool SELF = false>
@@ -111,42 +111,34 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
   const int grp = lane >> 4;  // lane group: K sub-range, and output rows 4*grp..4*grp+3
   const int nout = p.num_slices * p.rank;
 
-  // SELF: the batch's adapter counts, the start of each adapter's run of the
-  // padded order (-1: absent), and the current unit's tile (token ids, then
-  // its adapter, then the tile count).
-  constexpr int kGroups = SELF ? LORA_MAX_LORAS + 1 : 1;
-  __shared__ int g_count[kGroups];
-  __shared__ int g_start[kGroups];
-  __shared__ int g_tile[SELF ? kTile + 2 : 1];
+  // SELF: every wave reads the whole map (8 tokens per lane, at most 2 KB) and
+  // keeps, lane-indexed (lane g for group g <= max_loras < 64), each adapter's
+  // count and the start of its run of the padded order (-1: absent); per unit
+  // it finds its tile's token ids itself and passes them between its lanes
+  // through its own LDS slice, so no wave waits for another.  Ballots, lane
+  // reads and scalar loops only: a chain of cross-lane shuffles costs ~0.1 us a
+  // step here.
+  __shared__ int w_tile[SELF ? kShrinkWaves : 1][kTile];
   const int groups = p.max_loras + 1;
-  int mgrp[kPerThread];  // wave 0: groups of tokens 8 * lane + e (-1 past the batch)
+  int mgrp[kPerThread];
+  int vcount = 0, vstart = -1, tiles_self = 0;
   if constexpr (SELF) {
-    for (int i = threadIdx.x; i < groups; i += kShrinkThreads) g_count[i] = 0;
-    __syncthreads();
-    if (wave == 0) {
-      load_groups(p.mapping, p.num_tokens, p.max_loras, lane * kPerThread, mgrp);
+    load_groups(p.mapping, p.num_tokens, p.max_loras, lane * kPerThread, mgrp);
+    int below = 0, present = 0, end = 0;  // tokens and adapters before group g
+    for (int gi = 1; gi < groups; ++gi) {
+      int c = 0;
 #pragma unroll
-      for (int e = 0; e < kPerThread; ++e)
-        if (mgrp[e] > 0) atomicAdd(&g_count[mgrp[e]], 1);  // exact counts, any order
-    }
-    __syncthreads();
-    if (wave == 0) {
-      int carry_s = 0, carry_k = 0, end = 0;
-      for (int base = 1; base < groups; base += kWave) {
-        const int i = base + lane;
-        const int c = i < groups ? g_count[i] : 0;
-        const unsigned long long present = __ballot(c > 0);
-        const int incl = wave_inclusive_scan(c);
-        const int k = carry_k + __popcll(present & ((1ull << lane) - 1ull));
-        const int start = round_up_tile(carry_s + incl - c + (kTile - 1) * k);
-        if (i < groups) g_start[i] = c > 0 ? start : -1;
-        if (c > 0) end = max(end, round_up_tile(start + c));
-        carry_s += __shfl(incl, kWave - 1, kWave);
-        carry_k += __popcll(present);
+      for (int e = 0; e < kPerThread; ++e) c += __popcll(__ballot(mgrp[e] == gi));
+      const int start = round_up_tile(below + (kTile - 1) * present);
+      vcount = lane == gi ? c : vcount;
+      vstart = lane == gi ? (c > 0 ? start : -1) : vstart;
+      if (c > 0) {
+        end = round_up_tile(start + c);
+        below += c;
+        ++present;
       }
-      end = wave_max(end);
-      if (lane == 0) g_tile[kTile + 1] = end / kTile;
     }
+    tiles_self = end / kTile;
   }
 
   for (XcdWalk walk = xcd_walk(units, SELF ? p.shrink_grid : static_cast<int>(gridDim.x));
@@ -158,45 +150,45 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
     const int o0 = (pg - part * p.num_groups) * 16 * NB;  // first output of the group
     int tiles_used, tile_lora, tile_id;
     if constexpr (SELF) {
-      __syncthreads();  // every wave has read the previous unit's tile
-      if (wave == 0) {
-        // the adapter group whose run covers tile m (runs start on tile
-        // boundaries, so the tile overlaps run i iff start_i <= 16 m < start_i + count_i)
-        int hit = -1, hit_start = 0;
-        for (int base = 1; base < groups; base += kWave) {
-          const int i = base + lane;
-          const int st = i < groups ? g_start[i] : -1;
-          const int c = i < groups ? g_count[i] : 0;
-          const unsigned long long b = __ballot(st >= 0 && kTile * m >= st && kTile * m < st + c);
-          if (b) {
-            const int src = __ffsll(static_cast<long long>(b)) - 1;
-            hit = __shfl(i, src, kWave);
-            hit_start = __shfl(st, src, kWave);
-            break;
-          }
+      // the adapter group whose run covers tile m (runs start on tile
+      // boundaries, so the tile overlaps run g iff start_g <= 16 m < start_g + count_g)
+      int hit = -1, hit_start = 0;
+      for (int gi = 1; gi < groups; ++gi) {
+        const int st = __builtin_amdgcn_readlane(vstart, gi);
+        const int c = __builtin_amdgcn_readlane(vcount, gi);
+        if (st >= 0 && kTile * m >= st && kTile * m < st + c) {
+          hit = gi;
+          hit_start = st;
         }
-        if (lane < kTile) g_tile[lane] = -1;
-        if (hit > 0) {
-          // its members of rank j0 .. j0 + 15 in token order
-          const int j0 = kTile * m - hit_start;
-          int mine = 0;
-#pragma unroll
-          for (int e = 0; e < kPerThread; ++e) mine += mgrp[e] == hit ? 1 : 0;
-          int r = wave_inclusive_scan(mine) - mine;
-#pragma unroll
-          for (int e = 0; e < kPerThread; ++e) {
-            if (mgrp[e] == hit) {
-              if (r >= j0 && r < j0 + kTile) g_tile[r - j0] = lane * kPerThread + e;
-              ++r;
-            }
-          }
-        }
-        if (lane == 0) g_tile[kTile] = hit > 0 ? hit - 1 : -1;  // the adapter, -1 for none
       }
-      __syncthreads();
-      tiles_used = g_tile[kTile + 1];
-      tile_lora = g_tile[kTile];
-      tile_id = g_tile[col];
+      int* slot = w_tile[wave];
+      if (lane < kTile) slot[lane] = -1;
+      if (hit > 0) {
+        // its members of rank j0 .. j0 + 15 in token order: a token's rank is
+        // the number of the group's tokens in lower lanes (ballots) plus those
+        // before it in its own lane
+        const int j0 = kTile * m - hit_start;
+        const unsigned long long lower = (1ull << lane) - 1ull;
+        int r = 0;
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) r += __popcll(__ballot(mgrp[e] == hit) & lower);
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) {
+          if (mgrp[e] == hit) {
+            if (r >= j0 && r < j0 + kTile) slot[r - j0] = lane * kPerThread + e;
+            ++r;
+          }
+        }
+      }
+      // (one wave's own LDS slice, written and read in program order: LDS
+      // operations of a wave complete in order; the fence keeps the compiler
+      // from moving the read above the other lanes' writes)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      tiles_used = tiles_self;
+      tile_lora = hit > 0 ? hit - 1 : -1;
+      tile_id = slot[col];
     } else {
       tiles_used = *p.num_tiles;
       tile_lora = p.tile_lora[m];
@@ -675,15 +667,19 @@ hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_token
                            const lora_meta_t& meta, hipStream_t stream);
 
 // Metadata and shrink of one batch.  Up to 512 token slots (the register
-// kernel's sizes, one wave holding the whole map): one fused launch.  Larger
-// batches: the metadata kernel, then the shrink.
+// kernel's sizes, one wave holding the whole map) and 16 adapter slots (the
+// shrink workgroups loop over the groups): one fused launch.  Otherwise the
+// metadata kernel, then the shrink.
+constexpr int kMaxFusedLoras = 16;
+
 hipError_t launch_prep_shrink(const int32_t* mapping, int num_tokens, const uint16_t* x,
                               int64_t ldx, int hidden, const uint16_t* const* lora_a,
                               int num_slices, int rank, float scale, float* buf, int num_splits,
                               const lora_meta_t& meta, int max_tokens, int max_loras,
                               int num_cus, hipStream_t stream) {
   const int nb = shrink_nb(num_slices, rank);
-  if (shrink_tile_blocks(max_tokens, nb) != 1 || max_tokens > kWave * kPerThread) {
+  if (shrink_tile_blocks(max_tokens, nb) != 1 || max_tokens > kWave * kPerThread ||
+      max_loras > kMaxFusedLoras) {
     const hipError_t e = launch_metadata(mapping, num_tokens, max_tokens, max_loras, meta, stream);
     if (e != hipSuccess) return e;
     return launch_shrink(x, ldx, hidden, lora_a, num_slices, rank, scale, buf, num_splits, meta,

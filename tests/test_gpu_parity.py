@@ -396,9 +396,11 @@ PREP_CASES = [  # T, maxT, hidden, slices, rank, L, kind, splits
     (16, 16, 256, [256], 8, 2, "wild", 2),
     (100, 128, 512, [96, 32], 16, 8, "wild", 3),
     (200, 256, 1024, [256, 256], 8, 4, "all_none", 2),
-    (300, 300, 1024, [512, 256], 32, 64, "runs", 5),
+    (300, 300, 1024, [512, 256], 32, 64, "runs", 5),               # > 16 slots: two launches
+    (480, 512, 1024, [512, 256], 32, 16, "wild", 5),
     (511, 512, 256, [256, 256, 256, 256], 8, 3, "extreme", 1),
     (512, 512, 2048, [1024], 64, 256, "wild", 16),
+    (512, 512, 2048, [1024], 64, 16, "extreme", 16),
     (512, 512, 1024, [256, 256, 256, 256], 64, 16, "runs", 4),  # 16 output blocks: 2 groups
     (700, 720, 1024, [512, 512], 16, 4, "wild", 3),             # larger: two launches
 ]
