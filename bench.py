@@ -38,7 +38,7 @@ CSRC = os.path.join(ROOT, "segmented_rank_gemm_amd", "csrc")
 # sources a kernel's measured traffic depends on
 KERNEL_SOURCES = {
     "lora_expand": ["expand.hip", "device_common.hpp"],
-    "lora_shrink": ["shrink.hip", "device_common.hpp"],
+    "lora_shrink": ["shrink.hip", "device_common.hpp", "metadata_group.hpp"],
 }
 
 
