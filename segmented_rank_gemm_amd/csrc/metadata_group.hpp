@@ -163,10 +163,15 @@ __device__ __forceinline__ void metadata_group(const int32_t* __restrict__ mappi
   for (int b0 = 0; total > 0 && b0 < num_tokens; b0 += kBlock) {
     const int t0 = b0 + tid * kPerThread;
     if (num_tokens > kBlock) load_groups(mapping, num_tokens, max_loras, t0, grp);
-    int mine = 0;
+    // members among this thread's tokens, and up to and including this lane
+    // (ballots with masked popcounts: no chain of cross-lane shuffles)
+    const unsigned long long upto = lane == kWave - 1 ? ~0ull : (2ull << lane) - 1ull;
+    int mine = 0, incl = 0;
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) mine += grp[e] == g ? 1 : 0;
-    const int incl = wave_inclusive_scan(mine);
+    for (int e = 0; e < kPerThread; ++e) {
+      mine += grp[e] == g ? 1 : 0;
+      incl += __popcll(__ballot(grp[e] == g) & upto);
+    }
     if (lane == kWave - 1) wave_scan[wave] = incl;
     __syncthreads();
     int before = 0, block_total = 0;
