@@ -57,21 +57,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x & (kWave - 1)); }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
+// Exclusive prefix sum over the wave's lanes of v >= 0, bit-sliced: one ballot
+// per bit in use, each lane counting the set bits of the lanes below it
+// (v_mbcnt).  No chain of cross-lane shuffles (a dependent shuffle costs about
+// 0.1 us on this part).
+__device__ __forceinline__ int wave_exclusive_sum(int v) {
+  int s = 0;
+  for (int b = 0; b < 31; ++b) {
+    if (__ballot((v >> b) != 0) == 0) break;  // wave-uniform
+    const unsigned long long m = __ballot((v >> b) & 1);
+    const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+        static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+    s += below << b;
   }
-  return v;
-}
-
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
+  return s;
 }
 
 // Segment table: the active adapter slots of one batch (from the metadata
@@ -121,14 +120,15 @@ __device__ void build_segment_table(SegmentTable& tab, const int32_t* __restrict
       const bool ok = i < na && id >= 0 && id < max_loras && cnt > 0 && st >= 0 &&
                       st <= max_tokens && cnt <= max_tokens - st;
       if (!ok) cnt = 0;
-      const int incl = wave_inclusive_scan((cnt + TILE - 1) / TILE);
+      const int nt = (cnt + TILE - 1) / TILE;
+      const int incl = wave_exclusive_sum(nt) + nt;
       if (i < na) {
         tab.start[i] = st;
         tab.count[i] = cnt;
         tab.lora[i] = ok ? id : 0;
         tab.tile_end[i] = carry + incl;
       }
-      carry += __shfl(incl, kWave - 1, kWave);
+      carry += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
     if (lane == 0) {
       tab.num_slots = na;
@@ -177,106 +177,6 @@ __device__ __forceinline__ Tile resolve_tile(const SegmentTable& tab, int m) {
 // is known; the table then says which slot (adapter) each row belongs to.  A
 // slot whose data does not describe a range inside [0, max_tokens) is dropped,
 // so a corrupted metadata buffer cannot send a kernel outside its arrays.
-struct SlotTable {
-  int start[LORA_MAX_LORAS];
-  int end[LORA_MAX_LORAS];
-  int lora[LORA_MAX_LORAS];
-  int num_slots;
-  int act_begin;  // first grouped position with an adapter
-  int act_end;    // one past the last
-};
-
-__device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-  for (int d = kWave / 2; d > 0; d >>= 1) v = min(v, __shfl_xor(v, d, kWave));
-  return v;
-}
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int d = kWave / 2; d > 0; d >>= 1) v = max(v, __shfl_xor(v, d, kWave));
-  return v;
-}
-
-// Fill `tab` from the metadata arrays.  Called by wave 0 only, without a
-// barrier: the caller issues its own independent loads first and then
-// synchronises, so both go out in the same round trip.
-__device__ void load_slot_table(SlotTable& tab, const int32_t* __restrict__ active_ids,
-                                const int32_t* __restrict__ counts,
-                                const int32_t* __restrict__ starts,
-                                const int32_t* __restrict__ num_active, int max_loras,
-                                int max_tokens) {
-  const int lane = lane_id();
-  // Every slot array is written in full by the metadata step, so all loads go
-  // out together with the slot count.
-  int na = *num_active;
-  int cnt0 = 0, st0 = 0, id0 = 0;
-  if (lane < max_loras) {
-    cnt0 = counts[lane];
-    st0 = starts[lane];
-    id0 = active_ids[lane];
-  }
-  na = na < 0 ? 0 : (na > max_loras ? max_loras : na);
-  int lo = max_tokens, hi = 0;
-  for (int base = 0; base < na; base += kWave) {
-    const int i = base + lane;
-    int cnt = cnt0, st = st0, id = id0;
-    if (base > 0) {
-      cnt = 0;
-      if (i < na) {
-        cnt = counts[i];
-        st = starts[i];
-        id = active_ids[i];
-      }
-    }
-    const bool ok = i < na && id >= 0 && id < max_loras && cnt > 0 && st >= 0 &&
-                    st <= max_tokens && cnt <= max_tokens - st;
-    if (i < na) {
-      tab.start[i] = ok ? st : max_tokens;  // a dropped slot owns no position
-      tab.end[i] = ok ? st + cnt : max_tokens;
-      tab.lora[i] = ok ? id : 0;
-    }
-    lo = min(lo, wave_min(ok ? st : max_tokens));
-    hi = max(hi, wave_max(ok ? st + cnt : 0));
-  }
-  if (lane == 0) {
-    tab.num_slots = na;
-    tab.act_begin = lo;
-    tab.act_end = hi;
-  }
-}
-
-// Last slot whose range starts at or before grouped position q (-1 if none).
-// Slots are in ascending position order.  Wave-uniform q.
-__device__ __forceinline__ int slot_at(const SlotTable& tab, int q) {
-  const int lane = lane_id();
-  int best = -1;
-  for (int base = 0; base < tab.num_slots; base += kWave) {
-    const int i = base + lane;
-    const unsigned long long hit = __ballot(i < tab.num_slots && tab.start[i] <= q);
-    if (hit) best = base + 63 - __clzll(static_cast<long long>(hit));
-  }
-  return best;
-}
-
-// The slots a tile of grouped positions [pos0, pos0 + rows) touches, as an
-// inclusive range [first, last]; first > last if the tile has no position with
-// an adapter.
-struct SlotRange {
-  int first;
-  int last;
-};
-__device__ __forceinline__ SlotRange tile_slots(const SlotTable& tab, int pos0, int rows) {
-  const int b = max(pos0, tab.act_begin);
-  const int e = min(pos0 + rows, tab.act_end);
-  SlotRange r{0, -1};
-  if (b < e) {
-    r.first = slot_at(tab, b);
-    r.last = slot_at(tab, e - 1);
-    if (r.first < 0) r.first = 0;
-  }
-  return r;
-}
-
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2),
 // so workgroup b runs on XCD b % 8.  Unit streams are remapped so that each XCD
 // takes one contiguous run of the natural unit order (consecutive tiles of one
@@ -332,18 +232,6 @@ __device__ __forceinline__ int tile_token(const int32_t* __restrict__ sorted, in
                                           int r, int max_tokens) {
   const int t = sorted[first + (r < rows ? r : rows - 1)];
   return (r < rows && t >= 0 && t < max_tokens) ? t : -1;
-}
-
-// Token index at grouped position q, loaded from a clamped (always valid)
-// position; validity against the slot table is decided by the caller.
-__device__ __forceinline__ int token_at_clamped(const int32_t* __restrict__ sorted, int q,
-                                                int max_tokens) {
-  return sorted[q < max_tokens ? q : max_tokens - 1];
-}
-
-// Whether grouped position q with loaded token id t is a row to compute.
-__device__ __forceinline__ bool row_valid(const SlotTable& tab, int q, int t, int max_tokens) {
-  return q >= tab.act_begin && q < tab.act_end && t >= 0 && t < max_tokens;
 }
 
 // All-ones or all-zeros, hidden from the optimizer (an empty asm with a VGPR
