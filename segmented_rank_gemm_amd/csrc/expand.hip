@@ -433,6 +433,10 @@ void expand_shared_kernel(ExpandParams p) {
   constexpr int kPieces = 16 * RANK / kExpandThreads;  // per thread per chunk
   __shared__ SegmentTable tab;
   __shared__ u32x4 b_lds[2][16 * RANK];
+  // per wave: the 16 rows' rank sums, row stride RANK + 4 floats (rows start
+  // on different banks)
+  constexpr int kRankStride = RANK + 4;
+  __shared__ __attribute__((aligned(16))) float rank_lds[kExpandWaves][16 * kRankStride];
 
   build_segment_table<kSharedTile>(tab, p.active_ids, p.counts, p.starts, p.num_active,
                                    p.max_loras, p.max_tokens);
@@ -535,40 +539,65 @@ void expand_shared_kernel(ExpandParams p) {
     load_b(ch0, bp);
 
     // Rank operand of this wave's rows: step q, lane (c, g) holds ranks
-    // 16q + 8*khalf .. +8 of row c, summed over the parts (loads of a group of
-    // 8 parts issued before the adds, adds in part order), as hi or lo bf16.
+    // 16q + 8*khalf .. +8 of row c, summed over the parts, as hi or lo bf16.
+    // The sums are made in a layout where every lane loads different data
+    // (lane (c, g4) sums ranks [kSpan g4, +kSpan) of row c; the operand layout
+    // would load each value twice, for its hi and its lo lanes), with the loads
+    // of kGroup parts issued before the adds (adds in part order), and reach
+    // the operand layout through the wave's own LDS slice.
     RankOperand<RANK> a;
     {
+      constexpr int kSpan = RANK / 4;              // ranks summed per lane
+      constexpr int kLd = kSpan / 4;               // 16-byte loads per part
+      constexpr int kGroup = RANK == 64 ? 4 : 8;   // parts per batch of loads
+      const int g4 = lane >> 4;
       const int64_t plane = static_cast<int64_t>(p.num_slices) * p.max_tokens * RANK;
-      const float* src0 =
-          p.buf + (static_cast<int64_t>(s) * p.max_tokens + (ta >= 0 ? ta : tsafe)) * RANK;
+      const float* src0 = p.buf +
+                          (static_cast<int64_t>(s) * p.max_tokens + (ta >= 0 ? ta : tsafe)) * RANK +
+                          kSpan * g4;
+      float v[kSpan];
+#pragma unroll
+      for (int e = 0; e < kSpan; ++e) v[e] = 0.f;
+      for (int sp0 = 0; sp0 < p.num_splits; sp0 += kGroup) {
+        uint32_t pm[kGroup];
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) pm[i] = opaque_mask(sp0 + i < p.num_splits);
+        u32x4 w[kGroup][kLd];
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+          const int sp = sp0 + i < p.num_splits ? sp0 + i : sp0;
+#pragma unroll
+          for (int l = 0; l < kLd; ++l) w[i][l] = load16(src0 + sp * plane + 4 * l);
+        }
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i)
+#pragma unroll
+          for (int l = 0; l < kLd; ++l)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * l + e] += __uint_as_float(w[i][l][e] & pm[i]);
+      }
+      float* sl = rank_lds[wave];
+#pragma unroll
+      for (int l = 0; l < kLd; ++l)
+        *reinterpret_cast<f32x4*>(sl + c * kRankStride + kSpan * g4 + 4 * l) =
+            f32x4{v[4 * l], v[4 * l + 1], v[4 * l + 2], v[4 * l + 3]};
+      // (the wave's own slice, written and read in program order: LDS
+      // operations of a wave complete in order; the fences keep the compiler
+      // from moving the reads above the other lanes' writes)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int q = 0; q < kSteps; ++q) {
-        const int k0 = 16 * q + 8 * khalf;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.f;
-        for (int sp0 = 0; sp0 < p.num_splits; sp0 += 8) {
-          uint32_t pm[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) pm[i] = opaque_mask(sp0 + i < p.num_splits);
-          u32x4 w[8][2];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int sp = sp0 + i < p.num_splits ? sp0 + i : sp0;
-            w[i][0] = load16(src0 + sp * plane + k0);
-            w[i][1] = load16(src0 + sp * plane + k0 + 4);
-          }
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] += __uint_as_float(w[i][e >> 2][e & 3] & pm[i]);
-        }
+        const float* r8 = sl + c * kRankStride + 16 * q + 8 * khalf;
+        const f32x4 lo4 = *reinterpret_cast<const f32x4*>(r8);
+        const f32x4 hi4 = *reinterpret_cast<const f32x4*>(r8 + 4);
+        const float t[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         uint32_t words[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const uint32_t hi = pack_bf16x2(v[e], v[e + 1]);
-          words[e / 2] = use_lo ? pack_bf16x2(v[e] - bf16_lo(hi), v[e + 1] - bf16_hi(hi)) : hi;
+          const uint32_t hi = pack_bf16x2(t[e], t[e + 1]);
+          words[e / 2] = use_lo ? pack_bf16x2(t[e] - bf16_lo(hi), t[e + 1] - bf16_hi(hi)) : hi;
         }
         a.op[q] = __builtin_bit_cast(bf16x8, u32x4{words[0], words[1], words[2], words[3]});
       }
