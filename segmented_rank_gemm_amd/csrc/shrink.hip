@@ -34,6 +34,8 @@ namespace lora {
 constexpr int kShrinkThreads = 256;
 constexpr int kShrinkWaves = kShrinkThreads / kWave;
 constexpr int kShrinkChunk = 64;  // hidden elements per wave step (two MFMA K-steps)
+constexpr int kMaxFusedLoras = 16;  // adapter slots the fused prepare + shrink serves
+constexpr int kMaxFusedGroups = kMaxFusedLoras + 1;
 
 struct ShrinkParams {
   const uint16_t* x;
@@ -113,24 +115,31 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
 
   // SELF: every wave reads the whole map (8 tokens per lane, at most 2 KB) and
   // keeps, lane-indexed (lane g for group g <= max_loras < 64), each adapter's
-  // count and the start of its run of the padded order (-1: absent); per unit
-  // it finds its tile's token ids itself and passes them between its lanes
-  // through its own LDS slice, so no wave waits for another.  Ballots, lane
-  // reads and scalar loops only: a chain of cross-lane shuffles costs ~0.1 us a
-  // step here.
+  // count and the start of its run of the padded order (-1: absent); the four
+  // waves count a quarter of the groups each (ballots) and share the counts
+  // through LDS.  Per unit each wave finds its tile's token ids itself and
+  // passes them between its lanes through its own LDS slice, so no wave waits
+  // for another.  Ballots, lane reads and scalar loops only: a chain of
+  // cross-lane shuffles costs ~0.1 us a step here.
   __shared__ int w_tile[SELF ? kShrinkWaves : 1][kTile];
+  __shared__ int g_count[SELF ? kMaxFusedGroups : 1];
   const int groups = p.max_loras + 1;
   int mgrp[kPerThread];
   int vcount = 0, vstart = -1, tiles_self = 0;
   if constexpr (SELF) {
     load_groups(p.mapping, p.num_tokens, p.max_loras, lane * kPerThread, mgrp);
-    int below = 0, present = 0, end = 0;  // tokens and adapters before group g
-    for (int gi = 1; gi < groups; ++gi) {
+    for (int gi = 1 + wave; gi < groups; gi += kShrinkWaves) {
       int c = 0;
 #pragma unroll
       for (int e = 0; e < kPerThread; ++e) c += __popcll(__ballot(mgrp[e] == gi));
+      if (lane == 0) g_count[gi] = c;
+    }
+    __syncthreads();
+    vcount = lane >= 1 && lane < groups ? g_count[lane] : 0;
+    int below = 0, present = 0, end = 0;  // tokens and adapters before group g
+    for (int gi = 1; gi < groups; ++gi) {
+      const int c = __builtin_amdgcn_readlane(vcount, gi);
       const int start = round_up_tile(below + (kTile - 1) * present);
-      vcount = lane == gi ? c : vcount;
       vstart = lane == gi ? (c > 0 ? start : -1) : vstart;
       if (c > 0) {
         end = round_up_tile(start + c);
@@ -670,7 +679,6 @@ hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_token
 // kernel's sizes, one wave holding the whole map) and 16 adapter slots (the
 // shrink workgroups loop over the groups): one fused launch.  Otherwise the
 // metadata kernel, then the shrink.
-constexpr int kMaxFusedLoras = 16;
 
 hipError_t launch_prep_shrink(const int32_t* mapping, int num_tokens, const uint16_t* x,
                               int64_t ldx, int hidden, const uint16_t* const* lora_a,
