@@ -433,6 +433,49 @@ def test_prepare_and_shrink_matches_two_calls(T, maxT, hidden, slices, rank, L, 
                           d2.buf.view(torch.int32).cpu().numpy())
 
 
+def _fused_fuzz_cases(n=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    kinds = ["wild", "all_none", "single", "runs", "extreme"]
+    out = []
+    for i in range(n):
+        maxT = int(rng.integers(1, 513))
+        T = int(rng.integers(0, maxT + 1))
+        L = int(rng.integers(1, 17))
+        rank = int(rng.choice([8, 16, 32, 64]))
+        S = int(rng.integers(1, 5))
+        slices = [8 * int(rng.integers(1, 65)) for _ in range(S)]
+        hidden = 8 * int(rng.integers(1, 257))
+        splits = int(rng.integers(1, 18))
+        out.append((T, maxT, hidden, slices, rank, L, kinds[i % len(kinds)], splits, i))
+    return out
+
+
+@pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,kind,splits,seed", _fused_fuzz_cases())
+def test_prepare_and_shrink_fuzz(T, maxT, hidden, slices, rank, L, kind, splits, seed):
+    """Random small shapes through the fused launch: metadata and every part of
+    buf equal to the two calls', word for word."""
+    rng = np.random.default_rng(seed + 500)
+    mapping = make_fuzz_mapping(rng, T, L, kind)
+    w = make_custom_workload(seed, T, hidden, slices, rank, L, 0.5, mapping, max_tokens=maxT)
+    d1 = H.upload(w, num_splits=splits)
+    d2 = H.upload(w, num_splits=splits)
+    srg.lora_prepare_metadata(d1.mapping, T, d1.meta)
+    srg.lora_shrink(d1.x, d1.lora_a, float(w.scale), d1.buf, splits, d1.meta)
+    srg.lora_prepare_and_shrink(d2.mapping, T, d2.x, d2.lora_a, float(w.scale), d2.buf, splits,
+                                d2.meta)
+    torch.cuda.synchronize()
+    m1, m2 = H.meta_host(d1), H.meta_host(d2)
+    nt = int(m1["num_tiles"][0])
+    assert np.array_equal(m1["sorted_token_ids"], m2["sorted_token_ids"])
+    for k in ["active_lora_ids", "num_tokens_per_lora", "lora_token_start", "num_active",
+              "num_tiles", "num_runs"]:
+        assert np.array_equal(m1[k], m2[k]), k
+    assert np.array_equal(m1["tile_token_ids"][:16 * nt], m2["tile_token_ids"][:16 * nt])
+    assert np.array_equal(m1["tile_lora"][:nt], m2["tile_lora"][:nt])
+    assert np.array_equal(d1.buf.view(torch.int32).cpu().numpy(),
+                          d2.buf.view(torch.int32).cpu().numpy())
+
+
 @pytest.mark.parametrize("cfg", [0, 1])
 def test_fused_step_parity_full_size(cfg):
     # the launch configuration the benchmark times for the decode step
