@@ -65,13 +65,10 @@ typedef enum lora_status {
 #define LORA_MAX_SPLITS 64     /* hidden-dimension partitions of the shrink */
 
 /* Tiles of the padded grouped order (see lora_meta_t): LORA_TILE positions
- * each, adapter runs starting on multiples of LORA_RUN_ALIGN(max_tokens)
- * positions, at most LORA_MAX_TILES(max_tokens, max_loras) tiles. */
+ * each, at most LORA_MAX_TILES(max_tokens, max_loras) of them. */
 #define LORA_TILE 16
-#define LORA_RUN_ALIGN(max_tokens) ((max_tokens) > 512 ? 64 : 16)
-#define LORA_MAX_TILES(max_tokens, max_loras)                                 \
-  (((max_tokens) + LORA_TILE - 1) / LORA_TILE +                               \
-   (LORA_RUN_ALIGN(max_tokens) / LORA_TILE) * (max_loras) + 1)
+#define LORA_MAX_TILES(max_tokens, max_loras) \
+  (((max_tokens) + LORA_TILE - 1) / LORA_TILE + (max_loras) + 1)
 
 /*
  * Per-batch grouping of the tokens by adapter: the segment description that
@@ -96,17 +93,13 @@ typedef enum lora_status {
  *
  *   tile_token_ids      int32 [LORA_MAX_TILES * LORA_TILE]: the k-th active
  *                       slot's tokens (in sorted_token_ids order) from
- *                       position P_k = round_up(S_k + (A - 1) * k, A), where
- *                       A = LORA_RUN_ALIGN(max_tokens) and S_k counts the
- *                       tokens of the slots before it; every other position
- *                       below num_tiles * LORA_TILE holds -1.  (The slack term
- *                       makes P_k a function of S_k and k alone, so each
- *                       slot's start is known without the other slots' sizes;
- *                       it leaves at most one empty run of A positions between
- *                       two slots.  With A = 64, for batches over 512 token
- *                       slots, every window of 64 positions from a multiple of
- *                       64 also belongs to one adapter: the large-batch shrink
- *                       reads such windows.)
+ *                       position P_k = round_up(S_k + (LORA_TILE - 1) * k,
+ *                       LORA_TILE), where S_k counts the tokens of the slots
+ *                       before it; every other position below
+ *                       num_tiles * LORA_TILE holds -1.  (The slack term makes
+ *                       P_k a function of S_k and k alone, so each slot's
+ *                       start is known without the other slots' sizes; it
+ *                       leaves at most one empty tile between two slots.)
  *   tile_lora           int32 [LORA_MAX_TILES]: the adapter id of each tile
  *                       below num_tiles, or -1 for a tile of -1 entries.
  *   num_tiles           int32 [1]: tiles in use.

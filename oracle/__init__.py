@@ -110,21 +110,13 @@ def prepare_metadata(mapping: np.ndarray, max_loras: int) -> Dict[str, np.ndarra
 TILE = 16  # positions per tile of the padded grouped order
 
 
-def run_align(max_tokens: int) -> int:
-    """Alignment of the adapter runs in the padded grouped order: 16 positions
-    for batches of at most 512 token slots, 64 above (see prepare_tiles)."""
-    return 16 if int(max_tokens) <= 512 else 64
-
-
-def prepare_tiles(mapping: np.ndarray, max_loras: int, align: int = TILE) -> Dict[str, np.ndarray]:
+def prepare_tiles(mapping: np.ndarray, max_loras: int) -> Dict[str, np.ndarray]:
     """The padded grouped order the kernels read tiles of: for the k-th
     adapter present (ascending id), its tokens in batch order from position
-    P_k = round_up(S_k + (align - 1) * k, align), S_k being the number of tokens
-    of the adapters before it; -1 everywhere else below num_tiles * TILE.
-    ``align`` is 16 (= TILE) or 64 (``run_align``): with 64 every window of 64
-    positions from a multiple of 64 holds one adapter's tokens at most.
-    Returns tile_token_ids [num_tiles * TILE], tile_lora [num_tiles] (the
-    adapter of each tile, -1 for a tile of -1 entries) and num_tiles [1].
+    P_k = round_up(S_k + (TILE - 1) * k, TILE), S_k being the number of tokens of the
+    adapters before it; -1 everywhere else below num_tiles * TILE.  Returns
+    tile_token_ids [num_tiles * TILE], tile_lora [num_tiles] (the adapter of
+    each tile, -1 for a tile of -1 entries) and num_tiles [1].
 
     A layout of this library's own (the pages fix only the grouping itself:
     vLLM PR #13096, "Why do we need a new set of kernels"); written out here
@@ -137,7 +129,7 @@ def prepare_tiles(mapping: np.ndarray, max_loras: int, align: int = TILE) -> Dic
     for k, l in enumerate(sorted(set(int(v) for v in ids if v >= 0))):
         toks = [t for t in range(ids.shape[0]) if ids[t] == l] if ids.shape[0] <= 4096 \
             else np.nonzero(ids == l)[0].tolist()
-        p_k = -(-(s_k + (align - 1) * k) // align) * align
+        p_k = -(-(s_k + (TILE - 1) * k) // TILE) * TILE
         runs.append((p_k, l, toks))
         s_k += len(toks)
     end = runs[-1][0] + len(runs[-1][2]) if runs else 0

@@ -55,15 +55,9 @@ class _MetaStruct(ctypes.Structure):
 TILE = 16  # positions per tile of the padded grouped order (LORA_TILE)
 
 
-def run_align(max_tokens: int) -> int:
-    """LORA_RUN_ALIGN: alignment of the adapter runs in the padded grouped order."""
-    return 64 if int(max_tokens) > 512 else 16
-
-
 def max_tiles(max_tokens: int, max_loras: int) -> int:
     """LORA_MAX_TILES: tiles the padded grouped order may use."""
-    return ((int(max_tokens) + TILE - 1) // TILE
-            + (run_align(max_tokens) // TILE) * int(max_loras) + 1)
+    return (int(max_tokens) + TILE - 1) // TILE + int(max_loras) + 1
 
 
 _VP = ctypes.c_void_p

@@ -33,8 +33,8 @@ namespace lora {
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void metadata_kernel(const int32_t* __restrict__ mapping,
                                                            int num_tokens, int max_loras,
-                                                           MetaOut out, int run_align) {
-  metadata_group<THREADS>(mapping, num_tokens, max_loras, out, blockIdx.x, run_align);
+                                                           MetaOut out) {
+  metadata_group<THREADS>(mapping, num_tokens, max_loras, out, blockIdx.x);
 }
 
 hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_tokens, int max_loras,
@@ -44,16 +44,13 @@ hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_token
                     meta.tile_lora, meta.num_tiles, meta.num_runs};
   if (max_tokens <= 64 * kPerThread) {
     hipLaunchKernelGGL(metadata_kernel<64>, dim3(max_loras + 1), dim3(64), 0, stream, mapping,
-                       num_tokens, max_loras, out,
-                       LORA_RUN_ALIGN(max_tokens));
+                       num_tokens, max_loras, out);
   } else if (max_tokens <= 256 * kPerThread) {
     hipLaunchKernelGGL(metadata_kernel<256>, dim3(max_loras + 1), dim3(256), 0, stream, mapping,
-                       num_tokens, max_loras, out,
-                       LORA_RUN_ALIGN(max_tokens));
+                       num_tokens, max_loras, out);
   } else {
     hipLaunchKernelGGL(metadata_kernel<1024>, dim3(max_loras + 1), dim3(1024), 0, stream, mapping,
-                       num_tokens, max_loras, out,
-                       LORA_RUN_ALIGN(max_tokens));
+                       num_tokens, max_loras, out);
   }
   return hipGetLastError();
 }

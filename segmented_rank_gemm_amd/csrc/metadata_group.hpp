@@ -51,15 +51,12 @@ constexpr int kMetaTile = LORA_TILE;
 __device__ __forceinline__ int round_up_tile(int v) {
   return (v + kMetaTile - 1) / kMetaTile * kMetaTile;
 }
-// v rounded up to a multiple of a (a power of two: 16 or 64), v >= 0.
-__device__ __forceinline__ int round_up_to(int v, int a) { return (v + a - 1) & ~(a - 1); }
 
 // Group g's share of the metadata, by one workgroup of THREADS threads (every
 // thread of the workgroup calls it); a block of the map is THREADS * 8 tokens.
 template <int THREADS>
 __device__ __forceinline__ void metadata_group(const int32_t* __restrict__ mapping, int num_tokens,
-                                               int max_loras, const MetaOut& out, int g,
-                                               int run_align) {
+                                               int max_loras, const MetaOut& out, int g) {
   constexpr int kWaves = THREADS / kWave;
   constexpr int kBlock = THREADS * kPerThread;
   __shared__ int present[LORA_MAX_LORAS + 1];
@@ -125,11 +122,11 @@ __device__ __forceinline__ void metadata_group(const int32_t* __restrict__ mappi
     npresent += __popcll(__ballot(p));
   }
 
-  // An adapter's run of the padded order starts at pstart, a multiple of
-  // run_align (16 or 64); group 0, no adapter, has none.
+  // An adapter's run of the padded order starts at pstart (group 0, no
+  // adapter, has none).
   const bool has_run = g > 0;
   const int s_k = start - n_none;  // tokens of lower adapters
-  const int pstart = round_up_to(s_k + (run_align - 1) * k, run_align);
+  const int pstart = round_up_tile(s_k + (kMetaTile - 1) * k);
 
   // The slot entries (group 0: the unused slots and the counts) and, past the
   // run's members, -1 up to the next run's start (for the last run, to the end
@@ -152,8 +149,7 @@ __device__ __forceinline__ void metadata_group(const int32_t* __restrict__ mappi
     }
     const int run_end = round_up_tile(pstart + total);
     const bool last = k == npresent - 1;
-    const int pnext =
-        last ? run_end : round_up_to(s_k + total + (run_align - 1) * (k + 1), run_align);
+    const int pnext = last ? run_end : round_up_tile(s_k + total + (kMetaTile - 1) * (k + 1));
     for (int i = pstart + total + tid; i < pnext; i += THREADS) out.tile_ids[i] = -1;
     for (int m = pstart / kMetaTile + tid; m < pnext / kMetaTile; m += THREADS)
       out.tile_lora[m] = m < run_end / kMetaTile ? g - 1 : -1;

@@ -90,8 +90,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
   if constexpr (SELF) {
     if (static_cast<int>(blockIdx.x) >= p.shrink_grid) {  // workgroup-uniform
       metadata_group<kShrinkThreads>(p.mapping, p.num_tokens, p.max_loras, p.meta_out,
-                                     static_cast<int>(blockIdx.x) - p.shrink_grid,
-                                     LORA_TILE);  // (at most 512 token slots)
+                                     static_cast<int>(blockIdx.x) - p.shrink_grid);
       return;
     }
   }

@@ -42,7 +42,7 @@ def _check_meta(meta_gpu, ref, T, max_tokens, sorted_fill=-7, mapping=None, L=No
         assert np.array_equal(meta_gpu[k], ref[k]), k
     if mapping is not None:
         # the padded tiles, bit for bit below num_tiles
-        tiles = oracle.prepare_tiles(mapping, L, align=oracle.run_align(max_tokens))
+        tiles = oracle.prepare_tiles(mapping, L)
         nt = int(tiles["num_tiles"][0])
         assert int(meta_gpu["num_tiles"][0]) == nt
         assert np.array_equal(meta_gpu["tile_token_ids"][:nt * 16], tiles["tile_token_ids"])

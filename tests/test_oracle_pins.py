@@ -190,42 +190,6 @@ def test_tiles_worked_example():
     assert t["num_tiles"].tolist() == [4]
 
 
-def test_tiles_worked_example_align64():
-    # the same batch with runs aligned to 64: S = 0, 2, 3 and k = 0, 1, 2 give
-    # starts round_up(S + 63k, 64) = 0, 128, 192 by hand (an empty window of 64
-    # between adapters 0 and 1, as the slack term allows)
-    t = oracle.prepare_tiles(np.array([2, -1, 0, 2, 1, -1, 0, 7]), 3, align=64)
-    want = np.full(13 * 16, -1)
-    want[[0, 1, 128, 192, 193]] = [2, 6, 4, 0, 3]
-    assert t["tile_token_ids"].tolist() == want.tolist()
-    assert t["tile_lora"].tolist() == [0] + [-1] * 7 + [1, -1, -1, -1, 2]
-    assert t["num_tiles"].tolist() == [13]
-    assert oracle.run_align(512) == 16 and oracle.run_align(513) == 64
-
-
-@pytest.mark.parametrize("kind", FUZZ_KINDS)
-@pytest.mark.parametrize("T,L", [(37, 3), (1000, 16), (4096, 64), (5000, 256)])
-def test_tiles_align64_windows_hold_one_adapter(kind, T, L):
-    rng = np.random.default_rng(T * 77 + L)
-    mapping = make_fuzz_mapping(rng, T, L, kind)
-    ids = _sanitize(mapping, L)
-    t = oracle.prepare_tiles(mapping, L, align=64)
-    tok, lora, nt = t["tile_token_ids"], t["tile_lora"], int(t["num_tiles"][0])
-    order = np.argsort(ids, kind="stable")
-    assert np.array_equal(tok[tok >= 0], order[ids[order] >= 0])
-    # every window of 64 positions holds one adapter's tokens at most, and each
-    # adapter's run starts on a multiple of 64
-    pad = np.full(-(-tok.size // 64) * 64, -1)
-    pad[:tok.size] = tok
-    for win in pad.reshape(-1, 64):
-        assert len(set(ids[win[win >= 0]].tolist())) <= 1
-    for l in sorted(set(ids[ids >= 0].tolist())):
-        first = int(np.nonzero(tok == order[ids[order] == l][0])[0][0])
-        assert first % 64 == 0
-    # the bound the buffers are sized by: ceil(T/16) + 4 L + 1 tiles
-    assert nt <= -(-T // 16) + 4 * L + 1
-
-
 def test_tiles_empty_and_no_adapter():
     for mapping in (np.zeros(0, dtype=np.int32), np.full(40, -1)):
         t = oracle.prepare_tiles(mapping, 4)
