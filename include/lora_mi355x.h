@@ -146,9 +146,9 @@ typedef struct lora_meta {
  *
  * Writes sorted_token_ids[0:num_tokens], all max_loras entries of the three
  * per-slot arrays, num_active, the padded tiles below num_tiles with
- * num_tiles, and num_runs.  A stable counting sort: bit-for-bit deterministic, no atomics on
- * global memory.  Grid: max_loras + 1 workgroups (of 64, 256 or 1024 threads
- * by max_tokens).
+ * num_tiles, and num_runs.  A stable counting sort: bit-for-bit
+ * deterministic, no atomics on global memory.  Grid: max_loras + 1
+ * workgroups (of 64, 256 or 1024 threads by max_tokens).
  */
 lora_status_t lora_prepare_metadata(const int32_t *token_lora_mapping, int32_t num_tokens,
                                     int32_t max_tokens, int32_t max_loras,
@@ -158,7 +158,10 @@ lora_status_t lora_prepare_metadata(const int32_t *token_lora_mapping, int32_t n
  * lora_shrink_default_splits - recommended number of hidden-dimension
  * partitions for lora_shrink (host only, no device access).  Returns a value in
  * [1, LORA_MAX_SPLITS], or 0 if an argument is out of range.  The result is a
- * pure function of its arguments.
+ * pure function of its arguments: a rule on the sizes alone.  The best value
+ * also depends on how the batch's tiles round against the compute units; the
+ * Python helper segmented_rank_gemm_amd.tuning.tune_shrink_splits measures it
+ * on a representative batch.
  */
 int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t max_loras,
                                    int32_t num_slices, int32_t rank);
