@@ -99,13 +99,15 @@ struct BStage {
 };
 
 // LDS slot of 16-byte piece pr of chunk row `row` (RANK / 8 pieces per row):
-// row-major, with the low three bits XOR-ed by (row / 8) % 8, so that the 16
-// lanes reading rows 8c + b (c = 0..15) of one block spread over the banks.
-// The XOR leaves the bits that hold row / 8 unchanged: a bijection on the
-// region's 16 * RANK slots.
+// row-major, with the low bits XOR-ed by row / 8 (four bits of it from rank 16
+// on, three at rank 8), so that the 16 lanes reading rows 8c + b (c = 0..15)
+// of one block fall on 16 different bank groups.  (With three bits, rows c and
+// c + 8 shared their banks: 2.4 conflict cycles per LDS instruction on the
+// prefill expand.)  The XOR only touches bits below those holding row / 8 (at
+// rank 8 it must stop at three): a bijection on the region's 16 * RANK slots.
 template <int RANK>
 __device__ __forceinline__ int bslot(int row, int pr) {
-  return (row * (RANK / 8) + pr) ^ ((row >> 3) & 7);
+  return (row * (RANK / 8) + pr) ^ ((row >> 3) & (RANK >= 16 ? 15 : 7));
 }
 
 // MW = 16-token blocks per tile; every block shares the B operand loads.
