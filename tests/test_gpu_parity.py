@@ -75,6 +75,7 @@ def test_metadata_bit_exact_full_size(cfg):
 FUZZ = [(0, 1, 1, "wild"), (0, 64, 8, "wild"), (1, 1, 1, "single"), (1, 5, 256, "wild"),
         (63, 64, 3, "runs"), (64, 64, 2, "wild"), (65, 100, 4, "extreme"), (1023, 1024, 16, "wild"),
         (1024, 1024, 64, "all_none"), (1025, 3000, 64, "runs"), (3000, 3000, 1, "wild"),
+        (4096, 4096, 64, "wild"), (2049, 4096, 7, "extreme"),  # one full 512-thread block
         (4097, 5000, 256, "wild"), (8192, 8192, 4, "runs"), (20000, 20000, 256, "extreme"),
         (65536, 70000, 33, "wild"), (777, 777, 255, "single"),
         (1 << 20, (1 << 20) + 3, 256, "wild")]  # many blocks, every adapter slot
