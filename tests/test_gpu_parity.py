@@ -404,6 +404,7 @@ PREP_CASES = [  # T, maxT, hidden, slices, rank, L, kind, splits
     (512, 512, 2048, [1024], 64, 16, "extreme", 16),
     (512, 512, 1024, [256, 256, 256, 256], 64, 16, "runs", 4),  # 16 output blocks: 2 groups
     (700, 720, 1024, [512, 512], 16, 4, "wild", 3),             # larger: two launches
+    (3000, 3500, 512, [256, 128], 32, 40, "runs", 4),           # 512-thread metadata
 ]
 
 
