@@ -99,15 +99,20 @@ struct BStage {
 };
 
 // LDS slot of 16-byte piece pr of chunk row `row` (RANK / 8 pieces per row):
-// row-major, with the low bits XOR-ed by row / 8 (four bits of it from rank 16
-// on, three at rank 8), so that the 16 lanes reading rows 8c + b (c = 0..15)
-// of one block fall on 16 different bank groups.  (With three bits, rows c and
-// c + 8 shared their banks: 2.4 conflict cycles per LDS instruction on the
-// prefill expand.)  The XOR only touches bits below those holding row / 8 (at
-// rank 8 it must stop at three): a bijection on the region's 16 * RANK slots.
+// row-major, with the low bits XOR-ed by a key taken from the row's high bits,
+// so that the 16 lanes reading rows 8c + b (c = 0..15) of one block fall on 16
+// different bank groups.  From rank 16 on the key is four bits of row / 8; at
+// rank 8 (one piece per row, 8-byte reads whose half-wave passes pair lanes c
+// and c + 8 on the same banks unless bit 3 of c enters the key) it is three
+// bits of row / 16, and a 16-lane write of 16 consecutive rows stays one
+// contiguous 256-byte block.  (With three bits of row / 8 at every rank, rows
+// c and c + 8 shared their banks: 2.4 conflict cycles per LDS instruction on
+// the prefill expand, 1.4 on the decode expand.)  The XOR only touches bits
+// below the row's block index: a bijection on the region's 16 * RANK slots.
 template <int RANK>
 __device__ __forceinline__ int bslot(int row, int pr) {
-  return (row * (RANK / 8) + pr) ^ ((row >> 3) & (RANK >= 16 ? 15 : 7));
+  if constexpr (RANK == 8) return row ^ ((row >> 4) & 7);
+  return (row * (RANK / 8) + pr) ^ ((row >> 3) & 15);
 }
 
 // MW = 16-token blocks per tile; every block shares the B operand loads.
