@@ -156,11 +156,21 @@ class LoraMeta:
         return ctypes.byref(self._struct)
 
 
+def _mapping_ptr(token_lora_mapping: torch.Tensor, num_tokens: int) -> int:
+    """Device address of the token -> adapter map (0 for an empty batch)."""
+    if not num_tokens:
+        return 0
+    ptr = _dev_ptr(token_lora_mapping, torch.int32, "token_lora_mapping")
+    if token_lora_mapping.dim() != 1 or not token_lora_mapping.is_contiguous():
+        raise ValueError("token_lora_mapping must be a contiguous 1-D tensor")
+    if token_lora_mapping.numel() < num_tokens:
+        raise ValueError("token_lora_mapping is shorter than num_tokens")
+    return ptr
+
+
 def lora_prepare_metadata(token_lora_mapping: torch.Tensor, num_tokens: int, meta: LoraMeta,
                           stream: Optional[torch.cuda.Stream] = None) -> None:
-    ptr = _dev_ptr(token_lora_mapping, torch.int32, "token_lora_mapping") if num_tokens else 0
-    if num_tokens and token_lora_mapping.numel() < num_tokens:
-        raise ValueError("token_lora_mapping is shorter than num_tokens")
+    ptr = _mapping_ptr(token_lora_mapping, num_tokens)
     _check("lora_prepare_metadata", lib().lora_prepare_metadata(
         ptr, int(num_tokens), meta.max_tokens, meta.max_loras, meta.struct_ref,
         _stream_handle(stream)))
@@ -174,9 +184,14 @@ def lora_shrink_default_splits(hidden: int, max_tokens: int, max_loras: int, num
 def _shrink_args(x: torch.Tensor, lora_a: Sequence[torch.Tensor], buf: torch.Tensor,
                  num_splits: int, meta: LoraMeta):
     S = len(lora_a)
+    if S < 1:
+        raise ValueError("lora_a must hold at least one slice")
+    if lora_a[0].dim() != 3:
+        raise ValueError("lora_a[s] must be [max_loras, rank, hidden]")
     _, rank, hidden = lora_a[0].shape
-    if x.dim() != 2 or x.stride(1) != 1 or x.shape[0] < meta.max_tokens:
-        raise ValueError("x must be [>=max_tokens, hidden] with unit column stride")
+    if (x.dim() != 2 or x.stride(1) != 1 or x.shape[0] < meta.max_tokens
+            or x.shape[1] < hidden):
+        raise ValueError("x must be [>=max_tokens, >=hidden] with unit column stride")
     if tuple(buf.shape) != (num_splits, S, meta.max_tokens, rank) or not buf.is_contiguous():
         raise ValueError("buf must be contiguous [num_splits, S, max_tokens, rank]")
     for a in lora_a:
@@ -204,9 +219,7 @@ def lora_prepare_and_shrink(token_lora_mapping: torch.Tensor, num_tokens: int, x
                             stream: Optional[torch.cuda.Stream] = None) -> None:
     """lora_prepare_metadata then lora_shrink on the same batch (one launch up to
     512 token slots); arguments as for those two."""
-    ptr = _dev_ptr(token_lora_mapping, torch.int32, "token_lora_mapping") if num_tokens else 0
-    if num_tokens and token_lora_mapping.numel() < num_tokens:
-        raise ValueError("token_lora_mapping is shorter than num_tokens")
+    ptr = _mapping_ptr(token_lora_mapping, num_tokens)
     S, rank, hidden, aptrs = _shrink_args(x, lora_a, buf, num_splits, meta)
     _check("lora_prepare_and_shrink", lib().lora_prepare_and_shrink(
         ptr, int(num_tokens), _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), hidden, aptrs,
@@ -219,6 +232,10 @@ def lora_expand(buf: torch.Tensor, num_splits: int, lora_b: Sequence[torch.Tenso
     """buf: fp32 [num_splits, S, max_tokens, rank]; lora_b[s]: bf16 [max_loras, n_s, rank];
     y: bf16 [>=max_tokens, >=sum(n_s)] (row stride y.stride(0)), updated in place."""
     S = len(lora_b)
+    if S < 1:
+        raise ValueError("lora_b must hold at least one slice")
+    if lora_b[0].dim() != 3:
+        raise ValueError("lora_b[s] must be [max_loras, n_s, rank]")
     rank = int(lora_b[0].shape[2])
     sizes = [int(b.shape[1]) for b in lora_b]
     if tuple(buf.shape) != (num_splits, S, meta.max_tokens, rank) or not buf.is_contiguous():

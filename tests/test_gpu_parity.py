@@ -282,6 +282,36 @@ def test_inputs_never_written():
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
 
 
+def test_binding_rejects_bad_views():
+    """The binding refuses, before any launch, views the library would misread:
+    a strided map, x narrower than hidden, a transposed y, empty weight lists,
+    host tensors; the buffers it was given stay as they were."""
+    w = make_workload(0, num_tokens=16, max_tokens=24)
+    d = H.upload(w, buf_fill=1.5)
+    y0 = d.y.clone()
+    strided = torch.zeros(2 * w.num_tokens, dtype=torch.int32, device="cuda")[::2]
+    with pytest.raises(ValueError, match="contiguous 1-D"):
+        srg.lora_prepare_metadata(strided, w.num_tokens, d.meta)
+    with pytest.raises(ValueError, match="contiguous 1-D"):
+        srg.lora_prepare_and_shrink(strided, w.num_tokens, d.x, d.lora_a, 1.0, d.buf,
+                                    d.num_splits, d.meta)
+    narrow = d.x[:, : w.hidden - 8]
+    with pytest.raises(ValueError, match=">=hidden"):
+        srg.lora_shrink(narrow, d.lora_a, 1.0, d.buf, d.num_splits, d.meta)
+    with pytest.raises(ValueError, match="at least one slice"):
+        srg.lora_shrink(d.x, [], 1.0, d.buf, d.num_splits, d.meta)
+    with pytest.raises(ValueError, match="at least one slice"):
+        srg.lora_expand(d.buf, d.num_splits, [], d.y, d.meta)
+    yt = torch.zeros((d.y.shape[1], d.y.shape[0]), dtype=torch.bfloat16, device="cuda").t()
+    with pytest.raises(ValueError, match="unit column stride"):
+        srg.lora_expand(d.buf, d.num_splits, d.lora_b, yt, d.meta)
+    with pytest.raises(TypeError, match="device tensor"):
+        srg.lora_prepare_metadata(d.mapping.cpu(), w.num_tokens, d.meta)
+    torch.cuda.synchronize()
+    assert torch.equal(d.y.view(torch.int16), y0.view(torch.int16))
+    assert bool((d.buf == 1.5).all())
+
+
 def test_bitwise_deterministic():
     w = make_workload(4, num_tokens=900)
     outs = []
