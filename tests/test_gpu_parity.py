@@ -218,6 +218,47 @@ def test_large_batch_parts(T, hidden, slices, rank, L, splits):
     _full_check(w, d)
 
 
+def _large_fuzz_cases(n=16, seed=4099):
+    """Seeded random shapes above 512 token slots (the LDS-staged shrink; the
+    grid-strided and run-count walks of the rank-8/16 expand; the shared-B
+    expand at ranks 32 and 64): token count, slots, hidden size, slices, rank,
+    adapter slots, map kind, part count and row padding all drawn."""
+    rng = np.random.default_rng(seed)
+    kinds = ["wild", "runs", "extreme", "single", "all_none"]
+    out = []
+    for i in range(n):
+        maxT = int(rng.integers(513, 2561))
+        T = int(rng.integers(max(1, maxT - 300), maxT + 1))
+        hidden = int(rng.choice([64, 200, 512, 1032, 2048]))
+        rank = int(rng.choice([8, 16, 32, 64]))
+        S = int(rng.integers(1, 5))
+        slices = [8 * int(v) for v in rng.integers(1, 97, size=S)]
+        L = int(rng.choice([1, 3, 8, 17, 64]))
+        splits = int(rng.integers(1, min(16, max(1, hidden // 64)) + 1))
+        ldx_pad, ldy_pad = 8 * int(rng.integers(0, 3)), 8 * int(rng.integers(0, 3))
+        out.append((T, maxT, hidden, slices, rank, L, kinds[i % len(kinds)], splits,
+                    ldx_pad, ldy_pad, i))
+    return out
+
+
+@pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,kind,splits,ldx_pad,ldy_pad,seed",
+                         _large_fuzz_cases())
+def test_large_batch_step_fuzz(T, maxT, hidden, slices, rank, L, kind, splits, ldx_pad, ldy_pad,
+                               seed):
+    """The whole step through the fused entry point (two launches here) and the
+    expand, against the oracle, on seeded random large-batch shapes."""
+    print(f"[large fuzz] seed={seed} T={T} maxT={maxT} hidden={hidden} slices={slices} "
+          f"rank={rank} L={L} kind={kind} splits={splits}", flush=True)
+    rng = np.random.default_rng(10_000 + seed)
+    mapping = make_fuzz_mapping(rng, T, L, kind)
+    w = make_custom_workload(20_000 + seed, T, hidden, slices, rank, L, 0.75, mapping,
+                             max_tokens=maxT)
+    d = H.upload(w, num_splits=splits, ldx_pad=ldx_pad, ldy_pad=ldy_pad)
+    H.run_step_fused(d)
+    torch.cuda.synchronize()
+    _full_check(w, d)
+
+
 @pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,ldx_pad,ldy_pad,splits", SHAPES)
 def test_shape_sweep(T, maxT, hidden, slices, rank, L, ldx_pad, ldy_pad, splits):
     rng = np.random.default_rng(T + hidden)
