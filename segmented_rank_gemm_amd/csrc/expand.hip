@@ -408,22 +408,32 @@ constexpr int kSharedTile = 64;
 
 // Chunks per column range of the shared-B kernel, chosen for the batch at
 // hand (its tile count is known only on the device).  Each XCD's workgroups
-// take its run of units in rounds; a unit costs its chunks plus a start-up of
-// about three chunks' time (token ids, rank operand, first B chunk), so the
-// choice minimises rounds * (chunks + 3), ties to the longer range (measured
-// on the down_proj and 70B qkv batches: this cost orders all lengths from 2
-// to 16 as their times do).  Every lane computes the same value.
+// take its run of units in rounds; a unit costs its chunks plus a start-up,
+// in chunk times: half a chunk of fixed latency (token ids, first B chunk)
+// plus the fetch of the shrink's parts for the tile's rows, which pass through
+// the CU like the chunks' B and y (measured: the kernels are bound by what
+// each unit fetches, cache hits included).  The choice minimises rounds *
+// (chunks + start-up), ties to the longer range; on the down_proj (rank 64,
+// 8 parts: start-up 3.2) and 70B qkv (rank 32, 6 parts: 1.7) batches it picks
+// the fastest length measured.  Every lane computes the same value.
 // (The search runs at every workgroup's start, so it avoids integer division:
 // the range counts come from the host, and the rounds, integers below 2^20,
 // are exact enough in fp32 less a margin well above its rounding error.)
+template <int RANK>
 __device__ int shared_chunks_per_range(const ExpandParams& p, int tiles, int grid) {
+  // bytes one chunk moves: its B rows, and its y columns of the tile read and written
+  constexpr float kChunkBytes = kExpandCols * RANK * 2 + kSharedTile * kExpandCols * 2 * 2;
+  const float startup =
+      0.5f + static_cast<float>(kSharedTile * RANK * 4) * static_cast<float>(p.num_splits) /
+                 kChunkBytes;
   const int slots = (grid < p.num_cus ? grid : p.num_cus) / kXcds;  // CUs per XCD at work
   const float inv_slots = 1.0f / static_cast<float>(slots > 0 ? slots : 1);
   int best = 8;
   float best_cost = 3.0e38f;
   for (int cpr = kMaxSharedCpr; cpr >= 2; --cpr) {
     const int per_xcd = (tiles * p.ranges_by_cpr[cpr] + kXcds - 1) / kXcds;
-    const float cost = ceilf(static_cast<float>(per_xcd) * inv_slots - 1e-3f) * (cpr + 3);
+    const float cost =
+        ceilf(static_cast<float>(per_xcd) * inv_slots - 1e-3f) * (static_cast<float>(cpr) + startup);
     if (cost < best_cost) {
       best_cost = cost;
       best = cpr;
@@ -432,8 +442,10 @@ __device__ int shared_chunks_per_range(const ExpandParams& p, int tiles, int gri
   return best;
 }
 
+// Rank 32 fits three waves per SIMD (158 VGPRs), so three workgroups share a CU
+// (70B qkv batch: 39.3 against 40.8 us); rank 64 would spill there.
 template <int RANK>
-__global__ __launch_bounds__(kExpandThreads) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(kExpandThreads) __attribute__((amdgpu_waves_per_eu(RANK == 32 ? 3 : 1)))
 void expand_shared_kernel(ExpandParams p) {
   constexpr int kSteps = RANK / 16;
   constexpr int kRowPieces = RANK / 8;           // 16-byte pieces per B row
@@ -457,7 +469,7 @@ void expand_shared_kernel(ExpandParams p) {
   // (the table's values are the same in every lane: read them as scalars)
   const int num_tiles = __builtin_amdgcn_readfirstlane(tab.num_tiles);
   const int cpr = p.chunks_per_range > 0 ? p.chunks_per_range
-                                         : shared_chunks_per_range(p, num_tiles, gridDim.x);
+                                         : shared_chunks_per_range<RANK>(p, num_tiles, gridDim.x);
   int range_end[LORA_MAX_SLICES];  // running count of column ranges through slice s
   {
     int ranges = 0;
@@ -779,9 +791,10 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
     p.ranges_by_cpr[c] = r;
   }
   int64_t grid = tiles * ranges;
-  // shared-B: two workgroups per CU (one hides the other's unit start-up; the
-  // range choice counts rounds per CU, whose fetch rate bounds both)
-  int64_t wg_per_cu = shared ? 2 : 8;
+  // shared-B: two workgroups per CU at rank 64, three at rank 32 (one hides
+  // another's unit start-up; the range choice counts rounds per CU, whose
+  // fetch rate bounds them all)
+  int64_t wg_per_cu = shared ? (rank == 32 ? 3 : 2) : 8;
 #ifdef LORA_TUNING
   if (const char* e = getenv("LORA_EXPAND_SHARED_WPC")) if (shared) wg_per_cu = atoi(e);
 #endif
