@@ -148,7 +148,7 @@ typedef struct lora_meta {
  * per-slot arrays, num_active, the padded tiles below num_tiles with
  * num_tiles, and num_runs.  A stable counting sort: bit-for-bit
  * deterministic, no atomics on global memory.  Grid: max_loras + 1
- * workgroups (of 64, 256 or 1024 threads by max_tokens).
+ * workgroups (of 64, 256, 512 or 1024 threads by max_tokens).
  */
 lora_status_t lora_prepare_metadata(const int32_t *token_lora_mapping, int32_t num_tokens,
                                     int32_t max_tokens, int32_t max_loras,
