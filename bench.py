@@ -5,11 +5,12 @@ one synthetic batch, as two calls: lora_prepare_and_shrink (metadata and shrink,
 one launch up to 512 token slots) and lora_expand; the same step as three calls
 is reported next to it.  Inputs are resident in HBM before timing starts.  To keep
 the 256 MB Infinity Cache from serving repeats, R copies of every buffer (at
-least 1 GiB in total) are rotated: one HIP graph holds R consecutive steps, each
-on its own copy.  Per-kernel launch durations for the roofline figure are
-measured the same way (a graph of launches of one kernel, over enough copies
-that the kernel's own buffers span 1 GiB), with HIP events on the stream the
-graph is replayed on.  The CPU oracle is timed on the host's
+least 1 GiB in total) are rotated: one HIP graph holds consecutive steps, each
+on the next copy in turn (at least 16 steps, so that a replay's fixed cost is
+spread thin; a copy comes round again only after the others).  Per-kernel
+launch durations for the roofline figure are measured the same way (a graph of
+at least 32 launches of one kernel, over enough copies that the kernel's own
+buffers span 1 GiB), with HIP events on the stream the graph is replayed on.  The CPU oracle is timed on the host's
 cores on the same batch, as a reported baseline.
 
 Prints exactly one JSON line on stdout (progress goes to stderr).
@@ -33,6 +34,11 @@ CPU_BUDGET_S = 10.0      # the CPU baseline runs full batches for about this lon
 ROTATE_BYTES = 1 << 30
 ROTATE_CAP = 48 << 30    # device memory the rotated copies may take in all
 ROTATE_MAX_SETS = 512
+# A graph cycles through its copies until it holds at least this many launch
+# groups, so that the fixed cost of a replay is spread over many of them (a
+# copy comes round again only after the others, which span ROTATE_BYTES).
+MIN_GRAPH_STEPS = 16
+MIN_GRAPH_LAUNCHES = 32
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "segmented_rank_gemm_amd", "csrc")
 # sources a kernel's measured traffic depends on
@@ -293,17 +299,18 @@ def run_config(idx, args):
         sets.step(r)
     torch.cuda.synchronize()
 
-    g_step = capture([lambda s, r=r: sets.step(r, s) for r in range(R)])
+    G = R * max(1, math.ceil(MIN_GRAPH_STEPS / R))  # steps per graph, copies in turn
+    g_step = capture([lambda s, r=r: sets.step(r % R, s) for r in range(G)])
     steps = args.steps if args.steps is not None else R * 200
     warm = args.warmup if args.warmup is not None else R * 20
-    full, rem = divmod(steps, R)
-    g_rem = capture([lambda s, r=r: sets.step(r, s) for r in range(rem)]) if rem else None
-    wfull, wrem = divmod(warm, R)
+    full, rem = divmod(steps, G)
+    g_rem = capture([lambda s, r=r: sets.step(r % R, s) for r in range(rem)]) if rem else None
+    wfull, wrem = divmod(warm, G)
     log(f"[bench] warmup {warm} steps")
     for _ in range(wfull):
         g_step.replay()
     if wrem:
-        capture([lambda s, r=r: sets.step(r, s) for r in range(wrem)]).replay()
+        capture([lambda s, r=r: sets.step(r % R, s) for r in range(wrem)]).replay()
     torch.cuda.synchronize()
 
     log(f"[bench] timing {steps} steps")
@@ -342,8 +349,9 @@ def run_config(idx, args):
            "pair": lambda r, s: (sets.shrink(r, s), sets.expand(r, s)), "step3": sets.step3}
     for name in ("metadata", "shrink", "prepare_and_shrink", "expand", "pair", "step3"):
         n = rot[name]
-        g = capture([lambda s, r=r, f=fns[name]: f(r, s) for r in range(n)])
-        per[name] = time_graph(g, reps) / n
+        m = n * max(1, math.ceil(MIN_GRAPH_LAUNCHES / n))  # launch groups per graph
+        g = capture([lambda s, r=r, f=fns[name]: f(r % n, s) for r in range(m)])
+        per[name] = time_graph(g, reps) / m
         del g
     pair_s = per.pop("pair")
     step3_s = per.pop("step3")
