@@ -1,17 +1,20 @@
 """Throughput of the multi-LoRA metadata + shrink + expand step on one MI355X.
 
 A step is one pass of the whole path (grouping metadata, shrink, expand) over
-one synthetic batch, as two calls: lora_prepare_and_shrink (metadata and shrink,
-one launch up to 512 token slots) and lora_expand; the same step as three calls
-is reported next to it.  Inputs are resident in HBM before timing starts.  To keep
+one synthetic batch, through lora_fused_step: one launch on small batches
+(up to 512 token slots with few adapter outputs; the decode workload), else
+lora_prepare_and_shrink and lora_expand.  The same step as three calls is
+reported next to it.  Inputs are resident in HBM before timing starts.  To keep
 the 256 MB Infinity Cache from serving repeats, R copies of every buffer (at
 least 1 GiB in total) are rotated: one HIP graph holds consecutive steps, each
 on the next copy in turn (at least 16 steps, so that a replay's fixed cost is
-spread thin; a copy comes round again only after the others).  Per-kernel
-launch durations for the roofline figure are measured the same way (a graph of
-at least 32 launches of one kernel, over enough copies that the kernel's own
-buffers span 1 GiB), with HIP events on the stream the graph is replayed on.  The CPU oracle is timed on the host's
-cores on the same batch, as a reported baseline.
+spread thin; a copy comes round again only after the others), and the timed
+steps start on the copies the warm-up touched longest ago.  Per-kernel launch
+durations for the roofline figure are measured the same way (a graph of at
+least 32 launches of one kernel, over enough copies that the kernel's own
+buffers span 1 GiB), with HIP events on the stream the graph is replayed on;
+the roofline names the kernel of the step that takes the longest.  The CPU
+oracle is timed on the host's cores on the same batch, as a reported baseline.
 
 Prints exactly one JSON line on stdout (progress goes to stderr).
 """
@@ -30,7 +33,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
-CPU_BUDGET_S = 10.0      # the CPU baseline runs full batches for about this long
+CPU_RUN_S = 3.0          # each CPU baseline run repeats full batches for about this long
+CPU_MAX_THREADS = 16     # the host share of one GPU on the box
 ROTATE_BYTES = 1 << 30
 ROTATE_CAP = 48 << 30    # device memory the rotated copies may take in all
 ROTATE_MAX_SETS = 512
@@ -45,6 +49,8 @@ CSRC = os.path.join(ROOT, "segmented_rank_gemm_amd", "csrc")
 KERNEL_SOURCES = {
     "lora_expand": ["expand.hip", "device_common.hpp"],
     "lora_shrink": ["shrink.hip", "device_common.hpp", "metadata_group.hpp"],
+    "lora_prepare_metadata": ["metadata.hip", "device_common.hpp", "metadata_group.hpp"],
+    "lora_fused_step": ["token_step.hip", "device_common.hpp", "metadata_group.hpp"],
 }
 
 
@@ -109,7 +115,7 @@ class Sets:
         import torch
 
         import segmented_rank_gemm_amd as srg
-        from tests.gpu_harness import to_dev_bf16
+        from workloads.device import to_dev_bf16
 
         self.w, self.R, self.num_splits = w, R, num_splits
         T, maxT = w.num_tokens, w.max_tokens
@@ -123,6 +129,9 @@ class Sets:
         self.base = base
         self.sets = []
         self.T = T
+        # one workspace serves every copy: the calls are ordered on one stream
+        self.workspace = srg.fused_step_workspace(maxT, w.max_loras, w.num_slices, w.rank)
+        self.one_launch = self.workspace is not None
         self.grow(R)
 
     def grow(self, R):
@@ -175,8 +184,21 @@ class Sets:
         srg.lora_shrink(s["x"], s["a"], float(self.w.scale), s["buf"], self.num_splits, m, stream)
         srg.lora_expand(s["buf"], self.num_splits, s["b"], s["y"], m, stream)
 
+    def fused(self, r, stream=None, meta_r=None):
+        """The whole path in one call (lora_fused_step), writing copy meta_r's
+        metadata (default: copy r's)."""
+        import segmented_rank_gemm_amd as srg
+        s = self.sets[r]
+        m = s["meta"] if meta_r is None else self.sets[meta_r]["meta"]
+        srg.lora_fused_step(s["mapping"], self.T, s["x"], s["a"], s["b"], float(self.w.scale),
+                            s["buf"], self.num_splits, s["y"], m, self.workspace, stream=stream)
+
     def step(self, r, stream=None):
-        """The whole path: metadata + shrink (one call) and expand."""
+        """The whole path: lora_fused_step."""
+        self.fused(r, stream)
+
+    def step2(self, r, stream=None):
+        """The whole path as lora_prepare_and_shrink + lora_expand."""
         self.prep_shrink(r, stream)
         self.expand(r, stream)
 
@@ -240,19 +262,30 @@ def time_graph(g, reps):
     return start.elapsed_time(end) / 1e3 / reps
 
 
-def cpu_baseline(w):
-    import numpy as np
-
+def _cpu_run(w, threads, min_s):
+    """Full oracle batches (metadata + shrink + expand, fp64) repeated for at
+    least min_s seconds (and at least one batch): tokens per second."""
     import oracle
-    threads = min(16, os.cpu_count() or 1)
-    oracle.run_step(w, num_threads=threads)  # warm-up
     n, t0 = 0, time.perf_counter()
     while True:
         oracle.run_step(w, num_threads=threads)
         n += 1
         el = time.perf_counter() - t0
-        if el >= CPU_BUDGET_S or (n >= 1 and el * (n + 1) / n > 3 * CPU_BUDGET_S):
-            break
+        if el >= min_s:
+            return w.num_tokens * n / el, n, el
+
+
+def cpu_baseline(w):
+    """The oracle on the host: median of 3 runs on the threads the box gives one
+    GPU (at most 16, fewer if the process may use fewer cores), after a warm-up,
+    and one single-thread run."""
+    import oracle
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    threads = max(1, min(CPU_MAX_THREADS, avail))
+    oracle.run_step(w, num_threads=threads)  # warm-up
+    runs = [_cpu_run(w, threads, CPU_RUN_S) for _ in range(3)]
+    rates = sorted(r[0] for r in runs)
+    single = _cpu_run(w, 1, CPU_RUN_S)
     model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -261,9 +294,14 @@ def cpu_baseline(w):
                 break
     except OSError:
         pass
-    return dict(value=w.num_tokens * n / el, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"{n} full batches of {w.num_tokens} tokens (metadata+shrink+expand, fp64) "
-                       f"in {el:.1f} s; {model}".strip())
+    batches = sum(r[1] for r in runs)
+    secs = sum(r[2] for r in runs)
+    return dict(value=rates[1], unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"3 runs of full batches of {w.num_tokens} tokens (metadata+shrink+expand, "
+                       f"fp64), {batches} batches in {secs:.1f} s, median of the three; "
+                       f"{model}".strip(),
+                runs_tokens_per_s=rates, single_thread_tokens_per_s=single[0],
+                host_cores_visible=os.cpu_count(), cores_usable=avail)
 
 
 def run_config(idx, args):
@@ -300,20 +338,27 @@ def run_config(idx, args):
     torch.cuda.synchronize()
 
     G = R * max(1, math.ceil(MIN_GRAPH_STEPS / R))  # steps per graph, copies in turn
-    g_step = capture([lambda s, r=r: sets.step(r % R, s) for r in range(G)])
     steps = args.steps if args.steps is not None else R * 200
     warm = args.warmup if args.warmup is not None else R * 20
+    # warm-up on copies 0, 1, ...; the timed steps start where the warm-up
+    # stopped, so with fewer steps than copies none of them reuses a copy the
+    # warm-up has just brought into the caches
+    off = warm % R
+    g_warm = capture([lambda s, r=r: sets.step(r % R, s) for r in range(G)])
+    g_step = capture([lambda s, r=r: sets.step((off + r) % R, s) for r in range(G)])
     full, rem = divmod(steps, G)
-    g_rem = capture([lambda s, r=r: sets.step(r % R, s) for r in range(rem)]) if rem else None
+    g_rem = (capture([lambda s, r=r: sets.step((off + full * G + r) % R, s) for r in range(rem)])
+             if rem else None)
     wfull, wrem = divmod(warm, G)
     log(f"[bench] warmup {warm} steps")
     for _ in range(wfull):
-        g_step.replay()
+        g_warm.replay()
     if wrem:
         capture([lambda s, r=r: sets.step(r % R, s) for r in range(wrem)]).replay()
     torch.cuda.synchronize()
+    del g_warm
 
-    log(f"[bench] timing {steps} steps")
+    log(f"[bench] timing {steps} steps from copy {off}")
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -328,6 +373,7 @@ def run_config(idx, args):
     wall = time.perf_counter() - t0
     gpu_s = start.elapsed_time(end) / 1e3
     step_s = wall / steps
+    del g_step, g_rem
 
     # single-kernel graphs: average launch duration of each kernel over enough
     # copies that the kernel's own buffers span ROTATE_BYTES (so the Infinity
@@ -340,14 +386,18 @@ def run_config(idx, args):
     # (--rotate fixes the copies for every kernel, e.g. for short counter runs)
     kb["prepare_and_shrink"] = kb["shrink"] + kb["metadata"]
     kb["step3"] = sb
-    rot = {k: (R if k in ("metadata", "step3") or args.rotate else rotation(kb[k], sb, R))
-           for k in kb}
+    kb["step2"] = sb
+    kb["fused_step"] = sb
+    rot = {k: (R if k in ("metadata", "step3", "step2", "fused_step") or args.rotate
+               else rotation(kb[k], sb, R)) for k in kb}
     sets.grow(max(rot.values()))
     per = {}
     fns = {"metadata": sets.metadata, "shrink": sets.shrink, "expand": sets.expand,
-           "prepare_and_shrink": sets.prep_shrink,
-           "pair": lambda r, s: (sets.shrink(r, s), sets.expand(r, s)), "step3": sets.step3}
-    for name in ("metadata", "shrink", "prepare_and_shrink", "expand", "pair", "step3"):
+           "prepare_and_shrink": sets.prep_shrink, "fused_step": sets.fused,
+           "pair": lambda r, s: (sets.shrink(r, s), sets.expand(r, s)), "step3": sets.step3,
+           "step2": sets.step2}
+    for name in ("metadata", "shrink", "prepare_and_shrink", "expand", "fused_step", "pair",
+                 "step2", "step3"):
         n = rot[name]
         m = n * max(1, math.ceil(MIN_GRAPH_LAUNCHES / n))  # launch groups per graph
         g = capture([lambda s, r=r, f=fns[name]: f(r % n, s) for r in range(m)])
@@ -355,11 +405,14 @@ def run_config(idx, args):
         del g
     pair_s = per.pop("pair")
     step3_s = per.pop("step3")
+    step2_s = per.pop("step2")
 
     # layer stack: one metadata step serves a model's L LoRA layers of this
     # shape, each with its own weights, activations and outputs.  Stacks are
     # rotated like the steps (each stack takes L copies and computes its
-    # metadata on its first), so that the buffers span ROTATE_BYTES.
+    # metadata on its first).  One-launch sizes: every layer is a
+    # lora_fused_step; otherwise the first layer groups the batch in its
+    # lora_prepare_and_shrink and the others run lora_shrink + lora_expand on it.
     stack = None
     L = args.layers
     if L > 0:
@@ -369,15 +422,18 @@ def run_config(idx, args):
         calls = []
         for k in range(K):
             m = k * L
-            # the first layer groups the batch in its shrink call; the others reuse it
-            calls.append(lambda s, m=m: (sets.prep_shrink(m, s), sets.expand(m, s)))
-            calls += [lambda s, r=m + l, m=m: sets.layer(r, m, s) for l in range(1, L)]
+            if sets.one_launch:
+                calls += [lambda s, r=m + l, m=m: sets.fused(r, s, meta_r=m) for l in range(L)]
+            else:
+                calls.append(lambda s, m=m: (sets.prep_shrink(m, s), sets.expand(m, s)))
+                calls += [lambda s, r=m + l, m=m: sets.layer(r, m, s) for l in range(1, L)]
         g = capture(calls)
         t_stack = time_graph(g, max(2, reps // 10)) / K
         del g
         stack = {
             "layers": L, "rotated_stacks": K, "us": t_stack * 1e6, "us_per_layer": t_stack / L * 1e6,
-            "metadata_share": per["metadata"] / t_stack,
+            "calls": ("lora_fused_step per layer" if sets.one_launch else
+                      "lora_prepare_and_shrink + lora_expand, then lora_shrink + lora_expand"),
             "layer_tokens_per_s": w.num_tokens * L / t_stack,
         }
 
@@ -393,8 +449,19 @@ def run_config(idx, args):
     upd_s = time_graph(g_upd, reps) / Rc
     del g_copy, g_upd, srcs, dsts
 
-    exp_bytes = st["expand_bytes"]
-    achieved = exp_bytes / per["expand"] / 1e9
+    # the kernels of the step with their algorithmic bytes per launch; the
+    # roofline is that of the one that takes the longest
+    if sets.one_launch:
+        step_kernels = {"lora_fused_step": (per["fused_step"], st["total_bytes"])}
+    else:
+        step_kernels = {
+            "lora_prepare_metadata": (per["metadata"], st["index_bytes"]),
+            "lora_shrink": (per["shrink"], st["shrink_bytes"]),
+            "lora_expand": (per["expand"], st["expand_bytes"]),
+        }
+    dom = max(step_kernels, key=lambda k: step_kernels[k][0])
+    dom_s, dom_bytes = step_kernels[dom]
+    achieved = dom_bytes / dom_s / 1e9
     out = {
         "metric": "fused shrink+expand tokens/s and achieved HBM GB/s (% of peak), "
                   "Llama-2-7B qkv r=8",
@@ -418,21 +485,27 @@ def run_config(idx, args):
             "rotated_sets": R, "rotated_sets_per_kernel": rot, "parallelism": "single GPU",
         },
         "roofline": {
-            "bound": "hbm", "kernel": "lora_expand", "achieved": achieved,
+            "bound": "hbm", "kernel": dom, "achieved": achieved,
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic("lora_expand", CONFIGS[idx]["name"]),
-            "algorithmic_bytes_per_launch": exp_bytes,
-            "avg_launch_us": per["expand"] * 1e6,
-            "frac_of_update_ceiling": achieved / (2 * cb / upd_s / 1e9),
+            "traffic": measured_traffic(dom, CONFIGS[idx]["name"]),
+            "algorithmic_bytes_per_launch": dom_bytes,
+            "avg_launch_us": dom_s * 1e6,
+            "step_kernels_us": {k: v[0] * 1e6 for k, v in step_kernels.items()},
         },
         "step": {
-            "calls": "lora_prepare_and_shrink + lora_expand",
+            "calls": "lora_fused_step",
+            "launches": ("one" if sets.one_launch else
+                         "lora_prepare_and_shrink (one or two kernels) + lora_expand"),
             "gpu_event_ms_per_step": gpu_s / steps * 1e3,
             "algorithmic_bytes": st["total_bytes"],
             "achieved_GBs": st["total_bytes"] / step_s / 1e9,
             "frac_of_peak": st["total_bytes"] / step_s / 1e9 / HBM_PEAK_GBS,
         },
         "kernels_us": {k: v * 1e6 for k, v in per.items()},
+        "step_two_calls": {
+            "calls": "lora_prepare_and_shrink + lora_expand",
+            "us": step2_s * 1e6, "tokens_per_s": w.num_tokens / step2_s,
+        },
         "step_three_calls": {
             "calls": "lora_prepare_metadata + lora_shrink + lora_expand",
             "us": step3_s * 1e6, "tokens_per_s": w.num_tokens / step3_s,

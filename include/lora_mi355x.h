@@ -28,8 +28,8 @@
  *   - Every pointer is a DEVICE pointer unless marked "host".  All memory is
  *     owned by the caller.  No call allocates, frees, synchronises or keeps
  *     state between calls; host arrays are read only during the call.
- *   - Every call enqueues one kernel on `stream` (lora_prepare_and_shrink: one
- *     or two, see there) and returns without waiting.  Launch grids depend
+ *   - Every call enqueues one kernel on `stream` (lora_prepare_and_shrink and
+ *     lora_fused_step: one or more, see there) and returns without waiting.  Launch grids depend
  *     only on the size arguments (max_tokens, max_loras, shapes), never on
  *     device data, so a sequence of calls can be
  *     captured once into a HIP graph and replayed.
@@ -217,11 +217,14 @@ lora_status_t lora_shrink(const uint16_t *x, int64_t ldx, int32_t hidden,
  * checks.  Writes exactly what the two calls write, bit for bit (meta in
  * full, buf rows of tokens with an adapter).
  *
- * With max_tokens <= 512 and max_loras <= 16 one kernel is enqueued: its
- * first workgroups do the shrink, finding each tile's tokens from the map
- * themselves, and the last max_loras + 1 workgroups compute the metadata.
- * Other sizes enqueue the metadata kernel and the shrink one after the other.  The grid still depends
- * only on the sizes, so the call can be captured in a graph.
+ * With max_tokens <= 512 one kernel is enqueued when max_loras * num_slices *
+ * rank <= 256 (the shrink then takes tiles of 16 consecutive tokens in batch
+ * order and the outputs of every adapter slot, each token keeping its own
+ * adapter's) or max_loras <= 16 (the shrink finds each grouped tile's tokens
+ * from the map itself); the last max_loras + 1 workgroups compute the
+ * metadata.  Other sizes enqueue the metadata kernel and the shrink one after
+ * the other.  The grid still depends only on the sizes, so the call can be
+ * captured in a graph.
  */
 lora_status_t lora_prepare_and_shrink(const int32_t *token_lora_mapping, int32_t num_tokens,
                                       const uint16_t *x, int64_t ldx, int32_t hidden,
@@ -257,6 +260,56 @@ lora_status_t lora_expand(const float *buf, int32_t num_splits, const uint16_t *
                           const int32_t *slice_sizes, int32_t num_slices, int32_t rank,
                           uint16_t *y, int64_t ldy, const lora_meta_t *meta, int32_t max_tokens,
                           int32_t max_loras, hipStream_t stream);
+
+/*
+ * lora_fused_step - the whole step for one batch (lora_prepare_metadata,
+ * lora_shrink, lora_expand), in one launch where the sizes allow it.
+ *
+ * Defined by: the passages cited for the three calls (vLLM PR #13096, "Why do
+ * we need a new set of kernels" and "Kernel Code Change" items 1 and 2; the
+ * shrink and expand kernels of its summary) and the MLC-LLM issue's Overview:
+ * Punica's single launch over every segment of the batch.
+ *
+ * Arguments: those of lora_prepare_metadata, lora_shrink and lora_expand for
+ * the same batch (same meanings and checks), plus
+ *   workspace        device memory of at least
+ *                    lora_fused_step_workspace_bytes(...) bytes, 256-byte
+ *                    aligned, ZERO-FILLED before its first use; every call
+ *                    leaves it zero-filled again once it has completed.  May
+ *                    be NULL when that size is 0.  Two calls that overlap in
+ *                    time must not share a workspace (one stream, or one
+ *                    workspace per stream).
+ *   workspace_bytes  its size.
+ *   options          host pointer, may be NULL (defaults).
+ * Writes what the three calls write: meta in full, buf (num_splits parts) at
+ * rows of tokens with an adapter, y at those rows and columns [0, sum n).
+ *
+ * One launch when max_tokens <= 512, rank is 8 or 16, max_loras * rank <= 64
+ * and max_loras * num_slices * rank <= 256 (lora_fused_step_workspace_bytes
+ * is then non-zero): tiles of 16 consecutive tokens in batch order; the
+ * shrink's workgroups hand each tile's parts to the expand's through the
+ * workspace's integer counters (bounded waits, no floating-point atomics; the
+ * results are the same bits on every run).  Other sizes: lora_prepare_and_shrink
+ * then lora_expand, and the workspace is not touched.
+ */
+typedef struct lora_step_options {
+  /* Upper bound on the polls of each cross-workgroup wait; a workgroup that
+   * reaches it computes the missing parts itself (same bits, more time).
+   * Negative: the default (65536).  0: never wait. */
+  int32_t wait_polls;
+} lora_step_options_t;
+
+int64_t lora_fused_step_workspace_bytes(int32_t max_tokens, int32_t max_loras,
+                                        int32_t num_slices, int32_t rank);
+
+lora_status_t lora_fused_step(const int32_t *token_lora_mapping, int32_t num_tokens,
+                              const uint16_t *x, int64_t ldx, int32_t hidden,
+                              const uint16_t *const *lora_a, const uint16_t *const *lora_b,
+                              const int32_t *slice_sizes, int32_t num_slices, int32_t rank,
+                              float scale, float *buf, int32_t num_splits, uint16_t *y,
+                              int64_t ldy, const lora_meta_t *meta, void *workspace,
+                              int64_t workspace_bytes, const lora_step_options_t *options,
+                              int32_t max_tokens, int32_t max_loras, hipStream_t stream);
 
 /* lora_status_string - static, human-readable name of a status code. */
 const char *lora_status_string(lora_status_t status);

@@ -21,7 +21,8 @@ import torch  # noqa: F401  (must precede loading the library, see above)
 
 __all__ = [
     "LIB_PATH", "LoraError", "LoraMeta", "lib", "lora_prepare_metadata", "lora_shrink",
-    "lora_prepare_and_shrink",
+    "lora_prepare_and_shrink", "lora_fused_step", "lora_fused_step_workspace_bytes",
+    "fused_step_workspace",
     "lora_shrink_default_splits", "lora_expand", "lora_stream_copy", "lora_stream_update",
     "lora_status_string",
     "LORA_MAX_LORAS", "LORA_MAX_SLICES", "LORA_MAX_SPLITS", "SUPPORTED_RANKS",
@@ -51,6 +52,10 @@ class _MetaStruct(ctypes.Structure):
                 ("num_active", ctypes.c_void_p), ("tile_token_ids", ctypes.c_void_p),
                 ("tile_lora", ctypes.c_void_p), ("num_tiles", ctypes.c_void_p),
                 ("num_runs", ctypes.c_void_p)]
+
+class _StepOptions(ctypes.Structure):
+    _fields_ = [("wait_polls", ctypes.c_int32)]
+
 
 TILE = 16  # positions per tile of the padded grouped order (LORA_TILE)
 
@@ -90,6 +95,13 @@ def lib() -> ctypes.CDLL:
         L.lora_expand.argtypes = [_VP, _I32, ctypes.POINTER(_VP), ctypes.POINTER(_I32), _I32, _I32,
                                   _VP, _I64, MP, _I32, _I32, _VP]
         L.lora_expand.restype = ctypes.c_int
+        L.lora_fused_step_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32]
+        L.lora_fused_step_workspace_bytes.restype = _I64
+        L.lora_fused_step.argtypes = [_VP, _I32, _VP, _I64, _I32, ctypes.POINTER(_VP),
+                                      ctypes.POINTER(_VP), ctypes.POINTER(_I32), _I32, _I32,
+                                      ctypes.c_float, _VP, _I32, _VP, _I64, MP, _VP, _I64,
+                                      ctypes.POINTER(_StepOptions), _I32, _I32, _VP]
+        L.lora_fused_step.restype = ctypes.c_int
         L.lora_stream_copy.argtypes = [_VP, _VP, _I64, _VP]
         L.lora_stream_copy.restype = ctypes.c_int
         L.lora_stream_update.argtypes = [_VP, _I64, _VP]
@@ -227,10 +239,8 @@ def lora_prepare_and_shrink(token_lora_mapping: torch.Tensor, num_tokens: int, x
         meta.struct_ref, meta.max_tokens, meta.max_loras, _stream_handle(stream)))
 
 
-def lora_expand(buf: torch.Tensor, num_splits: int, lora_b: Sequence[torch.Tensor], y: torch.Tensor,
-                meta: LoraMeta, stream: Optional[torch.cuda.Stream] = None) -> None:
-    """buf: fp32 [num_splits, S, max_tokens, rank]; lora_b[s]: bf16 [max_loras, n_s, rank];
-    y: bf16 [>=max_tokens, >=sum(n_s)] (row stride y.stride(0)), updated in place."""
+def _expand_args(buf: torch.Tensor, num_splits: int, lora_b: Sequence[torch.Tensor],
+                 y: torch.Tensor, meta: LoraMeta):
     S = len(lora_b)
     if S < 1:
         raise ValueError("lora_b must hold at least one slice")
@@ -247,22 +257,81 @@ def lora_expand(buf: torch.Tensor, num_splits: int, lora_b: Sequence[torch.Tenso
             raise ValueError("lora_b[s] must be contiguous [max_loras, n_s, rank]")
     bptrs = (_VP * S)(*[_dev_ptr(b, torch.bfloat16, "lora_b") for b in lora_b])
     nsz = (_I32 * S)(*sizes)
+    return S, rank, bptrs, nsz
+
+
+def lora_fused_step_workspace_bytes(max_tokens: int, max_loras: int, num_slices: int,
+                                    rank: int) -> int:
+    """Bytes of zero-filled workspace lora_fused_step needs (0: none, the sizes
+    take the multi-launch path)."""
+    return int(lib().lora_fused_step_workspace_bytes(max_tokens, max_loras, num_slices, rank))
+
+
+def fused_step_workspace(max_tokens: int, max_loras: int, num_slices: int, rank: int,
+                         device="cuda") -> Optional[torch.Tensor]:
+    """A zero-filled workspace for lora_fused_step (None when none is needed).
+    torch's allocations are 256-byte aligned."""
+    n = lora_fused_step_workspace_bytes(max_tokens, max_loras, num_slices, rank)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def lora_fused_step(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.Tensor,
+                    lora_a: Sequence[torch.Tensor], lora_b: Sequence[torch.Tensor], scale: float,
+                    buf: torch.Tensor, num_splits: int, y: torch.Tensor, meta: LoraMeta,
+                    workspace: Optional[torch.Tensor], wait_polls: Optional[int] = None,
+                    stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Metadata, shrink and expand of one batch (one launch where the sizes
+    allow); arguments as for lora_prepare_and_shrink and lora_expand, plus the
+    zero-filled workspace of fused_step_workspace (reused call after call)."""
+    ptr = _mapping_ptr(token_lora_mapping, num_tokens)
+    S, rank, hidden, aptrs = _shrink_args(x, lora_a, buf, num_splits, meta)
+    Sb, rank_b, bptrs, nsz = _expand_args(buf, num_splits, lora_b, y, meta)
+    if Sb != S or rank_b != rank:
+        raise ValueError("lora_a and lora_b disagree on slices or rank")
+    wptr, wbytes = 0, 0
+    if workspace is not None:
+        wptr, wbytes = _flat_dev_bytes(workspace, "workspace")
+    opts = None
+    if wait_polls is not None:
+        opts = ctypes.byref(_StepOptions(int(wait_polls)))
+    _check("lora_fused_step", lib().lora_fused_step(
+        ptr, int(num_tokens), _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), hidden, aptrs,
+        bptrs, nsz, S, rank, float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits),
+        _dev_ptr(y, torch.bfloat16, "y"), int(y.stride(0)), meta.struct_ref, wptr, int(wbytes),
+        opts, meta.max_tokens, meta.max_loras, _stream_handle(stream)))
+
+
+def lora_expand(buf: torch.Tensor, num_splits: int, lora_b: Sequence[torch.Tensor], y: torch.Tensor,
+                meta: LoraMeta, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """buf: fp32 [num_splits, S, max_tokens, rank]; lora_b[s]: bf16 [max_loras, n_s, rank];
+    y: bf16 [>=max_tokens, >=sum(n_s)] (row stride y.stride(0)), updated in place."""
+    S, rank, bptrs, nsz = _expand_args(buf, num_splits, lora_b, y, meta)
     _check("lora_expand", lib().lora_expand(
         _dev_ptr(buf, torch.float32, "buf"), int(num_splits), bptrs, nsz, S, rank,
         _dev_ptr(y, torch.bfloat16, "y"), int(y.stride(0)), meta.struct_ref, meta.max_tokens,
         meta.max_loras, _stream_handle(stream)))
 
 
+def _flat_dev_bytes(t: torch.Tensor, name: str):
+    """Device address and byte size of a contiguous device tensor (any dtype)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return int(t.data_ptr()), t.numel() * t.element_size()
+
+
 def lora_stream_copy(src: torch.Tensor, dst: torch.Tensor,
                      stream: Optional[torch.cuda.Stream] = None) -> None:
-    nbytes = src.numel() * src.element_size()
-    if dst.numel() * dst.element_size() < nbytes:
+    """Copy all of src into the first bytes of dst (both contiguous device tensors)."""
+    sp, nbytes = _flat_dev_bytes(src, "src")
+    dp, dbytes = _flat_dev_bytes(dst, "dst")
+    if dbytes < nbytes:
         raise ValueError("dst smaller than src")
-    _check("lora_stream_copy", lib().lora_stream_copy(int(src.data_ptr()), int(dst.data_ptr()),
-                                                      int(nbytes), _stream_handle(stream)))
+    _check("lora_stream_copy", lib().lora_stream_copy(sp, dp, int(nbytes), _stream_handle(stream)))
 
 
 def lora_stream_update(buf: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
-    nbytes = buf.numel() * buf.element_size()
-    _check("lora_stream_update", lib().lora_stream_update(int(buf.data_ptr()), int(nbytes),
-                                                          _stream_handle(stream)))
+    """Read, change and write back every byte of buf (a contiguous device tensor)."""
+    bp, nbytes = _flat_dev_bytes(buf, "buf")
+    _check("lora_stream_update", lib().lora_stream_update(bp, int(nbytes), _stream_handle(stream)))

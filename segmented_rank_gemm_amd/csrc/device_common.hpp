@@ -13,6 +13,13 @@ namespace lora {
 
 constexpr int kWave = 64;
 
+// Shrink work split (shared by every shrink kernel, so that a part's partial
+// sums are the same bits whichever kernel computes them): 256-thread
+// workgroups whose four waves take interleaved 64-element chunks of a part.
+constexpr int kShrinkThreads = 256;
+constexpr int kShrinkWaves = kShrinkThreads / kWave;
+constexpr int kShrinkChunk = 64;  // hidden elements per wave step (two MFMA K-steps)
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -42,6 +49,29 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p) {
 }
 __device__ __forceinline__ void store16_stream(void* p, u32x4 v) {
   __builtin_nontemporal_store(v, (LORA_GLOBAL u32x4*)(p));
+}
+
+// Device-coherent 16-byte accesses, for data that one workgroup of a launch
+// hands to another: the store is written through to the level every XCD shares
+// (each XCD has its own L2) and the load is served from there, never from a
+// stale line of the reading XCD's L2 (cache policy sc1, the code the compiler
+// emits for agent-scope atomic loads and stores, here on 16 bytes at once).
+// Offsets are bytes from the resource's base; an access past `bytes` is
+// dropped (store) or reads zero (load).  Word 3 is the gfx9 raw-buffer format.
+constexpr int kCachePolicyCoherent = 16;  // sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 load16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyCoherent);
+}
+__device__ __forceinline__ u32x2 load8_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCachePolicyCoherent);
+}
+__device__ __forceinline__ void store16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCachePolicyCoherent);
 }
 
 // Low / high bf16 of a packed pair, widened exactly to fp32.

@@ -29,6 +29,14 @@ hipError_t launch_prep_shrink(const int32_t* mapping, int num_tokens, const uint
                               int num_slices, int rank, float scale, float* buf, int num_splits,
                               const lora_meta_t& meta, int max_tokens, int max_loras,
                               int num_cus, hipStream_t stream);
+bool token_step_fits(int max_tokens, int max_loras, int num_slices, int rank);
+int64_t token_step_workspace_bytes(int max_tokens);
+hipError_t launch_token_step(const int32_t* mapping, int num_tokens, const uint16_t* x,
+                             int64_t ldx, int hidden, const uint16_t* const* lora_a,
+                             const uint16_t* const* lora_b, const int32_t* slice_sizes,
+                             int num_slices, int rank, float scale, float* buf, int num_splits,
+                             uint16_t* y, int64_t ldy, const lora_meta_t& meta, int* counters,
+                             int wait_polls, int max_tokens, int max_loras, hipStream_t stream);
 int shrink_group_blocks(int nb_total);
 int shrink_tile_blocks(int max_tokens, int nb);
 }  // namespace lora
@@ -199,6 +207,69 @@ lora_status_t lora_expand(const float* buf, int32_t num_splits, const uint16_t* 
   return launch_status(lora::launch_expand(buf, num_splits, lora_b, slice_sizes, num_slices, rank,
                                            y, ldy, *meta, max_tokens, max_loras, current_cus(),
                                            stream));
+}
+
+int64_t lora_fused_step_workspace_bytes(int32_t max_tokens, int32_t max_loras,
+                                        int32_t num_slices, int32_t rank) {
+  if (!sizes_ok(max_tokens, max_loras) || num_slices < 1 || num_slices > LORA_MAX_SLICES)
+    return 0;
+  if (!lora::token_step_fits(max_tokens, max_loras, num_slices, rank)) return 0;
+  return lora::token_step_workspace_bytes(max_tokens);
+}
+
+// Checks of lora_expand's arguments other than meta and the sizes.
+static lora_status_t expand_args(const float* buf, int32_t num_splits,
+                                 const uint16_t* const* lora_b, const int32_t* slice_sizes,
+                                 int32_t num_slices, int32_t rank, const uint16_t* y, int64_t ldy) {
+  if (!buf || !lora_b || !slice_sizes || !y || !aligned16(buf) || !aligned16(y))
+    return LORA_ERR_INVALID_ARGUMENT;
+  if (num_slices < 1 || num_slices > LORA_MAX_SLICES) return LORA_ERR_INVALID_ARGUMENT;
+  if (num_splits < 1 || num_splits > LORA_MAX_SPLITS) return LORA_ERR_INVALID_ARGUMENT;
+  if (rank < 1 || rank > 64) return LORA_ERR_INVALID_ARGUMENT;
+  int64_t n_total = 0;
+  for (int32_t s = 0; s < num_slices; ++s) {
+    if (!lora_b[s] || !aligned16(lora_b[s])) return LORA_ERR_INVALID_ARGUMENT;
+    if (slice_sizes[s] < 8 || slice_sizes[s] % 8 != 0) return LORA_ERR_INVALID_ARGUMENT;
+    n_total += slice_sizes[s];
+  }
+  if (n_total > (int64_t{1} << 30) || ldy < n_total || ldy % 8 != 0)
+    return LORA_ERR_INVALID_ARGUMENT;
+  if (!rank_supported(rank)) return LORA_ERR_UNSUPPORTED;
+  return LORA_OK;
+}
+
+lora_status_t lora_fused_step(const int32_t* token_lora_mapping, int32_t num_tokens,
+                              const uint16_t* x, int64_t ldx, int32_t hidden,
+                              const uint16_t* const* lora_a, const uint16_t* const* lora_b,
+                              const int32_t* slice_sizes, int32_t num_slices, int32_t rank,
+                              float scale, float* buf, int32_t num_splits, uint16_t* y,
+                              int64_t ldy, const lora_meta_t* meta, void* workspace,
+                              int64_t workspace_bytes, const lora_step_options_t* options,
+                              int32_t max_tokens, int32_t max_loras, hipStream_t stream) {
+  if (!meta_ok(meta) || !sizes_ok(max_tokens, max_loras)) return LORA_ERR_INVALID_ARGUMENT;
+  if (num_tokens < 0 || num_tokens > max_tokens) return LORA_ERR_INVALID_ARGUMENT;
+  if (num_tokens > 0 && !token_lora_mapping) return LORA_ERR_INVALID_ARGUMENT;
+  lora_status_t st = shrink_args(x, ldx, hidden, lora_a, num_slices, rank, buf, num_splits, meta,
+                                 max_tokens, max_loras);
+  if (st != LORA_OK) return st;
+  st = expand_args(buf, num_splits, lora_b, slice_sizes, num_slices, rank, y, ldy);
+  if (st != LORA_OK) return st;
+  const int64_t need = lora_fused_step_workspace_bytes(max_tokens, max_loras, num_slices, rank);
+  if (need > 0) {
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+        workspace_bytes < need)
+      return LORA_ERR_INVALID_ARGUMENT;
+    const int polls = options && options->wait_polls >= 0 ? options->wait_polls : 65536;
+    return launch_status(lora::launch_token_step(
+        token_lora_mapping, num_tokens, x, ldx, hidden, lora_a, lora_b, slice_sizes, num_slices,
+        rank, scale, buf, num_splits, y, ldy, *meta, static_cast<int*>(workspace), polls,
+        max_tokens, max_loras, stream));
+  }
+  st = lora_prepare_and_shrink(token_lora_mapping, num_tokens, x, ldx, hidden, lora_a, num_slices,
+                               rank, scale, buf, num_splits, meta, max_tokens, max_loras, stream);
+  if (st != LORA_OK) return st;
+  return lora_expand(buf, num_splits, lora_b, slice_sizes, num_slices, rank, y, ldy, meta,
+                     max_tokens, max_loras, stream);
 }
 
 lora_status_t lora_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {

@@ -31,9 +31,6 @@
 
 namespace lora {
 
-constexpr int kShrinkThreads = 256;
-constexpr int kShrinkWaves = kShrinkThreads / kWave;
-constexpr int kShrinkChunk = 64;  // hidden elements per wave step (two MFMA K-steps)
 constexpr int kMaxFusedLoras = 16;  // adapter slots the fused prepare + shrink serves
 constexpr int kMaxFusedGroups = kMaxFusedLoras + 1;
 
@@ -680,11 +677,23 @@ hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_token
 // shrink workgroups loop over the groups): one fused launch.  Otherwise the
 // metadata kernel, then the shrink.
 
+bool token_shrink_fits(int max_tokens, int max_loras, int num_slices, int rank);
+hipError_t launch_token_prep_shrink(const int32_t* mapping, int num_tokens, const uint16_t* x,
+                                    int64_t ldx, int hidden, const uint16_t* const* lora_a,
+                                    int num_slices, int rank, float scale, float* buf,
+                                    int num_splits, const lora_meta_t& meta, int max_tokens,
+                                    int max_loras, hipStream_t stream);
+
 hipError_t launch_prep_shrink(const int32_t* mapping, int num_tokens, const uint16_t* x,
                               int64_t ldx, int hidden, const uint16_t* const* lora_a,
                               int num_slices, int rank, float scale, float* buf, int num_splits,
                               const lora_meta_t& meta, int max_tokens, int max_loras,
                               int num_cus, hipStream_t stream) {
+  // few adapter outputs: the shrink in batch order (token_step.hip), which
+  // needs no grouping before its loads
+  if (token_shrink_fits(max_tokens, max_loras, num_slices, rank))
+    return launch_token_prep_shrink(mapping, num_tokens, x, ldx, hidden, lora_a, num_slices, rank,
+                                    scale, buf, num_splits, meta, max_tokens, max_loras, stream);
   const int nb = shrink_nb(num_slices, rank);
   if (shrink_tile_blocks(max_tokens, nb) != 1 || max_tokens > kWave * kPerThread ||
       max_loras > kMaxFusedLoras) {

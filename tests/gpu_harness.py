@@ -10,17 +10,10 @@ from typing import List, Optional
 import numpy as np
 import torch
 
+import oracle
 import segmented_rank_gemm_amd as srg
 from workloads import f32_from_bf16_bits
-
-
-def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
-    a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
-    return torch.from_numpy(a).cuda().view(torch.bfloat16)
-
-
-def from_dev_bf16(t: torch.Tensor) -> np.ndarray:
-    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+from workloads.device import from_dev_bf16, to_dev_bf16  # noqa: F401
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -76,6 +69,13 @@ def run_step_fused(d: DeviceWorkload, stream=None) -> None:
     srg.lora_expand(d.buf, d.num_splits, d.lora_b, d.y, d.meta, stream)
 
 
+def run_step_single(d: DeviceWorkload, workspace, stream=None, wait_polls=None) -> None:
+    """The same step through lora_fused_step (one launch where the sizes allow)."""
+    srg.lora_fused_step(d.mapping, d.w.num_tokens, d.x, d.lora_a, d.lora_b, float(d.w.scale),
+                        d.buf, d.num_splits, d.y, d.meta, workspace, wait_polls=wait_polls,
+                        stream=stream)
+
+
 META_KEYS = ["sorted_token_ids", "active_lora_ids", "num_tokens_per_lora", "lora_token_start",
              "num_active", "tile_token_ids", "tile_lora", "num_tiles", "num_runs"]
 
@@ -115,3 +115,57 @@ def buf_sum(d: DeviceWorkload) -> np.ndarray:
     """Sum over the shrink's parts, in part order, in float64: [S, max_tokens, r]."""
     b = d.buf.cpu().numpy().astype(np.float64)
     return b.sum(axis=0)
+
+
+def sanitize(mapping, L):
+    m = np.asarray(mapping, dtype=np.int64)
+    return np.where((m >= -1) & (m < L), m, -1)
+
+
+def check_meta(meta_gpu, ref, T, max_tokens, sorted_fill=-7, mapping=None, L=None):
+    assert np.array_equal(meta_gpu["sorted_token_ids"][:T], ref["sorted_token_ids"])
+    assert np.all(meta_gpu["sorted_token_ids"][T:max_tokens] == sorted_fill)
+    for k in META_KEYS[1:5]:
+        assert np.array_equal(meta_gpu[k], ref[k]), k
+    if mapping is not None:
+        # the padded tiles, bit for bit below num_tiles
+        tiles = oracle.prepare_tiles(mapping, L)
+        nt = int(tiles["num_tiles"][0])
+        assert int(meta_gpu["num_tiles"][0]) == nt
+        assert np.array_equal(meta_gpu["tile_token_ids"][:nt * 16], tiles["tile_token_ids"])
+        assert np.array_equal(meta_gpu["tile_lora"][:nt], tiles["tile_lora"])
+        assert np.array_equal(meta_gpu["num_runs"], oracle.count_runs(mapping, L))
+
+
+def full_check(w, d, literal=False):
+    T = w.num_tokens
+    ref = oracle.run_step(w)
+    check_meta(meta_host(d), ref, T, w.max_tokens, mapping=w.mapping[:T], L=w.max_loras)
+    ids = sanitize(w.mapping, w.max_loras)
+    act = ids >= 0
+    # shrink: sum of the parts against the fp64 projection (rows with an adapter)
+    bs = buf_sum(d)[:, :T]
+    if act.any():
+        b64 = ref["buf"][:, act]
+        brms = float(np.sqrt(np.mean(b64 * b64)))
+        berr = float(np.max(np.abs(bs[:, act] - b64)))
+        assert berr <= 1e-2 * brms + 1e-3, (berr, brms)
+    # expand
+    yg = from_dev_bf16(d.y)
+    rep = y_report(yg[:T, :w.n_total], ref["y64"][:, :w.n_total],
+                     ref["y_bf16"][:, :w.n_total])
+    assert rep["max_excess_over_half_ulp"] <= rep["tol"], rep
+    # rows without an adapter untouched, bit for bit; so are pad columns and rows >= T
+    assert np.array_equal(yg[:T][~act, :w.n_total], w.y0[:T][~act])
+    assert np.all(yg[:, w.n_total:] == 0x7FC1)
+    if w.max_tokens > T:
+        assert np.array_equal(yg[T:w.max_tokens, :w.n_total], w.y0[T:w.max_tokens])
+    # buf rows of tokens without an adapter keep their fill (NaN), in every part
+    braw = d.buf.cpu().numpy()
+    assert np.all(np.isnan(braw[:, :, :T][:, :, ~act]))
+    if literal:
+        print(f"\n[{w.name}] T={T} tol={rep['tol']:.4g} max_excess={rep['max_excess_over_half_ulp']:.3g} "
+              f"literal_over_tol(y64)={rep['literal_over_tol_vs_y64']} "
+              f"literal_over_tol(rne)={rep['literal_over_tol_vs_rne']} "
+              f"ulp_mismatch(rne)={rep['ulp_mismatch_vs_rne']}/{rep['n']}", flush=True)
+    return rep

@@ -182,3 +182,45 @@ def test_tuning_candidates():
         assert d in c
         assert all(1 <= v <= srg.LORA_MAX_SPLITS for v in c)
         assert all(v <= chunks for v in c if v != d)
+
+
+# ------------------------------------------------------------ lora_fused_step
+
+def test_fused_step_workspace_bytes():
+    # one 256-byte counter line per 16-token tile inside the one-launch domain, else none
+    assert srg.lora_fused_step_workspace_bytes(256, 4, 3, 8) == 16 * 256
+    assert srg.lora_fused_step_workspace_bytes(1, 1, 1, 8) == 256
+    assert srg.lora_fused_step_workspace_bytes(512, 8, 2, 8) == 32 * 256
+    assert srg.lora_fused_step_workspace_bytes(513, 4, 3, 8) == 0      # too many token slots
+    assert srg.lora_fused_step_workspace_bytes(256, 16, 1, 8) == 0     # max_loras * rank > 64
+    assert srg.lora_fused_step_workspace_bytes(256, 4, 3, 32) == 0     # rank 32
+    assert srg.lora_fused_step_workspace_bytes(256, 4, 4, 16) == 16 * 256  # 4*4*16 = 256 outputs
+    assert srg.lora_fused_step_workspace_bytes(256, 4, 4, 16) > 0
+    assert srg.lora_fused_step_workspace_bytes(0, 4, 3, 8) == 0         # invalid sizes
+    assert srg.lora_fused_step_workspace_bytes(256, 4, 5, 8) == 0
+
+
+def _fused(workspace=FAKE, workspace_bytes=1 << 20, options=None, **kw):
+    a = dict(map=FAKE, T=200, x=FAKE, ldx=4096, hidden=4096, S=3, rank=8, scale=1.0, buf=FAKE,
+             splits=16, y=FAKE, ldy=12288, maxT=256, L=4, meta=_meta(), n=4096)
+    a.update(kw)
+    sizes = (ctypes.c_int32 * a["S"])(*([a["n"]] * a["S"]))
+    return srg.lib().lora_fused_step(
+        a["map"], a["T"], a["x"], a["ldx"], a["hidden"], _ptrs(a["S"]), _ptrs(a["S"]), sizes,
+        a["S"], a["rank"], a["scale"], a["buf"], a["splits"], a["y"], a["ldy"], a["meta"],
+        workspace, workspace_bytes, options, a["maxT"], a["L"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(workspace=None), dict(workspace=FAKE + 16), dict(workspace_bytes=16 * 256 - 1),
+    dict(T=257), dict(T=-1), dict(map=None), dict(meta=_meta(num_runs=None)), dict(x=None),
+    dict(y=None), dict(buf=FAKE + 4), dict(ldy=4096), dict(n=12), dict(splits=0), dict(S=0),
+    dict(hidden=12),
+])
+def test_fused_step_rejects(kw):
+    assert _fused(**kw) == 1
+
+
+def test_fused_step_rejects_unsupported_rank():
+    # rank 12: valid range, no kernel for it (checked before anything is enqueued)
+    assert _fused(rank=12) == 2

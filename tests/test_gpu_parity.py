@@ -19,6 +19,9 @@ from workloads import (CONFIGS, make_custom_workload, make_fuzz_mapping,
 pytestmark = pytest.mark.gpu
 
 META_KEYS = H.META_KEYS
+_sanitize = H.sanitize
+_check_meta = H.check_meta
+_full_check = H.full_check
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -28,26 +31,6 @@ def _gpu():
     assert arch.startswith("gfx950"), arch
     yield
     torch.cuda.synchronize()
-
-
-def _sanitize(mapping, L):
-    m = np.asarray(mapping, dtype=np.int64)
-    return np.where((m >= -1) & (m < L), m, -1)
-
-
-def _check_meta(meta_gpu, ref, T, max_tokens, sorted_fill=-7, mapping=None, L=None):
-    assert np.array_equal(meta_gpu["sorted_token_ids"][:T], ref["sorted_token_ids"])
-    assert np.all(meta_gpu["sorted_token_ids"][T:max_tokens] == sorted_fill)
-    for k in META_KEYS[1:5]:
-        assert np.array_equal(meta_gpu[k], ref[k]), k
-    if mapping is not None:
-        # the padded tiles, bit for bit below num_tiles
-        tiles = oracle.prepare_tiles(mapping, L)
-        nt = int(tiles["num_tiles"][0])
-        assert int(meta_gpu["num_tiles"][0]) == nt
-        assert np.array_equal(meta_gpu["tile_token_ids"][:nt * 16], tiles["tile_token_ids"])
-        assert np.array_equal(meta_gpu["tile_lora"][:nt], tiles["tile_lora"])
-        assert np.array_equal(meta_gpu["num_runs"], oracle.count_runs(mapping, L))
 
 
 def _run_metadata(mapping, T, max_tokens, L):
@@ -90,40 +73,6 @@ def test_metadata_bit_exact_fuzz(T, maxT, L, kind):
 
 
 # --------------------------------------------------------- shrink + expand
-
-def _full_check(w, d, literal=False):
-    T = w.num_tokens
-    ref = oracle.run_step(w)
-    _check_meta(H.meta_host(d), ref, T, w.max_tokens, mapping=w.mapping[:T], L=w.max_loras)
-    ids = _sanitize(w.mapping, w.max_loras)
-    act = ids >= 0
-    # shrink: sum of the parts against the fp64 projection (rows with an adapter)
-    bs = H.buf_sum(d)[:, :T]
-    if act.any():
-        b64 = ref["buf"][:, act]
-        brms = float(np.sqrt(np.mean(b64 * b64)))
-        berr = float(np.max(np.abs(bs[:, act] - b64)))
-        assert berr <= 1e-2 * brms + 1e-3, (berr, brms)
-    # expand
-    yg = H.from_dev_bf16(d.y)
-    rep = H.y_report(yg[:T, :w.n_total], ref["y64"][:, :w.n_total],
-                     ref["y_bf16"][:, :w.n_total])
-    assert rep["max_excess_over_half_ulp"] <= rep["tol"], rep
-    # rows without an adapter untouched, bit for bit; so are pad columns and rows >= T
-    assert np.array_equal(yg[:T][~act, :w.n_total], w.y0[:T][~act])
-    assert np.all(yg[:, w.n_total:] == 0x7FC1)
-    if w.max_tokens > T:
-        assert np.array_equal(yg[T:w.max_tokens, :w.n_total], w.y0[T:w.max_tokens])
-    # buf rows of tokens without an adapter keep their fill (NaN), in every part
-    braw = d.buf.cpu().numpy()
-    assert np.all(np.isnan(braw[:, :, :T][:, :, ~act]))
-    if literal:
-        print(f"\n[{w.name}] T={T} tol={rep['tol']:.4g} max_excess={rep['max_excess_over_half_ulp']:.3g} "
-              f"literal_over_tol(y64)={rep['literal_over_tol_vs_y64']} "
-              f"literal_over_tol(rne)={rep['literal_over_tol_vs_rne']} "
-              f"ulp_mismatch(rne)={rep['ulp_mismatch_vs_rne']}/{rep['n']}", flush=True)
-    return rep
-
 
 REDUCED_T = [16, 200, 1000, 700, 900]
 
@@ -504,6 +453,17 @@ def test_prepare_and_shrink_matches_two_calls(T, maxT, hidden, slices, rank, L, 
     assert np.array_equal(m1["tile_lora"][:nt], m2["tile_lora"][:nt])
     assert np.array_equal(d1.buf.view(torch.int32).cpu().numpy(),
                           d2.buf.view(torch.int32).cpu().numpy())
+    # and the fused call's own result, expanded, against the oracle
+    _expand_and_check(w, d2)
+
+
+def _expand_and_check(w, d):
+    srg.lora_expand(d.buf, d.num_splits, d.lora_b, d.y, d.meta)
+    torch.cuda.synchronize()
+    if w.num_tokens == 0:
+        assert np.array_equal(H.from_dev_bf16(d.y)[:, :w.n_total], w.y0[:w.max_tokens])
+    else:
+        _full_check(w, d)
 
 
 def _fused_fuzz_cases(n=24, seed=2024):
@@ -547,6 +507,8 @@ def test_prepare_and_shrink_fuzz(T, maxT, hidden, slices, rank, L, kind, splits,
     assert np.array_equal(m1["tile_lora"][:nt], m2["tile_lora"][:nt])
     assert np.array_equal(d1.buf.view(torch.int32).cpu().numpy(),
                           d2.buf.view(torch.int32).cpu().numpy())
+    # and the fused call's own result, expanded, against the oracle
+    _expand_and_check(w, d2)
 
 
 @pytest.mark.parametrize("cfg", [0, 1])
