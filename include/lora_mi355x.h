@@ -311,6 +311,34 @@ lora_status_t lora_fused_step(const int32_t *token_lora_mapping, int32_t num_tok
                               int64_t workspace_bytes, const lora_step_options_t *options,
                               int32_t max_tokens, int32_t max_loras, hipStream_t stream);
 
+/*
+ * lora_fused_step_static - lora_fused_step without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture
+ * that must not call hipMalloc, tight serving loops, harnesses that forbid
+ * allocation).  Nothing is allocated: the one-launch path keeps its counters
+ * in a file-scope device array of the library, 8 KB, enough for its largest
+ * batch (512 token slots); each GPU the library runs on holds its own copy
+ * until the process ends.  The array is zero-filled when the library's code
+ * object is loaded and every call leaves it zero-filled again.  All calls on
+ * one GPU share that GPU's array: calls that overlap in time on one GPU (two
+ * streams, or two threads) race on it; order them on one stream.  The device
+ * is the calling thread's current device (that of `stream`); the array's
+ * device address is looked up on the first call on each device.
+ *
+ * Arguments, outputs, sizes and the multi-launch path for other sizes: as
+ * lora_fused_step.  A size whose counters would not fit the array returns
+ * LORA_ERR_UNSUPPORTED with nothing enqueued (no size the one-launch path
+ * accepts does); a failed lookup of the array returns LORA_ERR_LAUNCH.
+ */
+lora_status_t lora_fused_step_static(const int32_t *token_lora_mapping, int32_t num_tokens,
+                                     const uint16_t *x, int64_t ldx, int32_t hidden,
+                                     const uint16_t *const *lora_a,
+                                     const uint16_t *const *lora_b, const int32_t *slice_sizes,
+                                     int32_t num_slices, int32_t rank, float scale, float *buf,
+                                     int32_t num_splits, uint16_t *y, int64_t ldy,
+                                     const lora_meta_t *meta, const lora_step_options_t *options,
+                                     int32_t max_tokens, int32_t max_loras, hipStream_t stream);
+
 /* lora_status_string - static, human-readable name of a status code. */
 const char *lora_status_string(lora_status_t status);
 

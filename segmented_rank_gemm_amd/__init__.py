@@ -22,6 +22,7 @@ import torch  # noqa: F401  (must precede loading the library, see above)
 __all__ = [
     "LIB_PATH", "LoraError", "LoraMeta", "lib", "lora_prepare_metadata", "lora_shrink",
     "lora_prepare_and_shrink", "lora_fused_step", "lora_fused_step_workspace_bytes",
+    "lora_fused_step_static",
     "fused_step_workspace",
     "lora_shrink_default_splits", "lora_expand", "lora_stream_copy", "lora_stream_update",
     "lora_status_string",
@@ -102,6 +103,11 @@ def lib() -> ctypes.CDLL:
                                       ctypes.c_float, _VP, _I32, _VP, _I64, MP, _VP, _I64,
                                       ctypes.POINTER(_StepOptions), _I32, _I32, _VP]
         L.lora_fused_step.restype = ctypes.c_int
+        L.lora_fused_step_static.argtypes = [_VP, _I32, _VP, _I64, _I32, ctypes.POINTER(_VP),
+                                             ctypes.POINTER(_VP), ctypes.POINTER(_I32), _I32, _I32,
+                                             ctypes.c_float, _VP, _I32, _VP, _I64, MP,
+                                             ctypes.POINTER(_StepOptions), _I32, _I32, _VP]
+        L.lora_fused_step_static.restype = ctypes.c_int
         L.lora_stream_copy.argtypes = [_VP, _VP, _I64, _VP]
         L.lora_stream_copy.restype = ctypes.c_int
         L.lora_stream_update.argtypes = [_VP, _I64, _VP]
@@ -299,6 +305,28 @@ def lora_fused_step(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.
         bptrs, nsz, S, rank, float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits),
         _dev_ptr(y, torch.bfloat16, "y"), int(y.stride(0)), meta.struct_ref, wptr, int(wbytes),
         opts, meta.max_tokens, meta.max_loras, _stream_handle(stream)))
+
+
+def lora_fused_step_static(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.Tensor,
+                           lora_a: Sequence[torch.Tensor], lora_b: Sequence[torch.Tensor],
+                           scale: float, buf: torch.Tensor, num_splits: int, y: torch.Tensor,
+                           meta: LoraMeta, wait_polls: Optional[int] = None,
+                           stream: Optional[torch.cuda.Stream] = None) -> None:
+    """lora_fused_step with the library's own counter array instead of a
+    workspace (nothing is allocated; calls that overlap on one GPU race)."""
+    ptr = _mapping_ptr(token_lora_mapping, num_tokens)
+    S, rank, hidden, aptrs = _shrink_args(x, lora_a, buf, num_splits, meta)
+    Sb, rank_b, bptrs, nsz = _expand_args(buf, num_splits, lora_b, y, meta)
+    if Sb != S or rank_b != rank:
+        raise ValueError("lora_a and lora_b disagree on slices or rank")
+    opts = None
+    if wait_polls is not None:
+        opts = ctypes.byref(_StepOptions(int(wait_polls)))
+    _check("lora_fused_step_static", lib().lora_fused_step_static(
+        ptr, int(num_tokens), _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), hidden, aptrs,
+        bptrs, nsz, S, rank, float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits),
+        _dev_ptr(y, torch.bfloat16, "y"), int(y.stride(0)), meta.struct_ref, opts, meta.max_tokens,
+        meta.max_loras, _stream_handle(stream)))
 
 
 def lora_expand(buf: torch.Tensor, num_splits: int, lora_b: Sequence[torch.Tensor], y: torch.Tensor,

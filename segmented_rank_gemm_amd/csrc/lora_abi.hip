@@ -37,6 +37,8 @@ hipError_t launch_token_step(const int32_t* mapping, int num_tokens, const uint1
                              int num_slices, int rank, float scale, float* buf, int num_splits,
                              uint16_t* y, int64_t ldy, const lora_meta_t& meta, int* counters,
                              int wait_polls, int max_tokens, int max_loras, hipStream_t stream);
+int64_t token_step_scratch_bytes();
+hipError_t token_step_scratch(int** out);
 int shrink_group_blocks(int nb_total);
 int shrink_tile_blocks(int max_tokens, int nb);
 }  // namespace lora
@@ -238,14 +240,20 @@ static lora_status_t expand_args(const float* buf, int32_t num_splits,
   return LORA_OK;
 }
 
-lora_status_t lora_fused_step(const int32_t* token_lora_mapping, int32_t num_tokens,
-                              const uint16_t* x, int64_t ldx, int32_t hidden,
-                              const uint16_t* const* lora_a, const uint16_t* const* lora_b,
-                              const int32_t* slice_sizes, int32_t num_slices, int32_t rank,
-                              float scale, float* buf, int32_t num_splits, uint16_t* y,
-                              int64_t ldy, const lora_meta_t* meta, void* workspace,
-                              int64_t workspace_bytes, const lora_step_options_t* options,
-                              int32_t max_tokens, int32_t max_loras, hipStream_t stream) {
+// lora_fused_step and lora_fused_step_static: argument checks, then the
+// one-launch kernel on `counters` (from the caller's workspace or the
+// library's static array, resolved only once the arguments are known to be
+// valid and the one-launch path is taken) or the multi-launch path.
+// static_counters: use the library's array instead of workspace.
+static lora_status_t fused_step(const int32_t* token_lora_mapping, int32_t num_tokens,
+                                const uint16_t* x, int64_t ldx, int32_t hidden,
+                                const uint16_t* const* lora_a, const uint16_t* const* lora_b,
+                                const int32_t* slice_sizes, int32_t num_slices, int32_t rank,
+                                float scale, float* buf, int32_t num_splits, uint16_t* y,
+                                int64_t ldy, const lora_meta_t* meta, void* workspace,
+                                int64_t workspace_bytes, bool static_counters,
+                                const lora_step_options_t* options, int32_t max_tokens,
+                                int32_t max_loras, hipStream_t stream) {
   if (!meta_ok(meta) || !sizes_ok(max_tokens, max_loras)) return LORA_ERR_INVALID_ARGUMENT;
   if (num_tokens < 0 || num_tokens > max_tokens) return LORA_ERR_INVALID_ARGUMENT;
   if (num_tokens > 0 && !token_lora_mapping) return LORA_ERR_INVALID_ARGUMENT;
@@ -256,20 +264,53 @@ lora_status_t lora_fused_step(const int32_t* token_lora_mapping, int32_t num_tok
   if (st != LORA_OK) return st;
   const int64_t need = lora_fused_step_workspace_bytes(max_tokens, max_loras, num_slices, rank);
   if (need > 0) {
-    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
-        workspace_bytes < need)
-      return LORA_ERR_INVALID_ARGUMENT;
+    int* counters = nullptr;
+    if (static_counters) {
+      if (need > lora::token_step_scratch_bytes()) return LORA_ERR_UNSUPPORTED;
+      if (lora::token_step_scratch(&counters) != hipSuccess) return LORA_ERR_LAUNCH;
+    } else {
+      if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+          workspace_bytes < need)
+        return LORA_ERR_INVALID_ARGUMENT;
+      counters = static_cast<int*>(workspace);
+    }
     const int polls = options && options->wait_polls >= 0 ? options->wait_polls : 65536;
     return launch_status(lora::launch_token_step(
         token_lora_mapping, num_tokens, x, ldx, hidden, lora_a, lora_b, slice_sizes, num_slices,
-        rank, scale, buf, num_splits, y, ldy, *meta, static_cast<int*>(workspace), polls,
-        max_tokens, max_loras, stream));
+        rank, scale, buf, num_splits, y, ldy, *meta, counters, polls, max_tokens, max_loras,
+        stream));
   }
   st = lora_prepare_and_shrink(token_lora_mapping, num_tokens, x, ldx, hidden, lora_a, num_slices,
                                rank, scale, buf, num_splits, meta, max_tokens, max_loras, stream);
   if (st != LORA_OK) return st;
   return lora_expand(buf, num_splits, lora_b, slice_sizes, num_slices, rank, y, ldy, meta,
                      max_tokens, max_loras, stream);
+}
+
+lora_status_t lora_fused_step(const int32_t* token_lora_mapping, int32_t num_tokens,
+                              const uint16_t* x, int64_t ldx, int32_t hidden,
+                              const uint16_t* const* lora_a, const uint16_t* const* lora_b,
+                              const int32_t* slice_sizes, int32_t num_slices, int32_t rank,
+                              float scale, float* buf, int32_t num_splits, uint16_t* y,
+                              int64_t ldy, const lora_meta_t* meta, void* workspace,
+                              int64_t workspace_bytes, const lora_step_options_t* options,
+                              int32_t max_tokens, int32_t max_loras, hipStream_t stream) {
+  return fused_step(token_lora_mapping, num_tokens, x, ldx, hidden, lora_a, lora_b, slice_sizes,
+                    num_slices, rank, scale, buf, num_splits, y, ldy, meta, workspace,
+                    workspace_bytes, false, options, max_tokens, max_loras, stream);
+}
+
+lora_status_t lora_fused_step_static(const int32_t* token_lora_mapping, int32_t num_tokens,
+                                     const uint16_t* x, int64_t ldx, int32_t hidden,
+                                     const uint16_t* const* lora_a, const uint16_t* const* lora_b,
+                                     const int32_t* slice_sizes, int32_t num_slices, int32_t rank,
+                                     float scale, float* buf, int32_t num_splits, uint16_t* y,
+                                     int64_t ldy, const lora_meta_t* meta,
+                                     const lora_step_options_t* options, int32_t max_tokens,
+                                     int32_t max_loras, hipStream_t stream) {
+  return fused_step(token_lora_mapping, num_tokens, x, ldx, hidden, lora_a, lora_b, slice_sizes,
+                    num_slices, rank, scale, buf, num_splits, y, ldy, meta, nullptr, 0, true,
+                    options, max_tokens, max_loras, stream);
 }
 
 lora_status_t lora_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {

@@ -42,6 +42,8 @@
 // end of every launch: each expand unit counts itself out after its wait, and
 // the last one of a tile subtracts what the launch added.
 
+#include <mutex>
+
 #include "device_common.hpp"
 #include "metadata_group.hpp"
 
@@ -646,6 +648,42 @@ bool token_shrink_fits(int max_tokens, int max_loras, int num_slices, int rank) 
 bool token_step_fits(int max_tokens, int max_loras, int num_slices, int rank) {
   return token_shrink_fits(max_tokens, max_loras, num_slices, rank) &&
          (rank == 8 || rank == 16) && max_loras * rank <= kTokMaxLoraRank;
+}
+
+// Counters of lora_fused_step_static: a file-scope device array in place of
+// the caller's workspace, for callers that cannot allocate.  It covers the
+// largest one-launch batch (512 token slots, 32 tiles: 8 KB); every GPU the
+// library runs on holds its own copy until the process ends, zero-filled when
+// the code object is loaded, and every call leaves the counters it used at
+// zero again.  In host code `scratch` names a host-side stand-in, never the
+// device address: that comes from hipGetSymbolAddress, once per device.
+constexpr int kScratchTiles = kTokMaxTokens / kTokTile;
+static __device__ __align__(256) int scratch[kScratchTiles * kCounterInts];
+
+constexpr int kScratchDevices = 64;
+static int* g_scratch_ptr[kScratchDevices];
+static std::mutex g_scratch_mu;
+
+int64_t token_step_scratch_bytes() { return static_cast<int64_t>(sizeof(scratch)); }
+
+// Device address of this device's copy of `scratch` (the current device's:
+// the one the caller's stream belongs to).  Resolved on the first call on each
+// device, with that device current.
+hipError_t token_step_scratch(int** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<int*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 int64_t token_step_workspace_bytes(int max_tokens) {

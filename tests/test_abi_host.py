@@ -224,3 +224,17 @@ def test_fused_step_rejects(kw):
 def test_fused_step_rejects_unsupported_rank():
     # rank 12: valid range, no kernel for it (checked before anything is enqueued)
     assert _fused(rank=12) == 2
+
+
+def test_fused_step_static_rejects_before_any_lookup():
+    # invalid arguments are refused before the library looks up its array
+    a = dict(map=FAKE, T=200, x=FAKE, ldx=4096, hidden=4096, S=3, rank=8, buf=FAKE, splits=16,
+             y=FAKE, ldy=12288, maxT=256, L=4)
+    sizes = (ctypes.c_int32 * 3)(4096, 4096, 4096)
+    f = srg.lib().lora_fused_step_static
+    assert f(a["map"], 300, a["x"], a["ldx"], a["hidden"], _ptrs(3), _ptrs(3), sizes, 3, 8, 1.0,
+             a["buf"], 16, a["y"], a["ldy"], _meta(), None, 256, 4, None) == 1   # T > max_tokens
+    assert f(a["map"], 200, a["x"], a["ldx"], a["hidden"], _ptrs(3), _ptrs(3), sizes, 3, 12, 1.0,
+             a["buf"], 16, a["y"], a["ldy"], _meta(), None, 256, 4, None) == 2   # rank 12
+    assert f(None, 200, a["x"], a["ldx"], a["hidden"], _ptrs(3), _ptrs(3), sizes, 3, 8, 1.0,
+             a["buf"], 16, a["y"], a["ldy"], _meta(), None, 256, 4, None) == 1   # no map
