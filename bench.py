@@ -99,9 +99,10 @@ def parse():
     ap.add_argument("--rotate", type=int, default=None, help="buffer copies (default: >= 1 GiB)")
     ap.add_argument("--kernel-reps", type=int, default=50,
                     help="graph replays per single-kernel timing")
-    ap.add_argument("--tune", action="store_true",
-                    help="choose the shrink's part count by timing the candidates on this batch "
-                    "(segmented_rank_gemm_amd.tuning) instead of the size rule")
+    ap.add_argument("--rules", action="store_true",
+                    help="use the library's size rules for the part count and the expand's "
+                    "launch choices instead of the measured table (segmented_rank_gemm_amd/"
+                    "tuning_table.json)")
     ap.add_argument("--layers", type=int, default=32,
                     help="layers of the layer-stack timing (one metadata step, then shrink + "
                     "expand per layer on its own weights and activations; 0 skips it)")
@@ -109,15 +110,17 @@ def parse():
 
 
 class Sets:
-    """R device copies of one workload's buffers, plus the per-copy metadata."""
+    """R device copies of one workload's buffers, plus the per-copy metadata;
+    every expand call takes the given launch choices."""
 
-    def __init__(self, w, R, num_splits):
+    def __init__(self, w, R, num_splits, expand_cfg=None):
         import torch
 
         import segmented_rank_gemm_amd as srg
         from workloads.device import to_dev_bf16
 
         self.w, self.R, self.num_splits = w, R, num_splits
+        self.expand_cfg = expand_cfg
         T, maxT = w.num_tokens, w.max_tokens
         base = dict(
             mapping=torch.from_numpy(w.mapping.astype("int32")).cuda(),
@@ -174,7 +177,8 @@ class Sets:
     def expand(self, r, stream=None):
         import segmented_rank_gemm_amd as srg
         s = self.sets[r]
-        srg.lora_expand(s["buf"], self.num_splits, s["b"], s["y"], s["meta"], stream)
+        srg.lora_expand(s["buf"], self.num_splits, s["b"], s["y"], s["meta"], stream,
+                        config=self.expand_cfg)
 
     def layer(self, r, meta_r, stream=None):
         """Shrink + expand on copy r (one layer's weights and activations) with the
@@ -182,7 +186,8 @@ class Sets:
         import segmented_rank_gemm_amd as srg
         s, m = self.sets[r], self.sets[meta_r]["meta"]
         srg.lora_shrink(s["x"], s["a"], float(self.w.scale), s["buf"], self.num_splits, m, stream)
-        srg.lora_expand(s["buf"], self.num_splits, s["b"], s["y"], m, stream)
+        srg.lora_expand(s["buf"], self.num_splits, s["b"], s["y"], m, stream,
+                        config=self.expand_cfg)
 
     def fused(self, r, stream=None, meta_r=None):
         """The whole path in one call (lora_fused_step), writing copy meta_r's
@@ -191,7 +196,8 @@ class Sets:
         s = self.sets[r]
         m = s["meta"] if meta_r is None else self.sets[meta_r]["meta"]
         srg.lora_fused_step(s["mapping"], self.T, s["x"], s["a"], s["b"], float(self.w.scale),
-                            s["buf"], self.num_splits, s["y"], m, self.workspace, stream=stream)
+                            s["buf"], self.num_splits, s["y"], m, self.workspace, stream=stream,
+                            expand_config=self.expand_cfg)
 
     def step(self, r, stream=None):
         """The whole path: lora_fused_step."""
@@ -313,24 +319,18 @@ def run_config(idx, args):
     log(f"[bench] workload {idx} ({CONFIGS[idx]['name']}): generating inputs")
     w = make_workload(idx)
     st = workload_stats(w)
-    splits = srg.lora_shrink_default_splits(w.hidden, w.max_tokens, w.max_loras, w.num_slices,
-                                            w.rank)
-    tuning = None
-    if args.tune:
-        from segmented_rank_gemm_amd.tuning import tune_shrink_splits
-        log("[bench] tuning the shrink's part count")
-        one = Sets(w, 1, splits)
-        s0 = one.sets[0]
-        tuning = tune_shrink_splits(s0["x"], s0["a"], s0["b"], s0["y"], float(w.scale), s0["meta"])
-        del one, s0
-        torch.cuda.empty_cache()
-        splits = tuning["best"]
-        tuning = {"rule": tuning["default"], "best": tuning["best"],
-                  "pair_us": {str(k): round(v, 3) for k, v in tuning["us"].items()}}
+    from segmented_rank_gemm_amd.tuning import plan
+    rule_splits = srg.lora_shrink_default_splits(w.hidden, w.max_tokens, w.max_loras,
+                                                 w.num_slices, w.rank)
+    pl = plan(w.hidden, w.max_tokens, w.max_loras, w.slices, w.rank)
+    if args.rules:
+        pl = {"num_splits": rule_splits, "expand": srg.ExpandConfig(), "source": "size rule"}
+    splits = pl["num_splits"]
+    expand_cfg = pl["expand"] or srg.ExpandConfig()
     sb = set_bytes(w, splits)
     R = args.rotate or max(2, math.ceil(ROTATE_BYTES / sb))
     log(f"[bench] {R} rotated buffer sets of {sb / 1e6:.1f} MB, {splits} shrink parts")
-    sets = Sets(w, R, splits)
+    sets = Sets(w, R, splits, expand_cfg)
 
     # eager pass on every set so the metadata exists before single-kernel graphs replay
     for r in range(R):
@@ -407,6 +407,27 @@ def run_config(idx, args):
     step3_s = per.pop("step3")
     step2_s = per.pop("step2")
 
+    # V0-style input: the same batch regrouped by adapter (each group one
+    # contiguous run), through the general metadata kernel and the one-pass
+    # grouped one (same outputs)
+    import numpy as np
+    ids = np.where((w.mapping >= -1) & (w.mapping < w.max_loras), w.mapping, -1)
+    gmap = torch.from_numpy(w.mapping[np.argsort(ids, kind="stable")].astype("int32")).cuda()
+    gmaps = [gmap.clone() for _ in range(R)]
+    grouped = {}
+    for name, f in (("lora_prepare_metadata", srg.lora_prepare_metadata),
+                    ("lora_prepare_metadata_grouped", srg.lora_prepare_metadata_grouped)):
+        m = R * max(1, math.ceil(MIN_GRAPH_LAUNCHES / R))
+        g = capture([lambda s, r=r, f=f: f(gmaps[r % R], sets.T, sets.sets[r % R]["meta"], s)
+                     for r in range(m)])
+        grouped[name + "_us"] = time_graph(g, reps) / m * 1e6
+        del g
+    del gmaps
+    # (the copies' metadata is the regrouped batch's now: recompute it)
+    for r in range(sets.R):
+        sets.metadata(r)
+    torch.cuda.synchronize()
+
     # layer stack: one metadata step serves a model's L LoRA layers of this
     # shape, each with its own weights, activations and outputs.  Stacks are
     # rotated like the steps (each stack takes L copies and computes its
@@ -481,7 +502,8 @@ def run_config(idx, args):
             "active_tokens": st["active_tokens"], "hidden": w.hidden, "slices": w.slices,
             "rank": w.rank, "max_loras": w.max_loras, "active_adapters": st["active_adapters"],
             "scale": w.scale, "accumulate": "fp32", "shrink_parts": splits,
-            "shrink_parts_from": "measured" if tuning else "size rule", "tuning": tuning,
+            "shrink_parts_from": pl["source"], "shrink_parts_rule": rule_splits,
+            "expand_config": expand_cfg.as_dict(), "expand_config_from": pl["source"],
             "rotated_sets": R, "rotated_sets_per_kernel": rot, "parallelism": "single GPU",
         },
         "roofline": {
@@ -517,6 +539,7 @@ def run_config(idx, args):
             "frac_of_peak": (st["shrink_bytes"] + st["expand_bytes"]) / pair_s / 1e9 / HBM_PEAK_GBS,
         },
         "layer_stack": stack,
+        "grouped_input": dict(grouped, batch="the same batch regrouped by adapter (V0-style)"),
         "copy_ceiling": {"bytes_read_plus_written": 2 * cb, "us": copy_s * 1e6,
                          "GBs": 2 * cb / copy_s / 1e9},
         "update_ceiling": {"bytes_read_plus_written": 2 * cb, "us": upd_s * 1e6,

@@ -155,6 +155,29 @@ lora_status_t lora_prepare_metadata(const int32_t *token_lora_mapping, int32_t n
                                     const lora_meta_t *meta, hipStream_t stream);
 
 /*
+ * lora_prepare_metadata_grouped - lora_prepare_metadata for a batch that
+ * arrives grouped by adapter: every group (each adapter id, and the tokens
+ * without an adapter) occupies one contiguous run of the batch, in any order
+ * of the runs.
+ *
+ * Defined by: vLLM PR #13096, "Why do we need a new set of kernels" (the V0
+ * path grouped the requests by LoRA id and its kernels relied on it) and the
+ * MLC-LLM issue's Overview (Punica's segment vector, one segment per run).
+ *
+ * Arguments and outputs: exactly those of lora_prepare_metadata, bit for bit.
+ * One workgroup reads the map once (O(num_tokens) work in all) and derives
+ * every output from the run boundaries.  A batch that is NOT grouped is
+ * detected on the device in the same launch and handled by the general
+ * per-group code, group after group in that one workgroup: the same outputs,
+ * at (max_loras + 1) passes over the map (use lora_prepare_metadata for such
+ * batches).  Grid: one workgroup of 1024 threads.
+ */
+lora_status_t lora_prepare_metadata_grouped(const int32_t *token_lora_mapping,
+                                            int32_t num_tokens, int32_t max_tokens,
+                                            int32_t max_loras, const lora_meta_t *meta,
+                                            hipStream_t stream);
+
+/*
  * lora_shrink_default_splits - recommended number of hidden-dimension
  * partitions for lora_shrink (host only, no device access).  Returns a value in
  * [1, LORA_MAX_SPLITS], or 0 if an argument is out of range.  The result is a
@@ -234,6 +257,25 @@ lora_status_t lora_prepare_and_shrink(const int32_t *token_lora_mapping, int32_t
                                       int32_t max_loras, hipStream_t stream);
 
 /*
+ * Launch choices of lora_expand (host struct; every field has a "the library's
+ * rule" value).  They change how the work is cut and walked, never the result:
+ * any valid setting gives the same bits.  A per-shape table of measured
+ * choices is kept by the Python package (segmented_rank_gemm_amd.tuning).
+ *   chunks_per_range   128-column chunks of a unit: per wave at ranks 8/16
+ *                      (a unit spans 4x that), per workgroup at ranks 32/64.
+ *                      0: rule; 1..64 (1..16 at ranks 32/64).
+ *   range_fastest      unit order: 1 = a tile's column ranges one after
+ *                      another, 0 = tiles one after another; -1: rule.
+ *   workgroups_per_cu  workgroups per CU the persistent grid is sized for (no
+ *                      more than the kernel holds at once); 0: rule; 1..16.
+ */
+typedef struct lora_expand_config {
+  int32_t chunks_per_range;
+  int32_t range_fastest;
+  int32_t workgroups_per_cu;
+} lora_expand_config_t;
+
+/*
  * lora_expand - project each grouped token's rank-r vector up through its
  * adapter's B and add it into the output, slice by slice:
  *   y[t][off_s + n] = bf16( y[t][off_s + n] + sum_k buf[s][t][k] * B_s[l][n][k] ),
@@ -254,12 +296,15 @@ lora_status_t lora_prepare_and_shrink(const int32_t *token_lora_mapping, int32_t
  *               16-byte aligned.
  *   ldy         row stride of y in elements; >= sum of slice_sizes, multiple
  *               of 8.
+ *   config      host pointer to launch choices, or NULL for the library's
+ *               rules; an out-of-range field is LORA_ERR_INVALID_ARGUMENT.
  *   Other arguments as in lora_shrink.
  */
 lora_status_t lora_expand(const float *buf, int32_t num_splits, const uint16_t *const *lora_b,
                           const int32_t *slice_sizes, int32_t num_slices, int32_t rank,
                           uint16_t *y, int64_t ldy, const lora_meta_t *meta, int32_t max_tokens,
-                          int32_t max_loras, hipStream_t stream);
+                          int32_t max_loras, const lora_expand_config_t *config,
+                          hipStream_t stream);
 
 /*
  * lora_fused_step - the whole step for one batch (lora_prepare_metadata,
@@ -297,6 +342,8 @@ typedef struct lora_step_options {
    * reaches it computes the missing parts itself (same bits, more time).
    * Negative: the default (65536).  0: never wait. */
   int32_t wait_polls;
+  /* Launch choices of the expand on the multi-launch path (see lora_expand). */
+  lora_expand_config_t expand;
 } lora_step_options_t;
 
 int64_t lora_fused_step_workspace_bytes(int32_t max_tokens, int32_t max_loras,

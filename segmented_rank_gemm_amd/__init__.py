@@ -22,7 +22,7 @@ import torch  # noqa: F401  (must precede loading the library, see above)
 __all__ = [
     "LIB_PATH", "LoraError", "LoraMeta", "lib", "lora_prepare_metadata", "lora_shrink",
     "lora_prepare_and_shrink", "lora_fused_step", "lora_fused_step_workspace_bytes",
-    "lora_fused_step_static",
+    "lora_fused_step_static", "lora_prepare_metadata_grouped", "ExpandConfig",
     "fused_step_workspace",
     "lora_shrink_default_splits", "lora_expand", "lora_stream_copy", "lora_stream_update",
     "lora_status_string",
@@ -54,8 +54,45 @@ class _MetaStruct(ctypes.Structure):
                 ("tile_lora", ctypes.c_void_p), ("num_tiles", ctypes.c_void_p),
                 ("num_runs", ctypes.c_void_p)]
 
+class ExpandConfig(ctypes.Structure):
+    """lora_expand_config_t: launch choices of lora_expand (0 / -1: the
+    library's rule).  Any valid setting gives the same bits."""
+    _fields_ = [("chunks_per_range", ctypes.c_int32), ("range_fastest", ctypes.c_int32),
+                ("workgroups_per_cu", ctypes.c_int32)]
+
+    def __init__(self, chunks_per_range: int = 0, range_fastest: int = -1,
+                 workgroups_per_cu: int = 0):
+        super().__init__(int(chunks_per_range), int(range_fastest), int(workgroups_per_cu))
+
+    def as_dict(self):
+        return {"chunks_per_range": self.chunks_per_range, "range_fastest": self.range_fastest,
+                "workgroups_per_cu": self.workgroups_per_cu}
+
+
 class _StepOptions(ctypes.Structure):
-    _fields_ = [("wait_polls", ctypes.c_int32)]
+    _fields_ = [("wait_polls", ctypes.c_int32), ("expand", ExpandConfig)]
+
+
+def _expand_config(config, lora_b=None, num_splits=None, meta=None) -> Optional[ExpandConfig]:
+    """None: the library's rules; "table": the measured choices for the call's
+    shape in segmented_rank_gemm_amd/tuning_table.json (the rules if the table
+    does not have it); an ExpandConfig or a dict of its fields."""
+    if config is None or isinstance(config, ExpandConfig):
+        return config
+    if isinstance(config, str):
+        if config != "table":
+            raise ValueError(f"expand config {config!r}: expected 'table', None or ExpandConfig")
+        from .tuning import expand_config_for
+        return expand_config_for(lora_b, num_splits, meta)
+    return ExpandConfig(**config)
+
+
+def _step_options(wait_polls, expand_config, lora_b=None, num_splits=None, meta=None):
+    cfg = _expand_config(expand_config, lora_b, num_splits, meta)
+    if wait_polls is None and cfg is None:
+        return None
+    cfg = cfg or ExpandConfig()
+    return ctypes.byref(_StepOptions(-1 if wait_polls is None else int(wait_polls), cfg))
 
 
 TILE = 16  # positions per tile of the padded grouped order (LORA_TILE)
@@ -85,6 +122,8 @@ def lib() -> ctypes.CDLL:
         L.lora_status_string.restype = ctypes.c_char_p
         L.lora_prepare_metadata.argtypes = [_VP, _I32, _I32, _I32, MP, _VP]
         L.lora_prepare_metadata.restype = ctypes.c_int
+        L.lora_prepare_metadata_grouped.argtypes = [_VP, _I32, _I32, _I32, MP, _VP]
+        L.lora_prepare_metadata_grouped.restype = ctypes.c_int
         L.lora_shrink_default_splits.argtypes = [_I32, _I32, _I32, _I32, _I32]
         L.lora_shrink_default_splits.restype = _I32
         L.lora_shrink.argtypes = [_VP, _I64, _I32, ctypes.POINTER(_VP), _I32, _I32, ctypes.c_float,
@@ -94,7 +133,7 @@ def lib() -> ctypes.CDLL:
                                               _I32, ctypes.c_float, _VP, _I32, MP, _I32, _I32, _VP]
         L.lora_prepare_and_shrink.restype = ctypes.c_int
         L.lora_expand.argtypes = [_VP, _I32, ctypes.POINTER(_VP), ctypes.POINTER(_I32), _I32, _I32,
-                                  _VP, _I64, MP, _I32, _I32, _VP]
+                                  _VP, _I64, MP, _I32, _I32, ctypes.POINTER(ExpandConfig), _VP]
         L.lora_expand.restype = ctypes.c_int
         L.lora_fused_step_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32]
         L.lora_fused_step_workspace_bytes.restype = _I64
@@ -194,6 +233,17 @@ def lora_prepare_metadata(token_lora_mapping: torch.Tensor, num_tokens: int, met
         _stream_handle(stream)))
 
 
+def lora_prepare_metadata_grouped(token_lora_mapping: torch.Tensor, num_tokens: int,
+                                  meta: LoraMeta,
+                                  stream: Optional[torch.cuda.Stream] = None) -> None:
+    """lora_prepare_metadata for a batch already grouped by adapter (one pass;
+    an ungrouped batch gets the same outputs, more slowly)."""
+    ptr = _mapping_ptr(token_lora_mapping, num_tokens)
+    _check("lora_prepare_metadata_grouped", lib().lora_prepare_metadata_grouped(
+        ptr, int(num_tokens), meta.max_tokens, meta.max_loras, meta.struct_ref,
+        _stream_handle(stream)))
+
+
 def lora_shrink_default_splits(hidden: int, max_tokens: int, max_loras: int, num_slices: int,
                                rank: int) -> int:
     return int(lib().lora_shrink_default_splits(hidden, max_tokens, max_loras, num_slices, rank))
@@ -285,7 +335,7 @@ def lora_fused_step(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.
                     lora_a: Sequence[torch.Tensor], lora_b: Sequence[torch.Tensor], scale: float,
                     buf: torch.Tensor, num_splits: int, y: torch.Tensor, meta: LoraMeta,
                     workspace: Optional[torch.Tensor], wait_polls: Optional[int] = None,
-                    stream: Optional[torch.cuda.Stream] = None) -> None:
+                    stream: Optional[torch.cuda.Stream] = None, expand_config="table") -> None:
     """Metadata, shrink and expand of one batch (one launch where the sizes
     allow); arguments as for lora_prepare_and_shrink and lora_expand, plus the
     zero-filled workspace of fused_step_workspace (reused call after call)."""
@@ -297,9 +347,7 @@ def lora_fused_step(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.
     wptr, wbytes = 0, 0
     if workspace is not None:
         wptr, wbytes = _flat_dev_bytes(workspace, "workspace")
-    opts = None
-    if wait_polls is not None:
-        opts = ctypes.byref(_StepOptions(int(wait_polls)))
+    opts = _step_options(wait_polls, expand_config, lora_b, num_splits, meta)
     _check("lora_fused_step", lib().lora_fused_step(
         ptr, int(num_tokens), _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), hidden, aptrs,
         bptrs, nsz, S, rank, float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits),
@@ -311,7 +359,7 @@ def lora_fused_step_static(token_lora_mapping: torch.Tensor, num_tokens: int, x:
                            lora_a: Sequence[torch.Tensor], lora_b: Sequence[torch.Tensor],
                            scale: float, buf: torch.Tensor, num_splits: int, y: torch.Tensor,
                            meta: LoraMeta, wait_polls: Optional[int] = None,
-                           stream: Optional[torch.cuda.Stream] = None) -> None:
+                           stream: Optional[torch.cuda.Stream] = None, expand_config="table") -> None:
     """lora_fused_step with the library's own counter array instead of a
     workspace (nothing is allocated; calls that overlap on one GPU race)."""
     ptr = _mapping_ptr(token_lora_mapping, num_tokens)
@@ -319,9 +367,7 @@ def lora_fused_step_static(token_lora_mapping: torch.Tensor, num_tokens: int, x:
     Sb, rank_b, bptrs, nsz = _expand_args(buf, num_splits, lora_b, y, meta)
     if Sb != S or rank_b != rank:
         raise ValueError("lora_a and lora_b disagree on slices or rank")
-    opts = None
-    if wait_polls is not None:
-        opts = ctypes.byref(_StepOptions(int(wait_polls)))
+    opts = _step_options(wait_polls, expand_config, lora_b, num_splits, meta)
     _check("lora_fused_step_static", lib().lora_fused_step_static(
         ptr, int(num_tokens), _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), hidden, aptrs,
         bptrs, nsz, S, rank, float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits),
@@ -330,14 +376,20 @@ def lora_fused_step_static(token_lora_mapping: torch.Tensor, num_tokens: int, x:
 
 
 def lora_expand(buf: torch.Tensor, num_splits: int, lora_b: Sequence[torch.Tensor], y: torch.Tensor,
-                meta: LoraMeta, stream: Optional[torch.cuda.Stream] = None) -> None:
+                meta: LoraMeta, stream: Optional[torch.cuda.Stream] = None,
+                config="table") -> None:
     """buf: fp32 [num_splits, S, max_tokens, rank]; lora_b[s]: bf16 [max_loras, n_s, rank];
     y: bf16 [>=max_tokens, >=sum(n_s)] (row stride y.stride(0)), updated in place."""
     S, rank, bptrs, nsz = _expand_args(buf, num_splits, lora_b, y, meta)
     _check("lora_expand", lib().lora_expand(
         _dev_ptr(buf, torch.float32, "buf"), int(num_splits), bptrs, nsz, S, rank,
         _dev_ptr(y, torch.bfloat16, "y"), int(y.stride(0)), meta.struct_ref, meta.max_tokens,
-        meta.max_loras, _stream_handle(stream)))
+        meta.max_loras, _cfg_ref(_expand_config(config, lora_b, num_splits, meta)),
+        _stream_handle(stream)))
+
+
+def _cfg_ref(cfg):
+    return None if cfg is None else ctypes.byref(cfg)
 
 
 def _flat_dev_bytes(t: torch.Tensor, name: str):

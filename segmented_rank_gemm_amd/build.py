@@ -18,8 +18,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblora_mi355x.so")
 ARCH = "gfx950"
 
-SOURCES = ["lora_abi.hip", "metadata.hip", "shrink.hip", "expand.hip", "token_step.hip",
-           "stream_copy.hip"]
+SOURCES = ["lora_abi.hip", "metadata.hip", "metadata_grouped.hip", "shrink.hip", "expand.hip",
+           "token_step.hip", "stream_copy.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,

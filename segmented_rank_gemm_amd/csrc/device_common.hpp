@@ -214,20 +214,26 @@ __device__ __forceinline__ Tile resolve_tile(const SegmentTable& tab, int m) {
 // xcd * per_xcd + slot, + slots_per_xcd, ... within its XCD's run.
 constexpr int kXcds = 8;
 
+// Compute units of the MI355X (gfx950): 256, in 8 XCDs of 32.  Grid sizes
+// are a function of the size arguments and these constants only.
+constexpr int kCus = 256;
+
 // Clamp a persistent grid to the workgroups the device holds at once, so that
 // every launched workgroup runs from the start: one queued behind the resident
 // ones would begin its share of the units only when another ends, and a share
 // of large units then finishes far behind the rest.  Whole rounds over the
-// XCDs.  Host only.
-template <typename Kernel>
-inline int resident_grid(Kernel kernel, int threads, int grid) {
-  int per_cu = 0, dev = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
-      per_cu < 1 || hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus < 1)
-    return grid;
-  int64_t cap = static_cast<int64_t>(per_cu) * cus / kXcds * kXcds;
+// XCDs.  Host only.  The kernel's workgroups per CU (a property of its code:
+// registers and LDS) are looked up once per process and kept; a failed lookup
+// leaves the grid as it is.
+// (One instantiation per kernel, so each kernel keeps its own value.)
+template <auto Kernel>
+inline int resident_grid(int threads, int grid) {
+  static const int per_cu = [threads] {
+    int v = 0;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, Kernel, threads, 0) == hipSuccess ? v : 0;
+  }();
+  if (per_cu < 1) return grid;
+  int64_t cap = static_cast<int64_t>(per_cu) * kCus / kXcds * kXcds;
   cap = cap < kXcds ? kXcds : cap;
   return grid < cap ? grid : static_cast<int>(cap);
 }

@@ -24,10 +24,6 @@
 
 #include "device_common.hpp"
 
-#ifdef LORA_TUNING
-#include <cstdlib>
-#endif
-
 namespace lora {
 
 constexpr int kExpandThreads = 256;
@@ -691,14 +687,14 @@ void expand_shared_kernel(ExpandParams p) {
 
 template <int RANK>
 hipError_t launch_expand_shared(const ExpandParams& p, int grid, hipStream_t stream) {
-  grid = resident_grid(expand_shared_kernel<RANK>, kExpandThreads, grid);
+  grid = resident_grid<expand_shared_kernel<RANK>>(kExpandThreads, grid);
   hipLaunchKernelGGL((expand_shared_kernel<RANK>), dim3(grid), dim3(kExpandThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int RANK, int MW>
 hipError_t launch_expand_rank(const ExpandParams& p, int grid, hipStream_t stream) {
-  grid = resident_grid(expand_kernel<RANK, MW>, kExpandThreads, grid);
+  grid = resident_grid<expand_kernel<RANK, MW>>(kExpandThreads, grid);
   hipLaunchKernelGGL((expand_kernel<RANK, MW>), dim3(grid), dim3(kExpandThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -707,7 +703,7 @@ hipError_t launch_expand_rank(const ExpandParams& p, int grid, hipStream_t strea
 hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const* lora_b,
                          const int32_t* slice_sizes, int num_slices, int rank, uint16_t* y,
                          int64_t ldy, const lora_meta_t& meta, int max_tokens, int max_loras,
-                         int num_cus, hipStream_t stream) {
+                         int num_cus, const lora_expand_config_t* config, hipStream_t stream) {
   ExpandParams p{};
   p.buf = buf;
   p.num_splits = num_splits;
@@ -746,18 +742,14 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
     cpr = cpr < 1 ? 1 : (cpr > 8 ? 8 : cpr);
     if (large) cpr = 2;
   }
-#ifdef LORA_TUNING
-  if (const char* e = getenv("LORA_EXPAND_CPR")) cpr = atoi(e);
-#endif
+  if (config && config->chunks_per_range > 0) cpr = config->chunks_per_range;
   p.chunks_per_range = static_cast<int>(cpr);
   // Large batches take the column ranges of a tile one after another, so an
   // XCD's workgroups sweep whole y rows of a few tiles at a time (better DRAM
   // page locality: measured 125 vs 128 us on the prefill batch); small ones
   // keep tiles next to each other (their few rows fit a single sweep anyway).
   p.order_range_fastest = large ? 1 : 0;
-#ifdef LORA_TUNING
-  if (const char* e = getenv("LORA_EXPAND_ORDER")) p.order_range_fastest = atoi(e);
-#endif
+  if (config && config->range_fastest >= 0) p.order_range_fastest = config->range_fastest;
   // (shared-B kernel: the shortest range it may choose bounds the units)
   const int per_unit = shared ? (p.chunks_per_range > 0 ? p.chunks_per_range : 2)
                               : p.chunks_per_range * kExpandWaves;
@@ -795,9 +787,7 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
   // another's unit start-up; the range choice counts rounds per CU, whose
   // fetch rate bounds them all)
   int64_t wg_per_cu = shared ? (rank == 32 ? 3 : 2) : 8;
-#ifdef LORA_TUNING
-  if (const char* e = getenv("LORA_EXPAND_SHARED_WPC")) if (shared) wg_per_cu = atoi(e);
-#endif
+  if (config && config->workgroups_per_cu > 0) wg_per_cu = config->workgroups_per_cu;
   const int64_t cap = static_cast<int64_t>(num_cus) * wg_per_cu;
   grid = grid < cap ? grid : cap;
   grid = (grid + kXcds - 1) / kXcds * kXcds;  // whole rounds over the XCDs

@@ -13,6 +13,8 @@
 namespace lora {
 hipError_t launch_metadata(const int32_t* mapping, int num_tokens, int max_tokens, int max_loras,
                            const lora_meta_t& meta, hipStream_t stream);
+hipError_t launch_metadata_grouped(const int32_t* mapping, int num_tokens, int max_tokens,
+                                   int max_loras, const lora_meta_t& meta, hipStream_t stream);
 hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint16_t* const* lora_a,
                          int num_slices, int rank, float scale, float* buf, int num_splits,
                          const lora_meta_t& meta, int max_tokens, int max_loras, int num_cus,
@@ -20,7 +22,7 @@ hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint1
 hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const* lora_b,
                          const int32_t* slice_sizes, int num_slices, int rank, uint16_t* y,
                          int64_t ldy, const lora_meta_t& meta, int max_tokens, int max_loras,
-                         int num_cus, hipStream_t stream);
+                         int num_cus, const lora_expand_config_t* config, hipStream_t stream);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int num_cus,
                               hipStream_t stream);
 hipError_t launch_stream_update(void* buf, int64_t bytes, int num_cus, hipStream_t stream);
@@ -63,17 +65,9 @@ bool sizes_ok(int32_t max_tokens, int32_t max_loras) {
 
 bool rank_supported(int32_t rank) { return rank == 8 || rank == 16 || rank == 32 || rank == 64; }
 
-// Compute units of the current device: sizes the persistent grids.  A host
-// query answered from the runtime's cached device properties.
-int current_cus() {
-  int dev = 0;
-  int cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    return 256;
-  return cus;
-}
+// Compute units the persistent grids are sized for: the MI355X's 256 (a
+// constant: no call queries the device for it).
+int current_cus() { return 256; }
 
 lora_status_t launch_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_LAUNCH; }
 
@@ -99,6 +93,17 @@ lora_status_t lora_prepare_metadata(const int32_t* token_lora_mapping, int32_t n
   if (num_tokens > 0 && !token_lora_mapping) return LORA_ERR_INVALID_ARGUMENT;
   return launch_status(
       lora::launch_metadata(token_lora_mapping, num_tokens, max_tokens, max_loras, *meta, stream));
+}
+
+lora_status_t lora_prepare_metadata_grouped(const int32_t* token_lora_mapping,
+                                            int32_t num_tokens, int32_t max_tokens,
+                                            int32_t max_loras, const lora_meta_t* meta,
+                                            hipStream_t stream) {
+  if (!meta_ok(meta) || !sizes_ok(max_tokens, max_loras)) return LORA_ERR_INVALID_ARGUMENT;
+  if (num_tokens < 0 || num_tokens > max_tokens) return LORA_ERR_INVALID_ARGUMENT;
+  if (num_tokens > 0 && !token_lora_mapping) return LORA_ERR_INVALID_ARGUMENT;
+  return launch_status(lora::launch_metadata_grouped(token_lora_mapping, num_tokens, max_tokens,
+                                                     max_loras, *meta, stream));
 }
 
 int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t max_loras,
@@ -188,10 +193,18 @@ lora_status_t lora_prepare_and_shrink(const int32_t* token_lora_mapping, int32_t
                                                 stream));
 }
 
+static bool expand_config_ok(const lora_expand_config_t* c, int32_t rank) {
+  if (!c) return true;
+  const int32_t max_cpr = rank >= 32 ? 16 : 64;
+  return c->chunks_per_range >= 0 && c->chunks_per_range <= max_cpr && c->range_fastest >= -1 &&
+         c->range_fastest <= 1 && c->workgroups_per_cu >= 0 && c->workgroups_per_cu <= 16;
+}
+
 lora_status_t lora_expand(const float* buf, int32_t num_splits, const uint16_t* const* lora_b,
                           const int32_t* slice_sizes, int32_t num_slices, int32_t rank,
                           uint16_t* y, int64_t ldy, const lora_meta_t* meta, int32_t max_tokens,
-                          int32_t max_loras, hipStream_t stream) {
+                          int32_t max_loras, const lora_expand_config_t* config,
+                          hipStream_t stream) {
   if (!meta_ok(meta) || !sizes_ok(max_tokens, max_loras)) return LORA_ERR_INVALID_ARGUMENT;
   if (!buf || !lora_b || !slice_sizes || !y || !aligned16(buf) || !aligned16(y))
     return LORA_ERR_INVALID_ARGUMENT;
@@ -205,10 +218,11 @@ lora_status_t lora_expand(const float* buf, int32_t num_splits, const uint16_t* 
     n_total += slice_sizes[s];
   }
   if (n_total > (int64_t{1} << 30) || ldy < n_total || ldy % 8 != 0) return LORA_ERR_INVALID_ARGUMENT;
+  if (!expand_config_ok(config, rank)) return LORA_ERR_INVALID_ARGUMENT;
   if (!rank_supported(rank)) return LORA_ERR_UNSUPPORTED;
   return launch_status(lora::launch_expand(buf, num_splits, lora_b, slice_sizes, num_slices, rank,
                                            y, ldy, *meta, max_tokens, max_loras, current_cus(),
-                                           stream));
+                                           config, stream));
 }
 
 int64_t lora_fused_step_workspace_bytes(int32_t max_tokens, int32_t max_loras,
@@ -240,6 +254,10 @@ static lora_status_t expand_args(const float* buf, int32_t num_splits,
   return LORA_OK;
 }
 
+static const lora_expand_config_t* options_expand(const lora_step_options_t* options) {
+  return options ? &options->expand : nullptr;
+}
+
 // lora_fused_step and lora_fused_step_static: argument checks, then the
 // one-launch kernel on `counters` (from the caller's workspace or the
 // library's static array, resolved only once the arguments are known to be
@@ -262,6 +280,7 @@ static lora_status_t fused_step(const int32_t* token_lora_mapping, int32_t num_t
   if (st != LORA_OK) return st;
   st = expand_args(buf, num_splits, lora_b, slice_sizes, num_slices, rank, y, ldy);
   if (st != LORA_OK) return st;
+  if (!expand_config_ok(options_expand(options), rank)) return LORA_ERR_INVALID_ARGUMENT;
   const int64_t need = lora_fused_step_workspace_bytes(max_tokens, max_loras, num_slices, rank);
   if (need > 0) {
     int* counters = nullptr;
@@ -284,7 +303,7 @@ static lora_status_t fused_step(const int32_t* token_lora_mapping, int32_t num_t
                                rank, scale, buf, num_splits, meta, max_tokens, max_loras, stream);
   if (st != LORA_OK) return st;
   return lora_expand(buf, num_splits, lora_b, slice_sizes, num_slices, rank, y, ldy, meta,
-                     max_tokens, max_loras, stream);
+                     max_tokens, max_loras, options_expand(options), stream);
 }
 
 lora_status_t lora_fused_step(const int32_t* token_lora_mapping, int32_t num_tokens,

@@ -25,10 +25,6 @@
 #include "device_common.hpp"
 #include "metadata_group.hpp"
 
-#ifdef LORA_TUNING
-#include <cstdlib>
-#endif
-
 namespace lora {
 
 constexpr int kMaxFusedLoras = 16;  // adapter slots the fused prepare + shrink serves
@@ -540,14 +536,14 @@ void shrink_lds_kernel(ShrinkParams p) {
 
 template <int NB>
 hipError_t launch_shrink_lds_nb(const ShrinkParams& p, int grid, hipStream_t stream) {
-  grid = resident_grid(shrink_lds_kernel<NB>, kShrinkThreads, grid);
+  grid = resident_grid<shrink_lds_kernel<NB>>(kShrinkThreads, grid);
   hipLaunchKernelGGL((shrink_lds_kernel<NB>), dim3(grid), dim3(kShrinkThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int NB, int MW>
 hipError_t launch_shrink_nb(const ShrinkParams& p, int grid, hipStream_t stream) {
-  grid = resident_grid(shrink_kernel<NB, MW>, kShrinkThreads, grid);
+  grid = resident_grid<shrink_kernel<NB, MW>>(kShrinkThreads, grid);
   hipLaunchKernelGGL((shrink_kernel<NB, MW>), dim3(grid), dim3(kShrinkThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -556,7 +552,7 @@ hipError_t launch_shrink_nb(const ShrinkParams& p, int grid, hipStream_t stream)
 // then one workgroup per metadata group.
 template <int NB>
 hipError_t launch_prep_shrink_nb(ShrinkParams p, int grid, hipStream_t stream) {
-  grid = resident_grid(shrink_kernel<NB, 1, true>, kShrinkThreads, grid);
+  grid = resident_grid<shrink_kernel<NB, 1, true>>(kShrinkThreads, grid);
   p.shrink_grid = grid;
   const int total = grid + p.max_loras + 1;
   hipLaunchKernelGGL((shrink_kernel<NB, 1, true>), dim3(total), dim3(kShrinkThreads), 0, stream, p);
@@ -583,9 +579,6 @@ int shrink_group_blocks(int nb_total) { return nb_total <= 8 ? nb_total : 8; }
 // in flight, hidden split across the four waves), four (64-token tiles, the
 // LDS-staged kernel) for larger ones.
 int shrink_tile_blocks(int max_tokens, int nb) {
-#ifdef LORA_TUNING
-  if (const char* e = getenv("LORA_SHRINK_MW")) return atoi(e) >= 4 ? 4 : 1;
-#endif
   if (max_tokens <= 512) return 1;
   return 4;  // the LDS-staged kernel (64-token tiles)
 }

@@ -1,32 +1,45 @@
-"""Per-shape choice of the shrink's hidden-dimension parts, by measurement.
+"""Per-shape launch choices of the multi-LoRA path: a measured table.
 
 vLLM PR #11613 "[Do Not Merge] - LoRA V1 Reference PR" lists autotuning the V1
-LoRA kernels among the follow-up items of its split plan.  The one free launch
-parameter of the shrink + expand pair here is ``num_splits``: the number of
-contiguous hidden-dimension parts the shrink computes separately and the
-expand sums.  More parts spread a batch over more workgroups; fewer parts mean
-fewer partial rows for the expand to read and less start-up per unit.  Where
-the optimum lies depends on how the batch's tiles round against the compute
-units, and the tile count is a property of the batch's adapter mix, known only
-once the batch is grouped.  ``lora_shrink_default_splits`` is a rule on the
-sizes alone; ``tune_shrink_splits`` settles the question for a representative
-batch by timing the pair for each candidate and returning the fastest, to be
-stored with the shape (``num_splits`` fixes the ``buf`` shape, so a captured
-graph keeps the value it was captured with).
+LoRA kernels among the follow-up items of its split plan.  The choices that
+change how the work is cut but never the result are:
 
-This is a host-side utility for an offline tuning step, not part of the path:
-it only calls the library's entry points, allocates its own copies of the
-operands with torch, synchronises, and never writes the caller's tensors.
+* ``num_splits``: the number of contiguous hidden-dimension parts the shrink
+  computes separately and the expand sums.  More parts spread a batch over more
+  workgroups; fewer mean fewer partial rows to read and less start-up per
+  unit.  It fixes the ``buf`` shape, so a captured graph keeps the value it
+  was captured with.
+* the expand's launch choices (``lora_expand_config_t``): the column-range
+  length, the unit order and the workgroups per CU its grid is sized for.
+
+Where the optimum lies depends on how the batch's tiles round against the
+compute units, and the tile count is a property of the batch's adapter mix,
+known only once the batch is grouped, so the library's built-in rules are a
+function of the sizes alone and this module settles each shape by timing the
+candidates on a representative batch.  ``tuning_table.json`` (next to this
+file) holds the result per shape, written by ``python -m
+segmented_rank_gemm_amd.tuning --generate`` on the GPU; ``plan`` returns a
+shape's entry (or the rules), and the binding's ``lora_expand`` /
+``lora_fused_step`` use a shape's expand choices by default.
+
+The timing helpers are host-side utilities for an offline step, not part of
+the path: they only call the library's entry points, allocate their own copies
+of the operands with torch, synchronise, and never write the caller's tensors.
 """
 
 from __future__ import annotations
 
+import argparse
+import json
 import math
+import os
+import sys
+import time
 from typing import Dict, Iterable, List, Optional, Sequence
 
 import torch
 
-from . import (LORA_MAX_SPLITS, LoraMeta, lora_expand, lora_shrink,
+from . import (LORA_MAX_SPLITS, ExpandConfig, LoraMeta, lora_expand, lora_shrink,
                lora_shrink_default_splits)
 
 CHUNK = 64  # hidden elements per step of the shrink kernels; a part is a multiple of it
@@ -111,7 +124,7 @@ def tune_shrink_splits(x: torch.Tensor, lora_a: Sequence[torch.Tensor],
         def pair(i, stream, n=n, bufs=bufs):
             o = ops[i]
             lora_shrink(o["x"], o["a"], scale, bufs[i], n, meta, stream)
-            lora_expand(bufs[i], n, o["b"], o["y"], meta, stream)
+            lora_expand(bufs[i], n, o["b"], o["y"], meta, stream, config=None)
 
         for i in range(copies):  # eager pass first (and a check that the launch is accepted)
             pair(i, None)
@@ -122,3 +135,191 @@ def tune_shrink_splits(x: torch.Tensor, lora_a: Sequence[torch.Tensor],
     torch.cuda.synchronize()
     best = min(us, key=us.get)
     return {"best": best, "default": default, "us": us}
+
+
+# ------------------------------------------------------------------ table
+
+TABLE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tuning_table.json")
+_table_cache: Optional[Dict[str, dict]] = None
+
+
+def shape_key(hidden: int, max_tokens: int, max_loras: int, slices: Sequence[int],
+              rank: int) -> str:
+    """The table key of a shape: the sizes that fix the grids."""
+    return (f"hidden={int(hidden)},max_tokens={int(max_tokens)},max_loras={int(max_loras)},"
+            f"slices={'x'.join(str(int(n)) for n in slices)},rank={int(rank)}")
+
+
+def load_table(path: str = TABLE_PATH) -> Dict[str, dict]:
+    """The committed table ({} if there is none)."""
+    global _table_cache
+    if path == TABLE_PATH and _table_cache is not None:
+        return _table_cache
+    table = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            table = {e["key"]: e for e in json.load(f)["entries"]}
+    if path == TABLE_PATH:
+        _table_cache = table
+    return table
+
+
+def lookup(hidden: int, max_tokens: int, max_loras: int, slices: Sequence[int],
+           rank: int) -> Optional[dict]:
+    """The table's entry for a shape, or None."""
+    return load_table().get(shape_key(hidden, max_tokens, max_loras, slices, rank))
+
+
+def plan(hidden: int, max_tokens: int, max_loras: int, slices: Sequence[int],
+         rank: int) -> dict:
+    """Launch choices for a shape: the table's measured ones where the table
+    has the shape, else the library's size rules.  Returns
+    {"num_splits": n, "expand": ExpandConfig or None, "source": "table" | "size rule"}."""
+    e = lookup(hidden, max_tokens, max_loras, slices, rank)
+    if e is not None:
+        return {"num_splits": int(e["num_splits"]), "expand": ExpandConfig(**e["expand"]),
+                "source": "table"}
+    return {"num_splits": lora_shrink_default_splits(hidden, max_tokens, max_loras, len(slices),
+                                                     rank),
+            "expand": None, "source": "size rule"}
+
+
+def expand_config_for(lora_b: Sequence[torch.Tensor], num_splits: int,
+                      meta: LoraMeta) -> Optional[ExpandConfig]:
+    """The table's expand choices for the call at hand: the entry with the
+    same max_tokens, max_loras, slices and rank whose part count is the call's
+    (the expand reads that many parts; the hidden size does not reach it), or
+    None (the library's rules)."""
+    slices = [int(b.shape[1]) for b in lora_b]
+    rank = int(lora_b[0].shape[2])
+    for e in load_table().values():
+        sh = e.get("shape", {})
+        if (sh.get("max_tokens") == meta.max_tokens and sh.get("max_loras") == meta.max_loras
+                and sh.get("slices") == slices and sh.get("rank") == rank
+                and e.get("num_splits") == int(num_splits)):
+            return ExpandConfig(**e["expand"])
+    return None
+
+
+def _expand_candidates(rank: int) -> List[ExpandConfig]:
+    out = [ExpandConfig()]  # the rules
+    if rank <= 16:
+        for cpr in (1, 2, 3, 4, 8):
+            for order in (0, 1):
+                out.append(ExpandConfig(cpr, order, 0))
+    else:
+        for cpr in (0, 4, 6, 8, 12, 16):
+            for wpc in (1, 2, 3):
+                for order in (0, 1):
+                    out.append(ExpandConfig(cpr, order, wpc))
+    return out
+
+
+def tune_workload(w, reps: int = 20, log=print) -> dict:
+    """Measure the launch choices for one workload's shape on its batch: the
+    whole step (lora_fused_step: one launch where it applies, else
+    lora_prepare_and_shrink + lora_expand), first over the part counts with
+    the expand's rules, then over the expand's choices at the best part count.
+    Graphs over copies of the operands spanning 1 GiB, events on the replay
+    stream.  Returns the table entry."""
+    from workloads.device import to_dev_bf16
+
+    from . import fused_step_workspace, lora_fused_step
+
+    maxT, S, r = w.max_tokens, w.num_slices, w.rank
+    rule = lora_shrink_default_splits(w.hidden, maxT, w.max_loras, S, r)
+    ws = fused_step_workspace(maxT, w.max_loras, S, r)
+    one_launch = ws is not None
+    base = dict(mapping=torch.from_numpy(w.mapping.astype("int32")).cuda(),
+                x=to_dev_bf16(w.x[:maxT]), y=to_dev_bf16(w.y0[:maxT]),
+                a=[to_dev_bf16(a) for a in w.lora_a], b=[to_dev_bf16(b) for b in w.lora_b])
+    per_copy = (base["x"].numel() + base["y"].numel()) * 2 + sum(
+        t.numel() * 2 for t in base["a"] + base["b"])
+    copies = max(2, math.ceil((1 << 30) / per_copy))
+    ops = [dict(mapping=base["mapping"].clone(), x=base["x"].clone(), y=base["y"].clone(),
+                a=[t.clone() for t in base["a"]], b=[t.clone() for t in base["b"]],
+                meta=LoraMeta(maxT, w.max_loras)) for _ in range(copies)]
+
+    def time_step(n, cfg):
+        bufs = [torch.empty((n, S, maxT, r), dtype=torch.float32, device="cuda")
+                for _ in range(copies)]
+
+        def step(i, stream):
+            o = ops[i]
+            lora_fused_step(o["mapping"], w.num_tokens, o["x"], o["a"], o["b"], float(w.scale),
+                            bufs[i], n, o["y"], o["meta"], ws, stream=stream,
+                            expand_config=cfg if cfg is not None else ExpandConfig())
+
+        for i in range(copies):
+            step(i, None)
+        torch.cuda.synchronize()
+        t = _graph_seconds(step, copies, reps) * 1e6
+        del bufs
+        return t
+
+    cands = candidate_splits(w.hidden, maxT, w.max_loras, S, r)
+    if one_launch:
+        cands = sorted({c for c in cands if c >= 4} | ({rule, 20, 24, 32} & set(range(1, 65))))
+    us_splits = {}
+    for n in cands:
+        us_splits[n] = time_step(n, None)
+        log(f"[tune] {w.name} splits={n}: {us_splits[n]:.2f} us")
+    best_n = min(us_splits, key=us_splits.get)
+    us_expand = {}
+    best_cfg = ExpandConfig()
+    if not one_launch:
+        for cfg in _expand_candidates(r):
+            key = json.dumps(cfg.as_dict(), sort_keys=True)
+            us_expand[key] = time_step(best_n, cfg)
+            log(f"[tune] {w.name} splits={best_n} expand={key}: {us_expand[key]:.2f} us")
+        best_key = min(us_expand, key=us_expand.get)
+        best_cfg = ExpandConfig(**json.loads(best_key))
+    best_us = min(us_expand.values()) if us_expand else us_splits[best_n]
+    del ops
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {
+        "key": shape_key(w.hidden, maxT, w.max_loras, w.slices, r),
+        "shape": {"hidden": int(w.hidden), "max_tokens": int(maxT), "max_loras": int(w.max_loras),
+                  "slices": [int(n) for n in w.slices], "rank": int(r)},
+        "workload": w.name,
+        "num_splits": int(best_n),
+        "expand": best_cfg.as_dict(),
+        "step_us": round(best_us, 3),
+        "rule": {"num_splits": int(rule), "step_us": round(us_splits.get(rule, float("nan")), 3)},
+        "step_us_by_splits": {str(k): round(v, 3) for k, v in us_splits.items()},
+        "step_us_by_expand": {k: round(v, 3) for k, v in us_expand.items()},
+    }
+
+
+def generate(configs: Sequence[int], path: str = TABLE_PATH, reps: int = 20) -> None:
+    """Tune the given benchmark workloads and write the table (entries for
+    other shapes already in the file are kept)."""
+    from workloads import make_workload
+
+    table = dict(load_table(path)) if os.path.exists(path) else {}
+    for c in configs:
+        w = make_workload(c)
+        e = tune_workload(w, reps=reps, log=lambda *a: print(*a, file=sys.stderr, flush=True))
+        table[e["key"]] = e
+    out = {"device": torch.cuda.get_device_properties(0).gcnArchName,
+           "generated_by": "python -m segmented_rank_gemm_amd.tuning --generate",
+           "date": time.strftime("%Y-%m-%d"),
+           "entries": sorted(table.values(), key=lambda e: e["key"])}
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser(description="measure per-shape launch choices into the table")
+    ap.add_argument("--generate", action="store_true")
+    ap.add_argument("--configs", default="1,2,3,4")
+    ap.add_argument("--out", default=TABLE_PATH)
+    ap.add_argument("--reps", type=int, default=20)
+    a = ap.parse_args()
+    if a.generate:
+        root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+        if root not in sys.path:
+            sys.path.insert(0, root)
+        generate([int(c) for c in a.configs.split(",")], a.out, a.reps)

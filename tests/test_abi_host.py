@@ -126,8 +126,10 @@ def _expand(**kw):
     a.update(kw)
     bptr = a["b"] if not isinstance(a["b"], int) else _ptrs(a["b"])
     sizes = (ctypes.c_int32 * len(a["sizes"]))(*a["sizes"]) if a["sizes"] is not None else None
+    cfg = a.get("config")
+    cfg = ctypes.byref(srg.ExpandConfig(*cfg)) if cfg is not None else None
     return srg.lib().lora_expand(a["buf"], a["splits"], bptr, sizes, a["S"], a["rank"], a["y"],
-                                 a["ldy"], _meta(), a["maxT"], a["L"], None)
+                                 a["ldy"], _meta(), a["maxT"], a["L"], cfg, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -135,6 +137,12 @@ def _expand(**kw):
     (dict(sizes=(4096, 4096, 4092)), 1), (dict(sizes=(4096, 0, 4096)), 1), (dict(ldy=12280), 1),
     (dict(ldy=12290), 1), (dict(S=0), 1), (dict(S=5), 1), (dict(splits=0), 1),
     (dict(b=_ptrs(3, None)), 1), (dict(rank=80), 1), (dict(rank=24), 2),
+    # launch choices out of range
+    (dict(config=(-1, -1, 0)), 1), (dict(config=(65, -1, 0)), 1), (dict(config=(0, 2, 0)), 1),
+    (dict(config=(0, -2, 0)), 1), (dict(config=(0, -1, 17)), 1), (dict(config=(0, -1, -1)), 1),
+    (dict(rank=32, config=(17, -1, 0)), 1),
+    # in range, but an unsupported rank still refuses
+    (dict(rank=24, config=(4, 1, 2)), 2),
 ])
 def test_expand_rejects(kw, status):
     assert _expand(**kw) == status
@@ -238,3 +246,13 @@ def test_fused_step_static_rejects_before_any_lookup():
              a["buf"], 16, a["y"], a["ldy"], _meta(), None, 256, 4, None) == 2   # rank 12
     assert f(None, 200, a["x"], a["ldx"], a["hidden"], _ptrs(3), _ptrs(3), sizes, 3, 8, 1.0,
              a["buf"], 16, a["y"], a["ldy"], _meta(), None, 256, 4, None) == 1   # no map
+
+
+@pytest.mark.parametrize("num_tokens,max_tokens,max_loras,meta", [
+    (-1, 16, 4, None), (17, 16, 4, None), (4, 16, 257, None), (4, 16, 4, dict(num_runs=None)),
+])
+def test_prepare_metadata_grouped_rejects(num_tokens, max_tokens, max_loras, meta):
+    m = _meta(**(meta or {}))
+    assert srg.lib().lora_prepare_metadata_grouped(FAKE, num_tokens, max_tokens, max_loras, m,
+                                                   None) == 1
+    assert srg.lib().lora_prepare_metadata_grouped(None, 3, 16, 4, _meta(), None) == 1
