@@ -10,8 +10,9 @@
 // over the map, O(T) work in all (the general kernel has max_loras + 1
 // workgroups each read the whole map).
 //
-// One workgroup of 1024 threads:
-//  1. blocks of 8192 tokens (8 per thread, in registers): a run starts where a
+// One workgroup (64, 256, 512 or 1024 threads: the fewest whose 8-token-per-
+// thread block holds the batch, as for the metadata kernel):
+//  1. blocks of 8 tokens per thread (in registers): a run starts where a
 //     token's group (0: no adapter, id + 1 otherwise; ids outside
 //     [-1, max_loras) count as no adapter) differs from the previous token's;
 //     run starts are numbered in batch order by a block-wide scan of per-thread
@@ -32,23 +33,27 @@
 
 namespace lora {
 
-constexpr int kGroupedThreads = 1024;
-constexpr int kGroupedWaves = kGroupedThreads / kWave;
-constexpr int kGroupedBlock = kGroupedThreads * kPerThread;
 constexpr int kMaxGroups = LORA_MAX_LORAS + 1;
 
 // Block-wide exclusive sum of v >= 0 over the workgroup's threads (thread
-// order); also the total.  Uses `wsum` (kGroupedWaves ints of LDS).
+// order); also the total.  Uses `wsum` (one int of LDS per wave).  A
+// one-wave workgroup needs no barrier.
+template <int THREADS>
 __device__ __forceinline__ int block_exclusive_sum(int v, int* wsum, int& total) {
+  constexpr int kWaves = THREADS / kWave;
+  const int ex = wave_exclusive_sum(v);
+  if constexpr (kWaves == 1) {
+    total = __builtin_amdgcn_readlane(ex + v, kWave - 1);
+    return ex;
+  }
   const int lane = lane_id();
   const int wave = wave_index();
-  const int ex = wave_exclusive_sum(v);
   if (lane == kWave - 1) wsum[wave] = ex + v;
   __syncthreads();
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < kGroupedWaves; ++w) {
+  for (int w = 0; w < kWaves; ++w) {
     const int n = wsum[w];
     before += w < wave ? n : 0;
     total += n;
@@ -84,8 +89,10 @@ __device__ __forceinline__ void store_positions(int32_t* dst, int p0, int n,
   }
 }
 
-__global__ __launch_bounds__(kGroupedThreads) void metadata_grouped_kernel(
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void metadata_grouped_kernel(
     const int32_t* __restrict__ mapping, int num_tokens, int max_loras, MetaOut out) {
+  constexpr int kBlock = THREADS * kPerThread;
   __shared__ int run_pos[kMaxGroups + 1];
   __shared__ int run_grp[kMaxGroups];
   __shared__ int g_cnt[kMaxGroups];    // tokens per group
@@ -96,12 +103,12 @@ __global__ __launch_bounds__(kGroupedThreads) void metadata_grouped_kernel(
   __shared__ int k_cnt[kMaxGroups];
   __shared__ int k_pos[kMaxGroups];
   __shared__ int k_id[kMaxGroups];
-  __shared__ int wsum[kGroupedWaves];
+  __shared__ int wsum[THREADS / kWave];
   __shared__ int s_runs, s_bad;
 
   const int tid = threadIdx.x;
   const int groups = max_loras + 1;
-  for (int g = tid; g < groups; g += kGroupedThreads) {
+  for (int g = tid; g < groups; g += THREADS) {
     g_cnt[g] = 0;
     g_runs[g] = 0;
   }
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(kGroupedThreads) void metadata_grouped_kernel(
   __syncthreads();
 
   // 1. run starts, numbered in batch order
-  for (int b0 = 0; b0 < num_tokens; b0 += kGroupedBlock) {
+  for (int b0 = 0; b0 < num_tokens; b0 += kBlock) {
     const int t0 = b0 + tid * kPerThread;
     int grp[kPerThread];
     load_groups(mapping, num_tokens, max_loras, t0, grp);
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(kGroupedThreads) void metadata_grouped_kernel(
     }
     int total = 0;
     const int mine = __builtin_popcount(starts);
-    const int ex = block_exclusive_sum(mine, wsum, total);
+    const int ex = block_exclusive_sum<THREADS>(mine, wsum, total);
     const int base = s_runs;  // (read before the update below, after the scan's barriers)
     if (base + total > groups) {
       if (tid == 0) s_bad = 1;  // more runs than groups: some group has two
@@ -151,44 +158,61 @@ __global__ __launch_bounds__(kGroupedThreads) void metadata_grouped_kernel(
   const int runs = s_runs;
   if (!s_bad) {
     if (tid == 0) run_pos[runs] = num_tokens;
-    for (int r = tid; r < runs; r += kGroupedThreads)
+    for (int r = tid; r < runs; r += THREADS)
       if (atomicAdd(&g_runs[run_grp[r]], 1) > 0) s_bad = 1;  // benign: every writer stores 1
     __syncthreads();
   }
   if (s_bad) {
     // 4. not grouped: the general code, group by group
-    for (int g = 0; g < groups; ++g) metadata_group<kGroupedThreads>(mapping, num_tokens, max_loras, out, g);
+    for (int g = 0; g < groups; ++g) metadata_group<THREADS>(mapping, num_tokens, max_loras, out, g);
     return;
   }
 
   // 3. grouped
-  for (int r = tid; r < runs; r += kGroupedThreads) {
+  for (int r = tid; r < runs; r += THREADS) {
     const int g = run_grp[r];
     g_cnt[g] = run_pos[r + 1] - run_pos[r];
     g_pos[g] = run_pos[r];
   }
   __syncthreads();
-  // starts (all groups) and slots (groups of adapters present), one thread
-  // per group (groups <= 257 < 1024 threads)
-  const int gc = tid < groups ? g_cnt[tid] : 0;
-  const bool present = tid >= 1 && tid < groups && gc > 0;
-  int ngroups_tokens = 0, npresent = 0;
-  const int start = block_exclusive_sum(gc, wsum, ngroups_tokens);
-  const int slot = block_exclusive_sum(present ? 1 : 0, wsum, npresent);
-  if (tid < groups) g_start[tid] = start;
-  const int n_none = g_cnt[0];
-  int pstart = 0;
-  if (present) {
-    pstart = round_up_tile(start - n_none + (kMetaTile - 1) * slot);
-    k_pstart[slot] = pstart;
-    k_cnt[slot] = gc;
-    k_pos[slot] = g_pos[tid];
-    k_id[slot] = tid - 1;
-    out.active_ids[slot] = tid - 1;
-    out.counts[slot] = gc;
-    out.starts[slot] = start;
+  // starts (all groups) and slots (groups of adapters present): each thread
+  // takes a contiguous range of groups, sums it, and the ranges' sums are
+  // scanned across the workgroup
+  constexpr int kMaxPer = (kMaxGroups + THREADS - 1) / THREADS;
+  const int per = (groups + THREADS - 1) / THREADS;
+  const int g0 = tid * per;
+  int tok_sum = 0, pres_sum = 0;
+  for (int i = 0; i < per; ++i) {
+    const int g = g0 + i;
+    if (g < groups) {
+      tok_sum += g_cnt[g];
+      pres_sum += (g >= 1 && g_cnt[g] > 0) ? 1 : 0;
+    }
   }
-  for (int i = npresent + tid; i < max_loras; i += kGroupedThreads) {
+  int ngroups_tokens = 0, npresent = 0;
+  int start = block_exclusive_sum<THREADS>(tok_sum, wsum, ngroups_tokens);
+  int slot = block_exclusive_sum<THREADS>(pres_sum, wsum, npresent);
+  const int n_none = g_cnt[0];
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int g = g0 + i;
+    if (i < per && g < groups) {
+      const int gc = g_cnt[g];
+      g_start[g] = start;
+      if (g >= 1 && gc > 0) {
+        k_pstart[slot] = round_up_tile(start - n_none + (kMetaTile - 1) * slot);
+        k_cnt[slot] = gc;
+        k_pos[slot] = g_pos[g];
+        k_id[slot] = g - 1;
+        out.active_ids[slot] = g - 1;
+        out.counts[slot] = gc;
+        out.starts[slot] = start;
+        ++slot;
+      }
+      start += gc;
+    }
+  }
+  for (int i = npresent + tid; i < max_loras; i += THREADS) {
     out.active_ids[i] = -1;
     out.counts[i] = 0;
     out.starts[i] = num_tokens;
@@ -206,7 +230,7 @@ __global__ __launch_bounds__(kGroupedThreads) void metadata_grouped_kernel(
   // first (the last group whose start is <= p: an empty group shares its start
   // with the next non-empty group, which comes later), then a walk forward;
   // 16-byte stores where the 8 positions are whole and aligned.
-  for (int p0 = kPerThread * tid; p0 < num_tokens; p0 += kGroupedBlock) {
+  for (int p0 = kPerThread * tid; p0 < num_tokens; p0 += kBlock) {
     int g = last_le(g_start, groups, p0);
     int v[kPerThread];
 #pragma unroll
@@ -221,7 +245,7 @@ __global__ __launch_bounds__(kGroupedThreads) void metadata_grouped_kernel(
   // padded start is <= q, or in the gap after it
   if (npresent > 0) {
     const int nq = num_tiles * kMetaTile;
-    for (int q0 = kPerThread * tid; q0 < nq; q0 += kGroupedBlock) {
+    for (int q0 = kPerThread * tid; q0 < nq; q0 += kBlock) {
       int k = last_le(k_pstart, npresent, q0);
       int v[kPerThread];
 #pragma unroll
@@ -233,7 +257,7 @@ __global__ __launch_bounds__(kGroupedThreads) void metadata_grouped_kernel(
       }
       store_positions(out.tile_ids, q0, nq, v);
     }
-    for (int m = tid; m < num_tiles; m += kGroupedThreads) {
+    for (int m = tid; m < num_tiles; m += THREADS) {
       const int k = last_le(k_pstart, npresent, kMetaTile * m);
       out.tile_lora[m] = kMetaTile * m - k_pstart[k] < k_cnt[k] ? k_id[k] : -1;
     }
@@ -242,12 +266,22 @@ __global__ __launch_bounds__(kGroupedThreads) void metadata_grouped_kernel(
 
 hipError_t launch_metadata_grouped(const int32_t* mapping, int num_tokens, int max_tokens,
                                    int max_loras, const lora_meta_t& meta, hipStream_t stream) {
-  (void)max_tokens;
   const MetaOut out{meta.sorted_token_ids, meta.active_lora_ids, meta.num_tokens_per_lora,
                     meta.lora_token_start, meta.num_active, meta.tile_token_ids,
                     meta.tile_lora, meta.num_tiles, meta.num_runs};
-  hipLaunchKernelGGL(metadata_grouped_kernel, dim3(1), dim3(kGroupedThreads), 0, stream, mapping,
-                     num_tokens, max_loras, out);
+  if (max_tokens <= 64 * kPerThread) {
+    hipLaunchKernelGGL(metadata_grouped_kernel<64>, dim3(1), dim3(64), 0, stream, mapping,
+                       num_tokens, max_loras, out);
+  } else if (max_tokens <= 256 * kPerThread) {
+    hipLaunchKernelGGL(metadata_grouped_kernel<256>, dim3(1), dim3(256), 0, stream, mapping,
+                       num_tokens, max_loras, out);
+  } else if (max_tokens <= 512 * kPerThread) {
+    hipLaunchKernelGGL(metadata_grouped_kernel<512>, dim3(1), dim3(512), 0, stream, mapping,
+                       num_tokens, max_loras, out);
+  } else {
+    hipLaunchKernelGGL(metadata_grouped_kernel<1024>, dim3(1), dim3(1024), 0, stream, mapping,
+                       num_tokens, max_loras, out);
+  }
   return hipGetLastError();
 }
 
