@@ -113,7 +113,7 @@ class Sets:
     """R device copies of one workload's buffers, plus the per-copy metadata;
     every expand call takes the given launch choices."""
 
-    def __init__(self, w, R, num_splits, expand_cfg=None):
+    def __init__(self, w, R, num_splits, expand_cfg=None, start_delay_ns=None):
         import torch
 
         import segmented_rank_gemm_amd as srg
@@ -121,6 +121,7 @@ class Sets:
 
         self.w, self.R, self.num_splits = w, R, num_splits
         self.expand_cfg = expand_cfg
+        self.start_delay_ns = start_delay_ns  # None: the library's default
         T, maxT = w.num_tokens, w.max_tokens
         base = dict(
             mapping=torch.from_numpy(w.mapping.astype("int32")).cuda(),
@@ -197,7 +198,7 @@ class Sets:
         m = s["meta"] if meta_r is None else self.sets[meta_r]["meta"]
         srg.lora_fused_step(s["mapping"], self.T, s["x"], s["a"], s["b"], float(self.w.scale),
                             s["buf"], self.num_splits, s["y"], m, self.workspace, stream=stream,
-                            expand_config=self.expand_cfg)
+                            expand_config=self.expand_cfg, start_delay_ns=self.start_delay_ns)
 
     def step(self, r, stream=None):
         """The whole path: lora_fused_step."""
@@ -324,13 +325,14 @@ def run_config(idx, args):
                                                  w.num_slices, w.rank)
     pl = plan(w.hidden, w.max_tokens, w.max_loras, w.slices, w.rank)
     if args.rules:
-        pl = {"num_splits": rule_splits, "expand": srg.ExpandConfig(), "source": "size rule"}
+        pl = {"num_splits": rule_splits, "expand": srg.ExpandConfig(), "start_delay_ns": None,
+              "source": "size rule"}
     splits = pl["num_splits"]
     expand_cfg = pl["expand"] or srg.ExpandConfig()
     sb = set_bytes(w, splits)
     R = args.rotate or max(2, math.ceil(ROTATE_BYTES / sb))
     log(f"[bench] {R} rotated buffer sets of {sb / 1e6:.1f} MB, {splits} shrink parts")
-    sets = Sets(w, R, splits, expand_cfg)
+    sets = Sets(w, R, splits, expand_cfg, pl["start_delay_ns"])
 
     # eager pass on every set so the metadata exists before single-kernel graphs replay
     for r in range(R):
@@ -504,6 +506,7 @@ def run_config(idx, args):
             "scale": w.scale, "accumulate": "fp32", "shrink_parts": splits,
             "shrink_parts_from": pl["source"], "shrink_parts_rule": rule_splits,
             "expand_config": expand_cfg.as_dict(), "expand_config_from": pl["source"],
+            "start_delay_ns": pl["start_delay_ns"] if pl["start_delay_ns"] is not None else "default",
             "rotated_sets": R, "rotated_sets_per_kernel": rot, "parallelism": "single GPU",
         },
         "roofline": {

@@ -344,6 +344,12 @@ typedef struct lora_step_options {
   int32_t wait_polls;
   /* Launch choices of the expand on the multi-launch path (see lora_expand). */
   lora_expand_config_t expand;
+  /* One-launch path: how long (ns) each expand workgroup holds its own y and
+   * B loads back after it starts, so that the shrink workgroups' loads, which
+   * share each CU's fetch path with them, are served first.  Changes timing
+   * only, never results.  Negative: a default from the shrink's per-workgroup
+   * bytes; 0: no hold-off; above 100000: LORA_ERR_INVALID_ARGUMENT. */
+  int32_t start_delay_ns;
 } lora_step_options_t;
 
 int64_t lora_fused_step_workspace_bytes(int32_t max_tokens, int32_t max_loras,

@@ -70,7 +70,8 @@ class ExpandConfig(ctypes.Structure):
 
 
 class _StepOptions(ctypes.Structure):
-    _fields_ = [("wait_polls", ctypes.c_int32), ("expand", ExpandConfig)]
+    _fields_ = [("wait_polls", ctypes.c_int32), ("expand", ExpandConfig),
+                ("start_delay_ns", ctypes.c_int32)]
 
 
 def _expand_config(config, lora_b=None, num_splits=None, meta=None) -> Optional[ExpandConfig]:
@@ -87,12 +88,27 @@ def _expand_config(config, lora_b=None, num_splits=None, meta=None) -> Optional[
     return ExpandConfig(**config)
 
 
-def _step_options(wait_polls, expand_config, lora_b=None, num_splits=None, meta=None):
+def _start_delay(start_delay_ns, lora_b=None, num_splits=None, meta=None) -> Optional[int]:
+    """None: the library's default; "table": the measured choice for the call's
+    shape in segmented_rank_gemm_amd/tuning_table.json (the default if the
+    table does not have it); else nanoseconds."""
+    if isinstance(start_delay_ns, str):
+        if start_delay_ns != "table":
+            raise ValueError(f"start delay {start_delay_ns!r}: expected 'table', None or ns")
+        from .tuning import start_delay_for
+        return start_delay_for(lora_b, num_splits, meta)
+    return None if start_delay_ns is None else int(start_delay_ns)
+
+
+def _step_options(wait_polls, expand_config, start_delay_ns=None, lora_b=None, num_splits=None,
+                  meta=None):
     cfg = _expand_config(expand_config, lora_b, num_splits, meta)
-    if wait_polls is None and cfg is None:
+    delay = _start_delay(start_delay_ns, lora_b, num_splits, meta)
+    if wait_polls is None and cfg is None and delay is None:
         return None
     cfg = cfg or ExpandConfig()
-    return ctypes.byref(_StepOptions(-1 if wait_polls is None else int(wait_polls), cfg))
+    return ctypes.byref(_StepOptions(-1 if wait_polls is None else int(wait_polls), cfg,
+                                     -1 if delay is None else delay))
 
 
 TILE = 16  # positions per tile of the padded grouped order (LORA_TILE)
@@ -335,10 +351,12 @@ def lora_fused_step(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.
                     lora_a: Sequence[torch.Tensor], lora_b: Sequence[torch.Tensor], scale: float,
                     buf: torch.Tensor, num_splits: int, y: torch.Tensor, meta: LoraMeta,
                     workspace: Optional[torch.Tensor], wait_polls: Optional[int] = None,
-                    stream: Optional[torch.cuda.Stream] = None, expand_config="table") -> None:
+                    stream: Optional[torch.cuda.Stream] = None, expand_config="table",
+                    start_delay_ns="table") -> None:
     """Metadata, shrink and expand of one batch (one launch where the sizes
     allow); arguments as for lora_prepare_and_shrink and lora_expand, plus the
-    zero-filled workspace of fused_step_workspace (reused call after call)."""
+    zero-filled workspace of fused_step_workspace (reused call after call).
+    start_delay_ns: the one-launch path's expand hold-off (timing only)."""
     ptr = _mapping_ptr(token_lora_mapping, num_tokens)
     S, rank, hidden, aptrs = _shrink_args(x, lora_a, buf, num_splits, meta)
     Sb, rank_b, bptrs, nsz = _expand_args(buf, num_splits, lora_b, y, meta)
@@ -347,7 +365,7 @@ def lora_fused_step(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.
     wptr, wbytes = 0, 0
     if workspace is not None:
         wptr, wbytes = _flat_dev_bytes(workspace, "workspace")
-    opts = _step_options(wait_polls, expand_config, lora_b, num_splits, meta)
+    opts = _step_options(wait_polls, expand_config, start_delay_ns, lora_b, num_splits, meta)
     _check("lora_fused_step", lib().lora_fused_step(
         ptr, int(num_tokens), _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), hidden, aptrs,
         bptrs, nsz, S, rank, float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits),
@@ -359,7 +377,8 @@ def lora_fused_step_static(token_lora_mapping: torch.Tensor, num_tokens: int, x:
                            lora_a: Sequence[torch.Tensor], lora_b: Sequence[torch.Tensor],
                            scale: float, buf: torch.Tensor, num_splits: int, y: torch.Tensor,
                            meta: LoraMeta, wait_polls: Optional[int] = None,
-                           stream: Optional[torch.cuda.Stream] = None, expand_config="table") -> None:
+                           stream: Optional[torch.cuda.Stream] = None, expand_config="table",
+                           start_delay_ns="table") -> None:
     """lora_fused_step with the library's own counter array instead of a
     workspace (nothing is allocated; calls that overlap on one GPU race)."""
     ptr = _mapping_ptr(token_lora_mapping, num_tokens)
@@ -367,7 +386,7 @@ def lora_fused_step_static(token_lora_mapping: torch.Tensor, num_tokens: int, x:
     Sb, rank_b, bptrs, nsz = _expand_args(buf, num_splits, lora_b, y, meta)
     if Sb != S or rank_b != rank:
         raise ValueError("lora_a and lora_b disagree on slices or rank")
-    opts = _step_options(wait_polls, expand_config, lora_b, num_splits, meta)
+    opts = _step_options(wait_polls, expand_config, start_delay_ns, lora_b, num_splits, meta)
     _check("lora_fused_step_static", lib().lora_fused_step_static(
         ptr, int(num_tokens), _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), hidden, aptrs,
         bptrs, nsz, S, rank, float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits),

@@ -105,6 +105,7 @@ struct TokenParams {
   int expand_grid;   // workgroups of the expand (a multiple of 8)
   int* counters;     // [tiles][kCounterInts]
   int wait_polls;
+  int start_delay_ticks;  // expand units' hold-off before their first loads, 100 MHz ticks
   MetaOut meta_out;  // written by the workgroups past shrink_grid + expand_grid
 };
 
@@ -394,6 +395,17 @@ __device__ __forceinline__ void token_expand_unit(const TokenParams& p, int u, u
 #pragma unroll
       for (int j = 0; j < 4; ++j) yb.v[j] = load16_stream(p.y + yrow[j] + ycolc);
     };
+    // Hold this unit's y and B loads back while the shrink units' loads are
+    // served: they share each CU's fetch path with them, and the parts the
+    // unit waits for come sooner that way; y and B still arrive before the
+    // parts do.  Timed on the chip's constant 100 MHz clock.
+    if (p.start_delay_ticks > 0) {
+      const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+      while (__builtin_amdgcn_s_memrealtime() - t_start <
+             static_cast<uint64_t>(p.start_delay_ticks))
+        __builtin_amdgcn_s_sleep(2);
+      asm volatile("" ::: "memory");
+    }
     load_b();
     load_y();
 
@@ -772,13 +784,23 @@ hipError_t launch_token_prep_shrink(const int32_t* mapping, int num_tokens, cons
   return launch_token_nb<8, 4, false>(p, nb, stream);
 }
 
+// Default hold-off of the expand units (ns): the time a shrink unit's own
+// loads take to arrive, about 30 ns per KB of A and x it reads (measured on
+// the decode batch: a unit reading 56 KB, best at 1.5-1.9 us, 5% off the
+// step; the time is flat within +-0.2 us of the best and grows fast past it).
+static int token_step_default_delay_ns(const TokenParams& p, int nb) {
+  const int64_t bytes = static_cast<int64_t>(16 * nb + kTokTile * kTokShrinkMw) * p.split_len * 2;
+  return static_cast<int>(30 * bytes / 1024);
+}
+
 // The one-launch step.  The caller checked token_step_fits and the workspace.
 hipError_t launch_token_step(const int32_t* mapping, int num_tokens, const uint16_t* x,
                              int64_t ldx, int hidden, const uint16_t* const* lora_a,
                              const uint16_t* const* lora_b, const int32_t* slice_sizes,
                              int num_slices, int rank, float scale, float* buf, int num_splits,
                              uint16_t* y, int64_t ldy, const lora_meta_t& meta, int* counters,
-                             int wait_polls, int max_tokens, int max_loras, hipStream_t stream) {
+                             int wait_polls, int start_delay_ns, int max_tokens, int max_loras,
+                             hipStream_t stream) {
   int nb = 2;
   TokenParams p = token_params(mapping, num_tokens, x, ldx, hidden, lora_a, num_slices, rank,
                                scale, buf, num_splits, meta, max_tokens, max_loras, nb);
@@ -805,6 +827,8 @@ hipError_t launch_token_step(const int32_t* mapping, int num_tokens, const uint1
   p.expand_grid = (p.expand_units + kXcds - 1) / kXcds * kXcds;
   p.counters = counters;
   p.wait_polls = wait_polls;
+  if (start_delay_ns < 0) start_delay_ns = token_step_default_delay_ns(p, nb);
+  p.start_delay_ticks = (start_delay_ns + 5) / 10;
   if (rank == 8) {
     return max_loras <= 4 ? launch_token_nb<8, 4, true>(p, nb, stream)
                           : launch_token_nb<8, 8, true>(p, nb, stream);

@@ -11,6 +11,9 @@ change how the work is cut but never the result are:
   was captured with.
 * the expand's launch choices (``lora_expand_config_t``): the column-range
   length, the unit order and the workgroups per CU its grid is sized for.
+* on the one-launch path, how long the expand workgroups hold their own loads
+  back so that the shrink workgroups' loads are served first
+  (``lora_step_options_t.start_delay_ns``).
 
 Where the optimum lies depends on how the batch's tiles round against the
 compute units, and the tile count is a property of the batch's adapter mix,
@@ -20,7 +23,7 @@ candidates on a representative batch.  ``tuning_table.json`` (next to this
 file) holds the result per shape, written by ``python -m
 segmented_rank_gemm_amd.tuning --generate`` on the GPU; ``plan`` returns a
 shape's entry (or the rules), and the binding's ``lora_expand`` /
-``lora_fused_step`` use a shape's expand choices by default.
+``lora_fused_step`` use a shape's expand choices and hold-off by default.
 
 The timing helpers are host-side utilities for an offline step, not part of
 the path: they only call the library's entry points, allocate their own copies
@@ -174,22 +177,22 @@ def plan(hidden: int, max_tokens: int, max_loras: int, slices: Sequence[int],
          rank: int) -> dict:
     """Launch choices for a shape: the table's measured ones where the table
     has the shape, else the library's size rules.  Returns
-    {"num_splits": n, "expand": ExpandConfig or None, "source": "table" | "size rule"}."""
+    {"num_splits": n, "expand": ExpandConfig or None, "start_delay_ns": ns or None,
+     "source": "table" | "size rule"}."""
     e = lookup(hidden, max_tokens, max_loras, slices, rank)
     if e is not None:
+        delay = e.get("start_delay_ns")
         return {"num_splits": int(e["num_splits"]), "expand": ExpandConfig(**e["expand"]),
-                "source": "table"}
+                "start_delay_ns": None if delay is None else int(delay), "source": "table"}
     return {"num_splits": lora_shrink_default_splits(hidden, max_tokens, max_loras, len(slices),
                                                      rank),
-            "expand": None, "source": "size rule"}
+            "expand": None, "start_delay_ns": None, "source": "size rule"}
 
 
-def expand_config_for(lora_b: Sequence[torch.Tensor], num_splits: int,
-                      meta: LoraMeta) -> Optional[ExpandConfig]:
-    """The table's expand choices for the call at hand: the entry with the
-    same max_tokens, max_loras, slices and rank whose part count is the call's
-    (the expand reads that many parts; the hidden size does not reach it), or
-    None (the library's rules)."""
+def _entry_for(lora_b: Sequence[torch.Tensor], num_splits: int, meta: LoraMeta) -> Optional[dict]:
+    """The table entry with the call's max_tokens, max_loras, slices and rank
+    whose part count is the call's (the expand reads that many parts; the
+    hidden size does not reach it), or None."""
     slices = [int(b.shape[1]) for b in lora_b]
     rank = int(lora_b[0].shape[2])
     for e in load_table().values():
@@ -197,8 +200,29 @@ def expand_config_for(lora_b: Sequence[torch.Tensor], num_splits: int,
         if (sh.get("max_tokens") == meta.max_tokens and sh.get("max_loras") == meta.max_loras
                 and sh.get("slices") == slices and sh.get("rank") == rank
                 and e.get("num_splits") == int(num_splits)):
-            return ExpandConfig(**e["expand"])
+            return e
     return None
+
+
+def expand_config_for(lora_b: Sequence[torch.Tensor], num_splits: int,
+                      meta: LoraMeta) -> Optional[ExpandConfig]:
+    """The table's expand choices for the call at hand, or None (the
+    library's rules)."""
+    e = _entry_for(lora_b, num_splits, meta)
+    return None if e is None else ExpandConfig(**e["expand"])
+
+
+def start_delay_for(lora_b: Sequence[torch.Tensor], num_splits: int,
+                    meta: LoraMeta) -> Optional[int]:
+    """The table's one-launch expand hold-off (ns) for the call at hand, or
+    None (the library's default)."""
+    e = _entry_for(lora_b, num_splits, meta)
+    if e is None or e.get("start_delay_ns") is None:
+        return None
+    return int(e["start_delay_ns"])
+
+
+_DELAY_CANDIDATES_NS = (0, 800, 1000, 1200, 1400, 1600, 1800, 2000, 2200, 2600)
 
 
 def _expand_candidates(rank: int) -> List[ExpandConfig]:
@@ -240,7 +264,7 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
                 a=[t.clone() for t in base["a"]], b=[t.clone() for t in base["b"]],
                 meta=LoraMeta(maxT, w.max_loras)) for _ in range(copies)]
 
-    def time_step(n, cfg):
+    def time_step(n, cfg, delay=None):
         bufs = [torch.empty((n, S, maxT, r), dtype=torch.float32, device="cuda")
                 for _ in range(copies)]
 
@@ -248,7 +272,8 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
             o = ops[i]
             lora_fused_step(o["mapping"], w.num_tokens, o["x"], o["a"], o["b"], float(w.scale),
                             bufs[i], n, o["y"], o["meta"], ws, stream=stream,
-                            expand_config=cfg if cfg is not None else ExpandConfig())
+                            expand_config=cfg if cfg is not None else ExpandConfig(),
+                            start_delay_ns=delay)
 
         for i in range(copies):
             step(i, None)
@@ -274,7 +299,19 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
             log(f"[tune] {w.name} splits={best_n} expand={key}: {us_expand[key]:.2f} us")
         best_key = min(us_expand, key=us_expand.get)
         best_cfg = ExpandConfig(**json.loads(best_key))
-    best_us = min(us_expand.values()) if us_expand else us_splits[best_n]
+    # the one-launch path's expand hold-off, at the best part count (None:
+    # the library's default from the shrink's per-workgroup bytes)
+    us_delay = {}
+    best_delay = None
+    if one_launch:
+        us_delay["default"] = us_splits[best_n]
+        for d in _DELAY_CANDIDATES_NS:
+            us_delay[str(d)] = time_step(best_n, None, d)
+            log(f"[tune] {w.name} splits={best_n} start_delay_ns={d}: {us_delay[str(d)]:.2f} us")
+        best_key = min(us_delay, key=us_delay.get)
+        best_delay = None if best_key == "default" else int(best_key)
+    best_us = min(us_expand.values()) if us_expand else (
+        min(us_delay.values()) if us_delay else us_splits[best_n])
     del ops
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -285,10 +322,12 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
         "workload": w.name,
         "num_splits": int(best_n),
         "expand": best_cfg.as_dict(),
+        "start_delay_ns": best_delay,
         "step_us": round(best_us, 3),
         "rule": {"num_splits": int(rule), "step_us": round(us_splits.get(rule, float("nan")), 3)},
         "step_us_by_splits": {str(k): round(v, 3) for k, v in us_splits.items()},
         "step_us_by_expand": {k: round(v, 3) for k, v in us_expand.items()},
+        "step_us_by_start_delay_ns": {k: round(v, 3) for k, v in us_delay.items()},
     }
 
 

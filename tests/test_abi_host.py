@@ -229,6 +229,15 @@ def test_fused_step_rejects(kw):
     assert _fused(**kw) == 1
 
 
+def test_fused_step_rejects_long_start_delay():
+    # lora_step_options_t: wait_polls, then the three ints of the expand's
+    # config, then start_delay_ns
+    O = srg._StepOptions
+    assert (O.wait_polls.offset, O.expand.offset, O.start_delay_ns.offset) == (0, 4, 16)
+    assert ctypes.sizeof(O) == 20
+    assert _fused(options=ctypes.byref(O(-1, srg.ExpandConfig(), 100001))) == 1
+
+
 def test_fused_step_rejects_unsupported_rank():
     # rank 12: valid range, no kernel for it (checked before anything is enqueued)
     assert _fused(rank=12) == 2

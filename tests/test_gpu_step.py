@@ -33,10 +33,10 @@ def _workspace(w):
     return srg.fused_step_workspace(w.max_tokens, w.max_loras, w.num_slices, w.rank)
 
 
-def _run_fused(d, ws, wait_polls=None, stream=None):
+def _run_fused(d, ws, wait_polls=None, stream=None, start_delay_ns="table"):
     srg.lora_fused_step(d.mapping, d.w.num_tokens, d.x, d.lora_a, d.lora_b, float(d.w.scale),
                         d.buf, d.num_splits, d.y, d.meta, ws, wait_polls=wait_polls,
-                        stream=stream)
+                        stream=stream, start_delay_ns=start_delay_ns)
 
 
 def _check_against_two_calls(w, d_step, d_two):
@@ -135,6 +135,31 @@ def test_fused_step_without_waits_same_bits(T, maxT, hidden, slices, rank, L, sp
     _check_against_two_calls(w, d2, d1)
     assert np.array_equal(H.from_dev_bf16(d1.y), H.from_dev_bf16(d2.y))
     H.full_check(w, d2)
+
+
+@pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,splits", [
+    (256, 256, 4096, [4096, 4096, 4096], 8, 4, 16),
+    (77, 96, 640, [40, 264], 16, 4, 3),
+])
+def test_fused_step_start_delay_same_bits(T, maxT, hidden, slices, rank, L, splits):
+    """The expand units' hold-off changes timing only: no hold-off, the
+    library's default and a long one give the same bits, and the workspace
+    ends zero-filled each time."""
+    rng = np.random.default_rng(T * 7 + rank)
+    mapping = rng.integers(-1, L, size=T)
+    w = make_custom_workload(T, T, hidden, slices, rank, L, 0.75, mapping, max_tokens=maxT)
+    ws = _workspace(w)
+    runs = []
+    for delay in (0, None, 4000):
+        d = H.upload(w, num_splits=splits)
+        _run_fused(d, ws, start_delay_ns=delay)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0, delay
+        runs.append(d)
+    for d in runs[1:]:
+        _check_against_two_calls(w, d, runs[0])
+        assert np.array_equal(H.from_dev_bf16(runs[0].y), H.from_dev_bf16(d.y))
+    H.full_check(w, runs[0])
 
 
 def _fused_step_fuzz_cases(n=20, seed=77):
