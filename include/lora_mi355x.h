@@ -319,11 +319,13 @@ lora_status_t lora_expand(const float *buf, int32_t num_splits, const uint16_t *
  * the same batch (same meanings and checks), plus
  *   workspace        device memory of at least
  *                    lora_fused_step_workspace_bytes(...) bytes, 256-byte
- *                    aligned, ZERO-FILLED before its first use; every call
- *                    leaves it zero-filled again once it has completed.  May
- *                    be NULL when that size is 0.  Two calls that overlap in
- *                    time must not share a workspace (one stream, or one
- *                    workspace per stream).
+ *                    aligned, ZERO-FILLED before its first use.  It holds
+ *                    integer counters, which every call leaves zero-filled
+ *                    again once it has completed, and, for the part sums
+ *                    below, a scratch plane that each call overwrites before
+ *                    reading it.  May be NULL when that size is 0.  Two calls
+ *                    that overlap in time must not share a workspace (one
+ *                    stream, or one workspace per stream).
  *   workspace_bytes  its size.
  *   options          host pointer, may be NULL (defaults).
  * Writes what the three calls write: meta in full, buf (num_splits parts) at
@@ -335,7 +337,14 @@ lora_status_t lora_expand(const float *buf, int32_t num_splits, const uint16_t *
  * shrink's workgroups hand each tile's parts to the expand's through the
  * workspace's integer counters (bounded waits, no floating-point atomics; the
  * results are the same bits on every run).  Other sizes: lora_prepare_and_shrink
- * then lora_expand, and the workspace is not touched.
+ * then lora_expand.  On that path, for max_tokens > 512 at rank 32 or 64 with
+ * num_splits >= 2 (the workspace size is then non-zero), options->part_sums
+ * = 1 has the shrink also hand the expand each row's rank vector summed over
+ * the parts: the last shrink workgroup of each 64-token tile and output group
+ * (integer arrival counters in the workspace) adds the parts in the order the
+ * expand would, into the workspace's plane, and the expand reads that one
+ * plane instead of every part (the same bits as without it; buf is written as
+ * always).
  */
 typedef struct lora_step_options {
   /* Upper bound on the polls of each cross-workgroup wait; a workgroup that
@@ -350,6 +359,11 @@ typedef struct lora_step_options {
    * only, never results.  Negative: a default from the shrink's per-workgroup
    * bytes; 0: no hold-off; above 100000: LORA_ERR_INVALID_ARGUMENT. */
   int32_t start_delay_ns;
+  /* Multi-launch path, large batches at rank 32 or 64: 1 = the shrink sums
+   * the parts for the expand (see above); 0 or negative = the expand sums
+   * them (the default: the shrink's arrival round trips and the last
+   * workgroup's read-back cost about what the expand saves). */
+  int32_t part_sums;
 } lora_step_options_t;
 
 int64_t lora_fused_step_workspace_bytes(int32_t max_tokens, int32_t max_loras,

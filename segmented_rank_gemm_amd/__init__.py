@@ -71,7 +71,7 @@ class ExpandConfig(ctypes.Structure):
 
 class _StepOptions(ctypes.Structure):
     _fields_ = [("wait_polls", ctypes.c_int32), ("expand", ExpandConfig),
-                ("start_delay_ns", ctypes.c_int32)]
+                ("start_delay_ns", ctypes.c_int32), ("part_sums", ctypes.c_int32)]
 
 
 def _expand_config(config, lora_b=None, num_splits=None, meta=None) -> Optional[ExpandConfig]:
@@ -101,14 +101,14 @@ def _start_delay(start_delay_ns, lora_b=None, num_splits=None, meta=None) -> Opt
 
 
 def _step_options(wait_polls, expand_config, start_delay_ns=None, lora_b=None, num_splits=None,
-                  meta=None):
+                  meta=None, part_sums=None):
     cfg = _expand_config(expand_config, lora_b, num_splits, meta)
     delay = _start_delay(start_delay_ns, lora_b, num_splits, meta)
-    if wait_polls is None and cfg is None and delay is None:
+    if wait_polls is None and cfg is None and delay is None and not part_sums:
         return None
     cfg = cfg or ExpandConfig()
     return ctypes.byref(_StepOptions(-1 if wait_polls is None else int(wait_polls), cfg,
-                                     -1 if delay is None else delay))
+                                     -1 if delay is None else delay, 1 if part_sums else 0))
 
 
 TILE = 16  # positions per tile of the padded grouped order (LORA_TILE)
@@ -352,11 +352,13 @@ def lora_fused_step(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.
                     buf: torch.Tensor, num_splits: int, y: torch.Tensor, meta: LoraMeta,
                     workspace: Optional[torch.Tensor], wait_polls: Optional[int] = None,
                     stream: Optional[torch.cuda.Stream] = None, expand_config="table",
-                    start_delay_ns="table") -> None:
+                    start_delay_ns="table", part_sums: bool = False) -> None:
     """Metadata, shrink and expand of one batch (one launch where the sizes
     allow); arguments as for lora_prepare_and_shrink and lora_expand, plus the
     zero-filled workspace of fused_step_workspace (reused call after call).
-    start_delay_ns: the one-launch path's expand hold-off (timing only)."""
+    start_delay_ns: the one-launch path's expand hold-off (timing only);
+    part_sums: large rank-32/64 batches, the shrink sums the parts for the
+    expand (same bits)."""
     ptr = _mapping_ptr(token_lora_mapping, num_tokens)
     S, rank, hidden, aptrs = _shrink_args(x, lora_a, buf, num_splits, meta)
     Sb, rank_b, bptrs, nsz = _expand_args(buf, num_splits, lora_b, y, meta)
@@ -365,7 +367,8 @@ def lora_fused_step(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.
     wptr, wbytes = 0, 0
     if workspace is not None:
         wptr, wbytes = _flat_dev_bytes(workspace, "workspace")
-    opts = _step_options(wait_polls, expand_config, start_delay_ns, lora_b, num_splits, meta)
+    opts = _step_options(wait_polls, expand_config, start_delay_ns, lora_b, num_splits, meta,
+                         part_sums)
     _check("lora_fused_step", lib().lora_fused_step(
         ptr, int(num_tokens), _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), hidden, aptrs,
         bptrs, nsz, S, rank, float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits),

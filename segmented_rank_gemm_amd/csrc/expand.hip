@@ -34,6 +34,9 @@ constexpr int kMaxSharedCpr = 16;  // longest column range (chunks) of the share
 struct ExpandParams {
   const float* buf;
   int num_splits;
+  // shared-B kernel: the parts already summed per row (the shrink's part
+  // sums, same bits as summing buf here), or null: sum buf's parts
+  const float* part_sum;
   const uint16_t* b[LORA_MAX_SLICES];
   int n[LORA_MAX_SLICES];
   int off[LORA_MAX_SLICES];
@@ -415,13 +418,13 @@ constexpr int kSharedTile = 64;
 // (The search runs at every workgroup's start, so it avoids integer division:
 // the range counts come from the host, and the rounds, integers below 2^20,
 // are exact enough in fp32 less a margin well above its rounding error.)
-template <int RANK>
+template <int RANK, bool SUMS>
 __device__ int shared_chunks_per_range(const ExpandParams& p, int tiles, int grid) {
   // bytes one chunk moves: its B rows, and its y columns of the tile read and written
   constexpr float kChunkBytes = kExpandCols * RANK * 2 + kSharedTile * kExpandCols * 2 * 2;
   const float startup =
-      0.5f + static_cast<float>(kSharedTile * RANK * 4) * static_cast<float>(p.num_splits) /
-                 kChunkBytes;
+      0.5f + static_cast<float>(kSharedTile * RANK * 4) *
+                 static_cast<float>(SUMS ? 1 : p.num_splits) / kChunkBytes;
   const int slots = (grid < p.num_cus ? grid : p.num_cus) / kXcds;  // CUs per XCD at work
   const float inv_slots = 1.0f / static_cast<float>(slots > 0 ? slots : 1);
   int best = 8;
@@ -440,7 +443,8 @@ __device__ int shared_chunks_per_range(const ExpandParams& p, int tiles, int gri
 
 // Rank 32 fits three waves per SIMD (158 VGPRs), so three workgroups share a CU
 // (70B qkv batch: 39.3 against 40.8 us); rank 64 would spill there.
-template <int RANK>
+// SUMS: the rank vectors come summed (p.part_sum), else from buf's parts.
+template <int RANK, bool SUMS = false>
 __global__ __launch_bounds__(kExpandThreads) __attribute__((amdgpu_waves_per_eu(RANK == 32 ? 3 : 1)))
 void expand_shared_kernel(ExpandParams p) {
   constexpr int kSteps = RANK / 16;
@@ -465,7 +469,7 @@ void expand_shared_kernel(ExpandParams p) {
   // (the table's values are the same in every lane: read them as scalars)
   const int num_tiles = __builtin_amdgcn_readfirstlane(tab.num_tiles);
   const int cpr = p.chunks_per_range > 0 ? p.chunks_per_range
-                                         : shared_chunks_per_range<RANK>(p, num_tiles, gridDim.x);
+                                         : shared_chunks_per_range<RANK, SUMS>(p, num_tiles, gridDim.x);
   int range_end[LORA_MAX_SLICES];  // running count of column ranges through slice s
   {
     int ranges = 0;
@@ -564,7 +568,7 @@ void expand_shared_kernel(ExpandParams p) {
     {
       constexpr int kSpan = RANK / 4;              // ranks summed per lane
       constexpr int kLd = kSpan / 4;               // 16-byte loads per part
-      constexpr int kGroup = RANK == 64 ? 4 : 8;   // parts per batch of loads
+      constexpr int kGroup = part_sum_batch(RANK);  // parts per batch of loads
       const int g4 = lane >> 4;
       const int64_t plane = static_cast<int64_t>(p.num_slices) * p.max_tokens * RANK;
       const float* src0 = p.buf +
@@ -573,7 +577,18 @@ void expand_shared_kernel(ExpandParams p) {
       float v[kSpan];
 #pragma unroll
       for (int e = 0; e < kSpan; ++e) v[e] = 0.f;
-      for (int sp0 = 0; sp0 < p.num_splits; sp0 += kGroup) {
+      if constexpr (SUMS) {  // one plane, already summed in this order
+        const float* sum0 = p.part_sum +
+                            (static_cast<int64_t>(s) * p.max_tokens + (ta >= 0 ? ta : tsafe)) * RANK +
+                            kSpan * g4;
+#pragma unroll
+        for (int l = 0; l < kLd; ++l) {
+          const u32x4 w = load16(sum0 + 4 * l);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * l + e] = __uint_as_float(w[e]);
+        }
+      }
+      for (int sp0 = 0; !SUMS && sp0 < p.num_splits; sp0 += kGroup) {
         uint32_t pm[kGroup];
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) pm[i] = opaque_mask(sp0 + i < p.num_splits);
@@ -687,6 +702,12 @@ void expand_shared_kernel(ExpandParams p) {
 
 template <int RANK>
 hipError_t launch_expand_shared(const ExpandParams& p, int grid, hipStream_t stream) {
+  if (p.part_sum) {
+    grid = resident_grid<expand_shared_kernel<RANK, true>>(kExpandThreads, grid);
+    hipLaunchKernelGGL((expand_shared_kernel<RANK, true>), dim3(grid), dim3(kExpandThreads), 0,
+                       stream, p);
+    return hipGetLastError();
+  }
   grid = resident_grid<expand_shared_kernel<RANK>>(kExpandThreads, grid);
   hipLaunchKernelGGL((expand_shared_kernel<RANK>), dim3(grid), dim3(kExpandThreads), 0, stream, p);
   return hipGetLastError();
@@ -703,10 +724,12 @@ hipError_t launch_expand_rank(const ExpandParams& p, int grid, hipStream_t strea
 hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const* lora_b,
                          const int32_t* slice_sizes, int num_slices, int rank, uint16_t* y,
                          int64_t ldy, const lora_meta_t& meta, int max_tokens, int max_loras,
-                         int num_cus, const lora_expand_config_t* config, hipStream_t stream) {
+                         int num_cus, const lora_expand_config_t* config, hipStream_t stream,
+                         const float* part_sum) {
   ExpandParams p{};
   p.buf = buf;
   p.num_splits = num_splits;
+  p.part_sum = rank >= 32 ? part_sum : nullptr;
   p.num_slices = num_slices;
   int64_t total_chunks = 0;
   int off = 0;

@@ -18,11 +18,16 @@ hipError_t launch_metadata_grouped(const int32_t* mapping, int num_tokens, int m
 hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint16_t* const* lora_a,
                          int num_slices, int rank, float scale, float* buf, int num_splits,
                          const lora_meta_t& meta, int max_tokens, int max_loras, int num_cus,
-                         hipStream_t stream);
+                         hipStream_t stream, int* part_counters = nullptr,
+                         float* part_sum = nullptr);
 hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const* lora_b,
                          const int32_t* slice_sizes, int num_slices, int rank, uint16_t* y,
                          int64_t ldy, const lora_meta_t& meta, int max_tokens, int max_loras,
-                         int num_cus, const lora_expand_config_t* config, hipStream_t stream);
+                         int num_cus, const lora_expand_config_t* config, hipStream_t stream,
+                         const float* part_sum = nullptr);
+int64_t part_sum_workspace_bytes(int max_tokens, int max_loras, int num_slices, int rank);
+void part_sum_layout(void* workspace, int max_tokens, int max_loras, int num_slices, int rank,
+                     int num_splits, int** counters, float** plane);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int num_cus,
                               hipStream_t stream);
 hipError_t launch_stream_update(void* buf, int64_t bytes, int num_cus, hipStream_t stream);
@@ -30,7 +35,8 @@ hipError_t launch_prep_shrink(const int32_t* mapping, int num_tokens, const uint
                               int64_t ldx, int hidden, const uint16_t* const* lora_a,
                               int num_slices, int rank, float scale, float* buf, int num_splits,
                               const lora_meta_t& meta, int max_tokens, int max_loras,
-                              int num_cus, hipStream_t stream);
+                              int num_cus, hipStream_t stream, int* part_counters = nullptr,
+                              float* part_sum = nullptr);
 bool token_step_fits(int max_tokens, int max_loras, int num_slices, int rank);
 int64_t token_step_workspace_bytes(int max_tokens);
 hipError_t launch_token_step(const int32_t* mapping, int num_tokens, const uint16_t* x,
@@ -231,8 +237,9 @@ int64_t lora_fused_step_workspace_bytes(int32_t max_tokens, int32_t max_loras,
                                         int32_t num_slices, int32_t rank) {
   if (!sizes_ok(max_tokens, max_loras) || num_slices < 1 || num_slices > LORA_MAX_SLICES)
     return 0;
-  if (!lora::token_step_fits(max_tokens, max_loras, num_slices, rank)) return 0;
-  return lora::token_step_workspace_bytes(max_tokens);
+  if (lora::token_step_fits(max_tokens, max_loras, num_slices, rank))
+    return lora::token_step_workspace_bytes(max_tokens);
+  return lora::part_sum_workspace_bytes(max_tokens, max_loras, num_slices, rank);
 }
 
 // Checks of lora_expand's arguments other than meta and the sizes.
@@ -285,7 +292,8 @@ static lora_status_t fused_step(const int32_t* token_lora_mapping, int32_t num_t
   if (!expand_config_ok(options_expand(options), rank)) return LORA_ERR_INVALID_ARGUMENT;
   if (options && options->start_delay_ns > kMaxStartDelayNs) return LORA_ERR_INVALID_ARGUMENT;
   const int64_t need = lora_fused_step_workspace_bytes(max_tokens, max_loras, num_slices, rank);
-  if (need > 0) {
+  const bool one_launch = lora::token_step_fits(max_tokens, max_loras, num_slices, rank);
+  if (need > 0 && one_launch) {
     int* counters = nullptr;
     if (static_counters) {
       if (need > lora::token_step_scratch_bytes()) return LORA_ERR_UNSUPPORTED;
@@ -303,11 +311,25 @@ static lora_status_t fused_step(const int32_t* token_lora_mapping, int32_t num_t
         rank, scale, buf, num_splits, y, ldy, *meta, counters, polls, delay, max_tokens,
         max_loras, stream));
   }
-  st = lora_prepare_and_shrink(token_lora_mapping, num_tokens, x, ldx, hidden, lora_a, num_slices,
-                               rank, scale, buf, num_splits, meta, max_tokens, max_loras, stream);
+  // Multi-launch path.  With a workspace (large batches at ranks 32 and 64):
+  // the shrink also hands the expand its parts summed per row.
+  int* part_counters = nullptr;
+  float* part_sum = nullptr;
+  if (need > 0 && !static_counters && options && options->part_sums > 0) {
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+        workspace_bytes < need)
+      return LORA_ERR_INVALID_ARGUMENT;
+    lora::part_sum_layout(workspace, max_tokens, max_loras, num_slices, rank, num_splits,
+                          &part_counters, &part_sum);
+  }
+  st = launch_status(lora::launch_prep_shrink(token_lora_mapping, num_tokens, x, ldx, hidden,
+                                              lora_a, num_slices, rank, scale, buf, num_splits,
+                                              *meta, max_tokens, max_loras, current_cus(), stream,
+                                              part_counters, part_sum));
   if (st != LORA_OK) return st;
-  return lora_expand(buf, num_splits, lora_b, slice_sizes, num_slices, rank, y, ldy, meta,
-                     max_tokens, max_loras, options_expand(options), stream);
+  return launch_status(lora::launch_expand(buf, num_splits, lora_b, slice_sizes, num_slices, rank,
+                                           y, ldy, *meta, max_tokens, max_loras, current_cus(),
+                                           options_expand(options), stream, part_sum));
 }
 
 lora_status_t lora_fused_step(const int32_t* token_lora_mapping, int32_t num_tokens,

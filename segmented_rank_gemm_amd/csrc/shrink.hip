@@ -60,6 +60,12 @@ struct ShrinkParams {
   int num_tokens;
   int shrink_grid;
   MetaOut meta_out;
+  // large batches, ranks 32 and 64, when the caller gives a workspace: each
+  // (64-token tile, output group) counts its parts in at part_counters, and
+  // the last one to arrive sums them into part_sum (null: off)
+  int* part_counters;
+  float* part_sum;
+  uint32_t buf_bytes;  // bytes of buf (under 2^32 whenever part_sum is set)
 };
 
 // NB = number of 16-output blocks covering num_slices * rank outputs;
@@ -381,7 +387,7 @@ constexpr int kLdsTile = 64;  // tokens per tile (4 waves x 16)
 
 // Three workgroups per CU (registers and LDS allow it up to NB = 6), so that a
 // batch's units all run in one round.
-template <int NB>
+template <int NB, bool SUMS = false>
 __global__ __launch_bounds__(kShrinkThreads) __attribute__((amdgpu_waves_per_eu(NB <= 6 ? 3 : 2)))
 void shrink_lds_kernel(ShrinkParams p) {
   constexpr int kRows = kLdsTile + 16 * NB;       // x rows, then A rows
@@ -390,6 +396,7 @@ void shrink_lds_kernel(ShrinkParams p) {
   __shared__ SegmentTable tab;
   __shared__ u32x4 stage[2][kLdsRows * 8];
   __shared__ const uint16_t* slice_a[LORA_MAX_SLICES];
+  __shared__ int last_part;
 
   if (threadIdx.x < LORA_MAX_SLICES) slice_a[threadIdx.x] = p.a[threadIdx.x];
   build_segment_table<kLdsTile>(tab, p.active_ids, p.counts, p.starts, p.num_active, p.max_loras,
@@ -405,6 +412,78 @@ void shrink_lds_kernel(ShrinkParams p) {
   const int nout = p.num_slices * p.rank;
   const int piece = tid & 7;     // this thread's 16-byte piece of every row it loads
   const int row0 = tid >> 3;     // rows row0 + 32 j, j < kJ
+
+  // Part sums (p.part_sum set): parts are written with device-coherent
+  // stores; once all of a unit's have completed, one thread counts the part
+  // in at its (tile, output group) counter, and the workgroup that brings the
+  // count to num_splits reads every part of that tile and group back
+  // (device-coherent loads: other XCDs wrote them), sums them in the expand's
+  // order (part_sum_batch) into part_sum and returns the counter to zero.
+  // Integer counters only: the sum is the same bits whichever unit is last.
+  constexpr bool sums = SUMS;  // p.part_sum and p.part_counters set
+  const __amdgpu_buffer_rsrc_t rbuf = buffer_rsrc(p.buf, sums ? p.buf_bytes : 0u);
+  auto store_part = [&](int64_t e, f32x4 v) {
+    if constexpr (sums)
+      store16_coherent(rbuf, static_cast<uint32_t>(e * 4), __builtin_bit_cast(u32x4, v));
+    else
+      store16(p.buf + e, __builtin_bit_cast(u32x4, v));
+  };
+  auto count_in = [&](int m, int o0, const Tile& tile) {
+    if constexpr (!sums) return;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's part stores have completed
+    __syncthreads();
+    int* const ctr = p.part_counters + (m * p.num_groups + o0 / (16 * NB)) * kPartCounterInts;
+    if (tid == 0)
+      last_part = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  p.num_splits - 1;
+    __syncthreads();
+    if (!last_part) return;  // workgroup-uniform
+    if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // thread: tile row tid / 4, quads (tid % 4) + 4 k (k < NB) of the group's
+    // 4 NB quads of 4 outputs; parts in batches (four, or two above four
+    // blocks, within the registers), every load of a batch in flight before
+    // its adds
+    const int t = tile_token(p.sorted, tile.first, tile.rows, tid >> 2, p.max_tokens);
+    if (t < 0) return;  // a pad row (no barrier follows)
+    const int64_t plane = static_cast<int64_t>(p.num_slices) * p.max_tokens * p.rank;
+    int64_t e0[NB];
+    bool ok[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int o = o0 + 4 * ((tid & 3) + 4 * k);
+      ok[k] = o < nout;
+      const int oc = ok[k] ? o : o0;
+      e0[k] = (static_cast<int64_t>(oc >> p.rank_shift) * p.max_tokens + t) * p.rank +
+              (oc & (p.rank - 1));
+    }
+    f32x4 v[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int kBatch = NB <= 4 ? 4 : 2;
+    for (int sp0 = 0; sp0 < p.num_splits; sp0 += kBatch) {
+      u32x4 w[kBatch][NB];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int sp = sp0 + i < p.num_splits ? sp0 + i : sp0;
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+          w[i][k] = load16_coherent(rbuf, static_cast<uint32_t>((e0[k] + sp * plane) * 4));
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (sp0 + i < p.num_splits)  // uniform
+#pragma unroll
+          for (int k = 0; k < NB; ++k) v[k] += __builtin_bit_cast(f32x4, w[i][k]);
+    }
+    // the expand's batches end with parts past the last that add +0 (which
+    // turns a -0 sum into +0): one such add has the same effect
+    if (p.num_splits % part_sum_batch(p.rank) != 0)
+#pragma unroll
+      for (int k = 0; k < NB; ++k) v[k] += f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+      if (ok[k]) store16(p.part_sum + e0[k], __builtin_bit_cast(u32x4, v[k]));
+  };
 
   for (XcdWalk walk = xcd_walk(units, gridDim.x); walk.next < walk.end; walk.next += walk.step) {
     const int u = walk.next;
@@ -422,11 +501,12 @@ void shrink_lds_kernel(ShrinkParams p) {
       for (int nb = 0; nb < NB; ++nb) {
         const int o = o0 + 16 * nb + 4 * grp;
         if (t >= 0 && o < nout) {
-          float* dst = p.buf + ((static_cast<int64_t>(part) * p.num_slices + (o >> p.rank_shift)) *
-                                p.max_tokens + t) * p.rank + (o & (p.rank - 1));
-          store16(dst, u32x4{0u, 0u, 0u, 0u});
+          const int64_t e = ((static_cast<int64_t>(part) * p.num_slices + (o >> p.rank_shift)) *
+                             p.max_tokens + t) * p.rank + (o & (p.rank - 1));
+          store_part(e, f32x4{0.f, 0.f, 0.f, 0.f});
         }
       }
+      count_in(m, o0, tile);
       continue;
     }
 
@@ -525,17 +605,23 @@ void shrink_lds_kernel(ShrinkParams p) {
     for (int nb = 0; nb < NB; ++nb) {
       const int o = o0 + 16 * nb + 4 * grp;
       if (t >= 0 && o < nout) {
-        f32x4 v = acc[nb] * p.scale;
-        float* dst = p.buf + ((static_cast<int64_t>(part) * p.num_slices + (o >> p.rank_shift)) *
-                              p.max_tokens + t) * p.rank + (o & (p.rank - 1));
-        store16(dst, __builtin_bit_cast(u32x4, v));
+        const int64_t e = ((static_cast<int64_t>(part) * p.num_slices + (o >> p.rank_shift)) *
+                           p.max_tokens + t) * p.rank + (o & (p.rank - 1));
+        store_part(e, acc[nb] * p.scale);
       }
     }
+    count_in(m, o0, tile);
   }
 }
 
 template <int NB>
 hipError_t launch_shrink_lds_nb(const ShrinkParams& p, int grid, hipStream_t stream) {
+  if (p.part_sum) {
+    grid = resident_grid<shrink_lds_kernel<NB, true>>(kShrinkThreads, grid);
+    hipLaunchKernelGGL((shrink_lds_kernel<NB, true>), dim3(grid), dim3(kShrinkThreads), 0, stream,
+                       p);
+    return hipGetLastError();
+  }
   grid = resident_grid<shrink_lds_kernel<NB>>(kShrinkThreads, grid);
   hipLaunchKernelGGL((shrink_lds_kernel<NB>), dim3(grid), dim3(kShrinkThreads), 0, stream, p);
   return hipGetLastError();
@@ -632,14 +718,56 @@ static int shrink_nb(int num_slices, int rank) {
   return shrink_group_blocks((num_slices * rank + 15) / 16);
 }
 
+// Part sums (ShrinkParams.part_sum): large batches (the LDS-staged kernel's
+// 64-token tiles, which are the shared-B expand's) at ranks 32 and 64, with
+// more than one part.  Workspace: the arrival counters, one 64-byte slot per
+// (tile, output group), then the summed plane [S][max_tokens][r] fp32.
+static bool part_sums_apply(int max_tokens, int rank) { return max_tokens > 512 && rank >= 32; }
+
+static int64_t part_counter_bytes(int max_tokens, int max_loras, int num_slices, int rank) {
+  const int64_t tiles = (static_cast<int64_t>(max_tokens) + kLdsTile - 1) / kLdsTile + max_loras;
+  const int nb_total = (num_slices * rank + 15) / 16;
+  const int nb = shrink_group_blocks(nb_total);
+  const int64_t groups = (nb_total + nb - 1) / nb;
+  const int64_t bytes = tiles * groups * kPartCounterInts * static_cast<int64_t>(sizeof(int));
+  return (bytes + 255) / 256 * 256;
+}
+
+int64_t part_sum_workspace_bytes(int max_tokens, int max_loras, int num_slices, int rank) {
+  if (!part_sums_apply(max_tokens, rank)) return 0;
+  return part_counter_bytes(max_tokens, max_loras, num_slices, rank) +
+         static_cast<int64_t>(num_slices) * max_tokens * rank * static_cast<int64_t>(sizeof(float));
+}
+
+// The counters and the plane inside a workspace of part_sum_workspace_bytes;
+// null when the sums do not apply to the call (one part, or buf past 4 GB).
+void part_sum_layout(void* workspace, int max_tokens, int max_loras, int num_slices, int rank,
+                     int num_splits, int** counters, float** plane) {
+  *counters = nullptr;
+  *plane = nullptr;
+  const int64_t buf_bytes = static_cast<int64_t>(num_splits) * num_slices * max_tokens * rank * 4;
+  if (!workspace || !part_sums_apply(max_tokens, rank) || num_splits < 2 ||
+      buf_bytes >= (int64_t{1} << 32))
+    return;
+  *counters = static_cast<int*>(workspace);
+  *plane = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    part_counter_bytes(max_tokens, max_loras, num_slices, rank));
+}
+
 hipError_t launch_shrink(const uint16_t* x, int64_t ldx, int hidden, const uint16_t* const* lora_a,
                          int num_slices, int rank, float scale, float* buf, int num_splits,
                          const lora_meta_t& meta, int max_tokens, int max_loras, int num_cus,
-                         hipStream_t stream) {
-  const ShrinkParams p = shrink_params(x, ldx, hidden, lora_a, num_slices, rank, scale, buf,
-                                       num_splits, meta, max_tokens, max_loras);
+                         hipStream_t stream, int* part_counters, float* part_sum) {
+  ShrinkParams p = shrink_params(x, ldx, hidden, lora_a, num_slices, rank, scale, buf,
+                                 num_splits, meta, max_tokens, max_loras);
   const int nb = shrink_nb(num_slices, rank);
   const int mw = shrink_tile_blocks(max_tokens, nb);
+  if (mw == 4 && part_sum && part_counters) {
+    p.part_counters = part_counters;
+    p.part_sum = part_sum;
+    p.buf_bytes = static_cast<uint32_t>(static_cast<int64_t>(num_splits) * num_slices *
+                                        max_tokens * rank * 4);
+  }
   if (mw == 4) {
     // large batch: LDS-staged kernel, 64-token tiles, at most 3 workgroups per
     // CU, in whole rounds over the XCDs (and no more than are resident)
@@ -681,7 +809,8 @@ hipError_t launch_prep_shrink(const int32_t* mapping, int num_tokens, const uint
                               int64_t ldx, int hidden, const uint16_t* const* lora_a,
                               int num_slices, int rank, float scale, float* buf, int num_splits,
                               const lora_meta_t& meta, int max_tokens, int max_loras,
-                              int num_cus, hipStream_t stream) {
+                              int num_cus, hipStream_t stream, int* part_counters,
+                              float* part_sum) {
   // few adapter outputs: the shrink in batch order (token_step.hip), which
   // needs no grouping before its loads
   if (token_shrink_fits(max_tokens, max_loras, num_slices, rank))
@@ -693,7 +822,7 @@ hipError_t launch_prep_shrink(const int32_t* mapping, int num_tokens, const uint
     const hipError_t e = launch_metadata(mapping, num_tokens, max_tokens, max_loras, meta, stream);
     if (e != hipSuccess) return e;
     return launch_shrink(x, ldx, hidden, lora_a, num_slices, rank, scale, buf, num_splits, meta,
-                         max_tokens, max_loras, num_cus, stream);
+                         max_tokens, max_loras, num_cus, stream, part_counters, part_sum);
   }
   ShrinkParams p = shrink_params(x, ldx, hidden, lora_a, num_slices, rank, scale, buf, num_splits,
                                  meta, max_tokens, max_loras);

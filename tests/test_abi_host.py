@@ -204,6 +204,12 @@ def test_fused_step_workspace_bytes():
     assert srg.lora_fused_step_workspace_bytes(256, 4, 3, 32) == 0     # rank 32
     assert srg.lora_fused_step_workspace_bytes(256, 4, 4, 16) == 16 * 256  # 4*4*16 = 256 outputs
     assert srg.lora_fused_step_workspace_bytes(256, 4, 4, 16) > 0
+    # large batches at rank 32/64: arrival counters (64 bytes per 64-token tile
+    # and output group, rounded to 256) and the summed plane S * max_tokens * r
+    assert srg.lora_fused_step_workspace_bytes(1024, 16, 1, 64) == 32 * 64 + 1024 * 64 * 4
+    assert srg.lora_fused_step_workspace_bytes(4096, 64, 3, 32) == 128 * 64 + 3 * 4096 * 32 * 4
+    assert srg.lora_fused_step_workspace_bytes(600, 2, 3, 64) == 12 * 2 * 64 + 3 * 600 * 64 * 4
+    assert srg.lora_fused_step_workspace_bytes(4096, 4, 2, 16) == 0     # rank 16: no sums
     assert srg.lora_fused_step_workspace_bytes(0, 4, 3, 8) == 0         # invalid sizes
     assert srg.lora_fused_step_workspace_bytes(256, 4, 5, 8) == 0
 
@@ -231,11 +237,12 @@ def test_fused_step_rejects(kw):
 
 def test_fused_step_rejects_long_start_delay():
     # lora_step_options_t: wait_polls, then the three ints of the expand's
-    # config, then start_delay_ns
+    # config, then start_delay_ns and part_sums
     O = srg._StepOptions
-    assert (O.wait_polls.offset, O.expand.offset, O.start_delay_ns.offset) == (0, 4, 16)
-    assert ctypes.sizeof(O) == 20
-    assert _fused(options=ctypes.byref(O(-1, srg.ExpandConfig(), 100001))) == 1
+    assert (O.wait_polls.offset, O.expand.offset, O.start_delay_ns.offset,
+            O.part_sums.offset) == (0, 4, 16, 20)
+    assert ctypes.sizeof(O) == 24
+    assert _fused(options=ctypes.byref(O(-1, srg.ExpandConfig(), 100001, 0))) == 1
 
 
 def test_fused_step_rejects_unsupported_rank():

@@ -33,10 +33,10 @@ def _workspace(w):
     return srg.fused_step_workspace(w.max_tokens, w.max_loras, w.num_slices, w.rank)
 
 
-def _run_fused(d, ws, wait_polls=None, stream=None, start_delay_ns="table"):
+def _run_fused(d, ws, wait_polls=None, stream=None, start_delay_ns="table", part_sums=False):
     srg.lora_fused_step(d.mapping, d.w.num_tokens, d.x, d.lora_a, d.lora_b, float(d.w.scale),
                         d.buf, d.num_splits, d.y, d.meta, ws, wait_polls=wait_polls,
-                        stream=stream, start_delay_ns=start_delay_ns)
+                        stream=stream, start_delay_ns=start_delay_ns, part_sums=part_sums)
 
 
 def _check_against_two_calls(w, d_step, d_two):
@@ -159,6 +159,40 @@ def test_fused_step_start_delay_same_bits(T, maxT, hidden, slices, rank, L, spli
     for d in runs[1:]:
         _check_against_two_calls(w, d, runs[0])
         assert np.array_equal(H.from_dev_bf16(runs[0].y), H.from_dev_bf16(d.y))
+    H.full_check(w, runs[0])
+
+
+@pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,scale,splits", [
+    (900, 1024, 2048, [1024], 64, 16, 0.75, 6),             # down_proj-like: 6 parts, batches of 4
+    (1500, 1536, 1024, [512, 128, 128], 32, 12, 1.0, 7),    # GQA qkv-like: 6 output blocks
+    (700, 768, 1024, [256], 64, 5, -0.5, 4),                 # parts a whole batch; negative scale
+    (640, 640, 768, [384, 64], 32, 8, 0.5, 8),               # rank 32: batches of 8
+    (800, 1024, 1024, [256], 64, 6, 1.0, 1),                 # one part: no sums
+    (1100, 1100, 2056, [136, 264], 32, 64, 1.0, 3),          # 64 adapter slots, odd sizes
+])
+def test_part_sums_same_bits(T, maxT, hidden, slices, rank, L, scale, splits):
+    """Large rank-32/64 batches through lora_fused_step with part_sums: the
+    shrink sums each row's parts for the expand (workspace counters and
+    plane).  Same meta, parts and y, bit for bit, as lora_prepare_and_shrink +
+    lora_expand (which sum the parts in the expand) and as the step without
+    part sums; a second call on the used workspace gives the same bits again;
+    y within the path's tolerance of the oracle."""
+    rng = np.random.default_rng(T + rank)
+    mapping = rng.integers(-1, L, size=T)
+    w = make_custom_workload(T + 5, T, hidden, slices, rank, L, scale, mapping, max_tokens=maxT)
+    ws = _workspace(w)
+    assert ws is not None and ws.numel() > 0
+    d_two = H.upload(w, num_splits=splits)
+    H.run_step_fused(d_two)
+    runs = []
+    for sums in (True, True, False):
+        d = H.upload(w, num_splits=splits)
+        _run_fused(d, ws, part_sums=sums)
+        torch.cuda.synchronize()
+        runs.append(d)
+    for d in runs:
+        _check_against_two_calls(w, d, d_two)
+        assert np.array_equal(H.from_dev_bf16(d_two.y), H.from_dev_bf16(d.y))
     H.full_check(w, runs[0])
 
 
