@@ -369,6 +369,12 @@ typedef struct lora_step_options {
 int64_t lora_fused_step_workspace_bytes(int32_t max_tokens, int32_t max_loras,
                                         int32_t num_slices, int32_t rank);
 
+/* lora_fused_step_launches - host-only query: 1 when lora_fused_step runs
+ * the step in one launch for these sizes, 2 when it runs
+ * lora_prepare_and_shrink then lora_expand, 0 for sizes it rejects. */
+int32_t lora_fused_step_launches(int32_t max_tokens, int32_t max_loras, int32_t num_slices,
+                                 int32_t rank);
+
 lora_status_t lora_fused_step(const int32_t *token_lora_mapping, int32_t num_tokens,
                               const uint16_t *x, int64_t ldx, int32_t hidden,
                               const uint16_t *const *lora_a, const uint16_t *const *lora_b,

@@ -22,6 +22,7 @@ import torch  # noqa: F401  (must precede loading the library, see above)
 __all__ = [
     "LIB_PATH", "LoraError", "LoraMeta", "lib", "lora_prepare_metadata", "lora_shrink",
     "lora_prepare_and_shrink", "lora_fused_step", "lora_fused_step_workspace_bytes",
+    "lora_fused_step_launches",
     "lora_fused_step_static", "lora_prepare_metadata_grouped", "ExpandConfig",
     "fused_step_workspace",
     "lora_shrink_default_splits", "lora_expand", "lora_stream_copy", "lora_stream_update",
@@ -153,6 +154,8 @@ def lib() -> ctypes.CDLL:
         L.lora_expand.restype = ctypes.c_int
         L.lora_fused_step_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32]
         L.lora_fused_step_workspace_bytes.restype = _I64
+        L.lora_fused_step_launches.argtypes = [_I32, _I32, _I32, _I32]
+        L.lora_fused_step_launches.restype = _I32
         L.lora_fused_step.argtypes = [_VP, _I32, _VP, _I64, _I32, ctypes.POINTER(_VP),
                                       ctypes.POINTER(_VP), ctypes.POINTER(_I32), _I32, _I32,
                                       ctypes.c_float, _VP, _I32, _VP, _I64, MP, _VP, _I64,
@@ -334,9 +337,15 @@ def _expand_args(buf: torch.Tensor, num_splits: int, lora_b: Sequence[torch.Tens
 
 def lora_fused_step_workspace_bytes(max_tokens: int, max_loras: int, num_slices: int,
                                     rank: int) -> int:
-    """Bytes of zero-filled workspace lora_fused_step needs (0: none, the sizes
-    take the multi-launch path)."""
+    """Bytes of zero-filled workspace lora_fused_step needs for these sizes
+    (0: none)."""
     return int(lib().lora_fused_step_workspace_bytes(max_tokens, max_loras, num_slices, rank))
+
+
+def lora_fused_step_launches(max_tokens: int, max_loras: int, num_slices: int, rank: int) -> int:
+    """1: lora_fused_step runs these sizes in one launch; 2: as
+    lora_prepare_and_shrink then lora_expand; 0: sizes it rejects."""
+    return int(lib().lora_fused_step_launches(max_tokens, max_loras, num_slices, rank))
 
 
 def fused_step_workspace(max_tokens: int, max_loras: int, num_slices: int, rank: int,
@@ -352,13 +361,14 @@ def lora_fused_step(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.
                     buf: torch.Tensor, num_splits: int, y: torch.Tensor, meta: LoraMeta,
                     workspace: Optional[torch.Tensor], wait_polls: Optional[int] = None,
                     stream: Optional[torch.cuda.Stream] = None, expand_config="table",
-                    start_delay_ns="table", part_sums: bool = False) -> None:
+                    start_delay_ns="table", part_sums="table") -> None:
     """Metadata, shrink and expand of one batch (one launch where the sizes
     allow); arguments as for lora_prepare_and_shrink and lora_expand, plus the
     zero-filled workspace of fused_step_workspace (reused call after call).
     start_delay_ns: the one-launch path's expand hold-off (timing only);
     part_sums: large rank-32/64 batches, the shrink sums the parts for the
-    expand (same bits)."""
+    expand (same bits); "table": the table's choice for the shape (off when
+    the table has none)."""
     ptr = _mapping_ptr(token_lora_mapping, num_tokens)
     S, rank, hidden, aptrs = _shrink_args(x, lora_a, buf, num_splits, meta)
     Sb, rank_b, bptrs, nsz = _expand_args(buf, num_splits, lora_b, y, meta)
@@ -367,6 +377,11 @@ def lora_fused_step(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.
     wptr, wbytes = 0, 0
     if workspace is not None:
         wptr, wbytes = _flat_dev_bytes(workspace, "workspace")
+    if isinstance(part_sums, str):
+        if part_sums != "table":
+            raise ValueError(f"part_sums {part_sums!r}: expected 'table' or a bool")
+        from .tuning import part_sums_for
+        part_sums = part_sums_for(lora_b, num_splits, meta)
     opts = _step_options(wait_polls, expand_config, start_delay_ns, lora_b, num_splits, meta,
                          part_sums)
     _check("lora_fused_step", lib().lora_fused_step(

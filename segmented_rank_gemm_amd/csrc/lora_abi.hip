@@ -242,6 +242,14 @@ int64_t lora_fused_step_workspace_bytes(int32_t max_tokens, int32_t max_loras,
   return lora::part_sum_workspace_bytes(max_tokens, max_loras, num_slices, rank);
 }
 
+int32_t lora_fused_step_launches(int32_t max_tokens, int32_t max_loras, int32_t num_slices,
+                                 int32_t rank) {
+  if (!sizes_ok(max_tokens, max_loras) || num_slices < 1 || num_slices > LORA_MAX_SLICES ||
+      !(rank == 8 || rank == 16 || rank == 32 || rank == 64))
+    return 0;
+  return lora::token_step_fits(max_tokens, max_loras, num_slices, rank) ? 1 : 2;
+}
+
 // Checks of lora_expand's arguments other than meta and the sizes.
 static lora_status_t expand_args(const float* buf, int32_t num_splits,
                                  const uint16_t* const* lora_b, const int32_t* slice_sizes,

@@ -13,7 +13,9 @@ change how the work is cut but never the result are:
   length, the unit order and the workgroups per CU its grid is sized for.
 * on the one-launch path, how long the expand workgroups hold their own loads
   back so that the shrink workgroups' loads are served first
-  (``lora_step_options_t.start_delay_ns``).
+  (``lora_step_options_t.start_delay_ns``); on the multi-launch path for large
+  rank-32/64 batches, whether the shrink sums the parts for the expand
+  (``part_sums``).
 
 Where the optimum lies depends on how the batch's tiles round against the
 compute units, and the tile count is a property of the batch's adapter mix,
@@ -178,15 +180,16 @@ def plan(hidden: int, max_tokens: int, max_loras: int, slices: Sequence[int],
     """Launch choices for a shape: the table's measured ones where the table
     has the shape, else the library's size rules.  Returns
     {"num_splits": n, "expand": ExpandConfig or None, "start_delay_ns": ns or None,
-     "source": "table" | "size rule"}."""
+     "part_sums": bool, "source": "table" | "size rule"}."""
     e = lookup(hidden, max_tokens, max_loras, slices, rank)
     if e is not None:
         delay = e.get("start_delay_ns")
         return {"num_splits": int(e["num_splits"]), "expand": ExpandConfig(**e["expand"]),
-                "start_delay_ns": None if delay is None else int(delay), "source": "table"}
+                "start_delay_ns": None if delay is None else int(delay),
+                "part_sums": bool(e.get("part_sums", False)), "source": "table"}
     return {"num_splits": lora_shrink_default_splits(hidden, max_tokens, max_loras, len(slices),
                                                      rank),
-            "expand": None, "start_delay_ns": None, "source": "size rule"}
+            "expand": None, "start_delay_ns": None, "part_sums": False, "source": "size rule"}
 
 
 def _entry_for(lora_b: Sequence[torch.Tensor], num_splits: int, meta: LoraMeta) -> Optional[dict]:
@@ -210,6 +213,12 @@ def expand_config_for(lora_b: Sequence[torch.Tensor], num_splits: int,
     library's rules)."""
     e = _entry_for(lora_b, num_splits, meta)
     return None if e is None else ExpandConfig(**e["expand"])
+
+
+def part_sums_for(lora_b: Sequence[torch.Tensor], num_splits: int, meta: LoraMeta) -> bool:
+    """Whether the table has the shrink sum the parts for the call at hand."""
+    e = _entry_for(lora_b, num_splits, meta)
+    return bool(e is not None and e.get("part_sums", False))
 
 
 def start_delay_for(lora_b: Sequence[torch.Tensor], num_splits: int,
@@ -248,12 +257,13 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
     stream.  Returns the table entry."""
     from workloads.device import to_dev_bf16
 
-    from . import fused_step_workspace, lora_fused_step
+    from . import fused_step_workspace, lora_fused_step, lora_fused_step_launches
 
     maxT, S, r = w.max_tokens, w.num_slices, w.rank
     rule = lora_shrink_default_splits(w.hidden, maxT, w.max_loras, S, r)
     ws = fused_step_workspace(maxT, w.max_loras, S, r)
-    one_launch = ws is not None
+    one_launch = lora_fused_step_launches(maxT, w.max_loras, S, r) == 1
+    sums_possible = not one_launch and ws is not None  # the part sums' workspace
     base = dict(mapping=torch.from_numpy(w.mapping.astype("int32")).cuda(),
                 x=to_dev_bf16(w.x[:maxT]), y=to_dev_bf16(w.y0[:maxT]),
                 a=[to_dev_bf16(a) for a in w.lora_a], b=[to_dev_bf16(b) for b in w.lora_b])
@@ -264,7 +274,7 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
                 a=[t.clone() for t in base["a"]], b=[t.clone() for t in base["b"]],
                 meta=LoraMeta(maxT, w.max_loras)) for _ in range(copies)]
 
-    def time_step(n, cfg, delay=None):
+    def time_step(n, cfg, delay=None, sums=False):
         bufs = [torch.empty((n, S, maxT, r), dtype=torch.float32, device="cuda")
                 for _ in range(copies)]
 
@@ -273,7 +283,7 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
             lora_fused_step(o["mapping"], w.num_tokens, o["x"], o["a"], o["b"], float(w.scale),
                             bufs[i], n, o["y"], o["meta"], ws, stream=stream,
                             expand_config=cfg if cfg is not None else ExpandConfig(),
-                            start_delay_ns=delay)
+                            start_delay_ns=delay, part_sums=sums)
 
         for i in range(copies):
             step(i, None)
@@ -299,6 +309,24 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
             log(f"[tune] {w.name} splits={best_n} expand={key}: {us_expand[key]:.2f} us")
         best_key = min(us_expand, key=us_expand.get)
         best_cfg = ExpandConfig(**json.loads(best_key))
+    # the same two sweeps with the shrink summing the parts for the expand
+    us_sums = {}
+    best_sums = False
+    if sums_possible:
+        us_sums_splits = {}
+        for n in cands:
+            if n >= 2:
+                us_sums_splits[n] = time_step(n, None, sums=True)
+                log(f"[tune] {w.name} part sums, splits={n}: {us_sums_splits[n]:.2f} us")
+        sn = min(us_sums_splits, key=us_sums_splits.get)
+        for cfg in _expand_candidates(r):
+            key = json.dumps(cfg.as_dict(), sort_keys=True)
+            us_sums[key] = time_step(sn, cfg, sums=True)
+            log(f"[tune] {w.name} part sums, splits={sn} expand={key}: {us_sums[key]:.2f} us")
+        skey = min(us_sums, key=us_sums.get)
+        if us_sums[skey] < min(us_expand.values()):
+            best_sums, best_n, best_cfg = True, sn, ExpandConfig(**json.loads(skey))
+            us_expand = dict(us_expand, **{"part sums " + k: v for k, v in us_sums.items()})
     # the one-launch path's expand hold-off, at the best part count (None:
     # the library's default from the shrink's per-workgroup bytes)
     us_delay = {}
@@ -323,11 +351,13 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
         "num_splits": int(best_n),
         "expand": best_cfg.as_dict(),
         "start_delay_ns": best_delay,
+        "part_sums": best_sums,
         "step_us": round(best_us, 3),
         "rule": {"num_splits": int(rule), "step_us": round(us_splits.get(rule, float("nan")), 3)},
         "step_us_by_splits": {str(k): round(v, 3) for k, v in us_splits.items()},
         "step_us_by_expand": {k: round(v, 3) for k, v in us_expand.items()},
         "step_us_by_start_delay_ns": {k: round(v, 3) for k, v in us_delay.items()},
+        "step_us_with_part_sums": {k: round(v, 3) for k, v in us_sums.items()},
     }
 
 
