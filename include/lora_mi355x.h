@@ -364,6 +364,14 @@ typedef struct lora_step_options {
    * them (the default: the shrink's arrival round trips and the last
    * workgroup's read-back cost about what the expand saves). */
   int32_t part_sums;
+  /* Multi-launch path, max_tokens > 512: 1 = the first launch is the shrink in
+   * batch order (64-token tiles of consecutive tokens, each adapter present in
+   * a tile one pass over its x rows) beside the metadata workgroups, instead
+   * of the metadata kernel then the grouped shrink; the same bits.  Faster on
+   * batches of request runs (a tile holds one or two adapters), slower on maps
+   * drawn per token.  0 or negative: off (the default).  Ignored together
+   * with part_sums = 1. */
+  int32_t batch_order_shrink;
 } lora_step_options_t;
 
 int64_t lora_fused_step_workspace_bytes(int32_t max_tokens, int32_t max_loras,

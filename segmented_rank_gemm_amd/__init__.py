@@ -72,7 +72,8 @@ class ExpandConfig(ctypes.Structure):
 
 class _StepOptions(ctypes.Structure):
     _fields_ = [("wait_polls", ctypes.c_int32), ("expand", ExpandConfig),
-                ("start_delay_ns", ctypes.c_int32), ("part_sums", ctypes.c_int32)]
+                ("start_delay_ns", ctypes.c_int32), ("part_sums", ctypes.c_int32),
+                ("batch_order_shrink", ctypes.c_int32)]
 
 
 def _expand_config(config, lora_b=None, num_splits=None, meta=None) -> Optional[ExpandConfig]:
@@ -101,15 +102,28 @@ def _start_delay(start_delay_ns, lora_b=None, num_splits=None, meta=None) -> Opt
     return None if start_delay_ns is None else int(start_delay_ns)
 
 
+def _table_flag(value, name, lora_b, num_splits, meta) -> bool:
+    """A yes/no launch choice: a bool, or "table" for the table's choice for
+    the call's shape (no when the table has none)."""
+    if isinstance(value, str):
+        if value != "table":
+            raise ValueError(f"{name} {value!r}: expected 'table' or a bool")
+        from .tuning import flag_for
+        return flag_for(name, lora_b, num_splits, meta)
+    return bool(value)
+
+
 def _step_options(wait_polls, expand_config, start_delay_ns=None, lora_b=None, num_splits=None,
-                  meta=None, part_sums=None):
+                  meta=None, part_sums=False, batch_order_shrink=False):
     cfg = _expand_config(expand_config, lora_b, num_splits, meta)
     delay = _start_delay(start_delay_ns, lora_b, num_splits, meta)
-    if wait_polls is None and cfg is None and delay is None and not part_sums:
+    sums = _table_flag(part_sums, "part_sums", lora_b, num_splits, meta)
+    batch = _table_flag(batch_order_shrink, "batch_order_shrink", lora_b, num_splits, meta)
+    if wait_polls is None and cfg is None and delay is None and not sums and not batch:
         return None
     cfg = cfg or ExpandConfig()
     return ctypes.byref(_StepOptions(-1 if wait_polls is None else int(wait_polls), cfg,
-                                     -1 if delay is None else delay, 1 if part_sums else 0))
+                                     -1 if delay is None else delay, int(sums), int(batch)))
 
 
 TILE = 16  # positions per tile of the padded grouped order (LORA_TILE)
@@ -361,14 +375,16 @@ def lora_fused_step(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.
                     buf: torch.Tensor, num_splits: int, y: torch.Tensor, meta: LoraMeta,
                     workspace: Optional[torch.Tensor], wait_polls: Optional[int] = None,
                     stream: Optional[torch.cuda.Stream] = None, expand_config="table",
-                    start_delay_ns="table", part_sums="table") -> None:
+                    start_delay_ns="table", part_sums="table",
+                    batch_order_shrink="table") -> None:
     """Metadata, shrink and expand of one batch (one launch where the sizes
     allow); arguments as for lora_prepare_and_shrink and lora_expand, plus the
     zero-filled workspace of fused_step_workspace (reused call after call).
     start_delay_ns: the one-launch path's expand hold-off (timing only);
     part_sums: large rank-32/64 batches, the shrink sums the parts for the
-    expand (same bits); "table": the table's choice for the shape (off when
-    the table has none)."""
+    expand (same bits); batch_order_shrink: large batches, the shrink in batch
+    order beside the metadata in one launch (same bits).  "table": the
+    table's choice for the shape (off when the table has none)."""
     ptr = _mapping_ptr(token_lora_mapping, num_tokens)
     S, rank, hidden, aptrs = _shrink_args(x, lora_a, buf, num_splits, meta)
     Sb, rank_b, bptrs, nsz = _expand_args(buf, num_splits, lora_b, y, meta)
@@ -377,13 +393,8 @@ def lora_fused_step(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.
     wptr, wbytes = 0, 0
     if workspace is not None:
         wptr, wbytes = _flat_dev_bytes(workspace, "workspace")
-    if isinstance(part_sums, str):
-        if part_sums != "table":
-            raise ValueError(f"part_sums {part_sums!r}: expected 'table' or a bool")
-        from .tuning import part_sums_for
-        part_sums = part_sums_for(lora_b, num_splits, meta)
     opts = _step_options(wait_polls, expand_config, start_delay_ns, lora_b, num_splits, meta,
-                         part_sums)
+                         part_sums, batch_order_shrink)
     _check("lora_fused_step", lib().lora_fused_step(
         ptr, int(num_tokens), _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), hidden, aptrs,
         bptrs, nsz, S, rank, float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits),

@@ -244,8 +244,9 @@ struct XcdWalk {
   int step;
 };
 
-__device__ __forceinline__ XcdWalk xcd_walk(int units, int grid) {
-  const int b = blockIdx.x;
+// b: this workgroup's index among the `grid` workgroups of the walk (its
+// launch index, or that less a multiple of kXcds workgroups placed before it)
+__device__ __forceinline__ XcdWalk xcd_walk(int units, int grid, int b) {
   const int xcd = b % kXcds;
   const int slot = b / kXcds;
   const int per_xcd = (units + kXcds - 1) / kXcds;
@@ -255,6 +256,9 @@ __device__ __forceinline__ XcdWalk xcd_walk(int units, int grid) {
   w.end = min(units, (xcd + 1) * per_xcd);
   w.step = slots;
   return w;
+}
+__device__ __forceinline__ XcdWalk xcd_walk(int units, int grid) {
+  return xcd_walk(units, grid, static_cast<int>(blockIdx.x));
 }
 
 // Loads below are issued unconditionally from addresses that are always valid

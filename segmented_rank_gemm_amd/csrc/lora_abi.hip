@@ -36,7 +36,7 @@ hipError_t launch_prep_shrink(const int32_t* mapping, int num_tokens, const uint
                               int num_slices, int rank, float scale, float* buf, int num_splits,
                               const lora_meta_t& meta, int max_tokens, int max_loras,
                               int num_cus, hipStream_t stream, int* part_counters = nullptr,
-                              float* part_sum = nullptr);
+                              float* part_sum = nullptr, bool batch_order = false);
 bool token_step_fits(int max_tokens, int max_loras, int num_slices, int rank);
 int64_t token_step_workspace_bytes(int max_tokens);
 hipError_t launch_token_step(const int32_t* mapping, int num_tokens, const uint16_t* x,
@@ -333,7 +333,9 @@ static lora_status_t fused_step(const int32_t* token_lora_mapping, int32_t num_t
   st = launch_status(lora::launch_prep_shrink(token_lora_mapping, num_tokens, x, ldx, hidden,
                                               lora_a, num_slices, rank, scale, buf, num_splits,
                                               *meta, max_tokens, max_loras, current_cus(), stream,
-                                              part_counters, part_sum));
+                                              part_counters, part_sum,
+                                              options && options->batch_order_shrink > 0 &&
+                                                  part_sum == nullptr));
   if (st != LORA_OK) return st;
   return launch_status(lora::launch_expand(buf, num_splits, lora_b, slice_sizes, num_slices, rank,
                                            y, ldy, *meta, max_tokens, max_loras, current_cus(),

@@ -614,6 +614,189 @@ void shrink_lds_kernel(ShrinkParams p) {
   }
 }
 
+// Batch-order LDS shrink: the first launch of the step for large batches made
+// of request runs.  Tile m is tokens [64m, 64m + 64) in batch order, so its x
+// rows follow from m and no grouping is needed before the loads; the
+// workgroups past shrink_grid compute the metadata in the same launch (the
+// metadata kernel's per-group code).  Each adapter present in the tile is one
+// pass of the LDS-staged kernel's chunk loop over x and that adapter's A rows,
+// storing the outputs of the tile's tokens that have that adapter; a tile's
+// first adapter and its others are separate units (two per tile and part),
+// so a tile that straddles two requests takes two workgroups, not twice one's
+// time.  A token's outputs are the same bits as the grouped kernel's: the same
+// chunks, the same matrix-core sequence per token (a column of the product
+// depends only on its own x row).  A tile with k adapters streams its x rows k
+// times, so this suits batches whose tiles hold one or two adapters (PR13096's
+// V1 batches of whole requests), not maps drawn per token.
+template <int NB>
+__global__ __launch_bounds__(kShrinkThreads) __attribute__((amdgpu_waves_per_eu(NB <= 6 ? 3 : 2)))
+void shrink_batch_kernel(ShrinkParams p) {
+  // The metadata workgroups come first (dispatched first, so they run beside
+  // the shrink, not after it when the shrink fills the CUs), padded to whole
+  // rounds over the XCDs so that the shrink's workgroups keep their XCDs.
+  const int meta_wgs = (p.max_loras + 1 + kXcds - 1) / kXcds * kXcds;
+  if (static_cast<int>(blockIdx.x) < meta_wgs) {  // workgroup-uniform
+    if (static_cast<int>(blockIdx.x) <= p.max_loras)
+      metadata_group<kShrinkThreads>(p.mapping, p.num_tokens, p.max_loras, p.meta_out,
+                                     static_cast<int>(blockIdx.x));
+    return;
+  }
+  constexpr int kRows = kLdsTile + 16 * NB;       // x rows, then A rows
+  constexpr int kJ = (kRows * 8 + kShrinkThreads - 1) / kShrinkThreads;  // pieces per thread
+  constexpr int kLdsRows = kJ * (kShrinkThreads / 8);
+  __shared__ u32x4 stage[2][kLdsRows * 8];
+  __shared__ const uint16_t* slice_a[LORA_MAX_SLICES];
+  if (threadIdx.x < LORA_MAX_SLICES) slice_a[threadIdx.x] = p.a[threadIdx.x];
+  __syncthreads();
+
+  const int tiles = (p.num_tokens + kLdsTile - 1) / kLdsTile;
+  const int units = 2 * tiles * p.num_splits * p.num_groups;  // (tile, first adapter or the rest)
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = wave_index();
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int nout = p.num_slices * p.rank;
+  const int piece = tid & 7;
+  const int row0 = tid >> 3;
+
+  for (XcdWalk walk = xcd_walk(units, p.shrink_grid, static_cast<int>(blockIdx.x) - meta_wgs);
+       walk.next < walk.end; walk.next += walk.step) {
+    const int u = walk.next >> 1;
+    const bool rest = (walk.next & 1) != 0;  // the tile's adapters after its first
+    const int pg = u / tiles;
+    const int m = u - pg * tiles;
+    const int part = pg / p.num_groups;
+    const int o0 = (pg - part * p.num_groups) * 16 * NB;
+    const int t0 = m * kLdsTile;  // < num_tokens
+    const int kbeg = part * p.split_len;
+    const int kend = min(p.hidden, kbeg + p.split_len);
+    // this lane's token (MFMA N index) and its adapter; lane L of every wave
+    // also holds the adapter of tile row L, so every wave sees the tile's set
+    const int tm = t0 + 16 * wave + col;
+    const int lm = tm < p.num_tokens ? group_of(p.mapping[tm], p.max_loras) - 1 : -1;
+    const int lr = t0 + lane < p.num_tokens ? group_of(p.mapping[t0 + lane], p.max_loras) - 1 : -1;
+    auto store_out = [&](int nb, f32x4 v) {
+      const int o = o0 + 16 * nb + 4 * grp;
+      if (o < nout) {
+        float* dst = p.buf + ((static_cast<int64_t>(part) * p.num_slices + (o >> p.rank_shift)) *
+                              p.max_tokens + tm) * p.rank + (o & (p.rank - 1));
+        store16(dst, __builtin_bit_cast(u32x4, v));
+      }
+    };
+    if (kbeg >= kend) {
+      // an empty part still owes its (zero) contribution
+      if (lm >= 0 && !rest)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) store_out(nb, f32x4{0.f, 0.f, 0.f, 0.f});
+      continue;
+    }
+    const int nchunks = (kend - kbeg + kShrinkChunk - 1) / kShrinkChunk;
+    // x rows: the tile's tokens (a row past the batch reads the tile's first)
+    const uint16_t* src[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int r = row0 + 32 * j;
+      if (r < kLdsTile) src[j] = p.x + static_cast<int64_t>(t0 + r < p.num_tokens ? t0 + r : t0) * p.ldx;
+    }
+    // the tile's adapters, lowest lane first (the same order in every wave):
+    // the first, or all the others
+    uint64_t pending = __ballot(lr >= 0);
+    if (pending != 0) {
+      const int first = __builtin_amdgcn_readlane(lr, static_cast<int>(__builtin_ctzll(pending)));
+      pending = rest ? pending & ~__ballot(lr == first) : __ballot(lr == first);
+    }
+    while (pending != 0) {  // workgroup-uniform
+      const int l = __builtin_amdgcn_readlane(lr, static_cast<int>(__builtin_ctzll(pending)));
+      pending &= ~__ballot(lr == l);
+      // A rows of adapter l for the group's outputs (past the last: the last)
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const int r = row0 + 32 * j;
+        if (r >= kLdsTile) {
+          int o = o0 + (r - kLdsTile);
+          o = o < nout ? o : nout - 1;
+          src[j] = slice_a[o >> p.rank_shift] +
+                   (static_cast<int64_t>(l) * p.rank + (o & (p.rank - 1))) * p.hidden;
+        }
+      }
+      // the chunk loop of shrink_lds_kernel, unchanged
+      struct Staged {
+        u32x4 v[kJ];
+      };
+      auto gload = [&](int c, Staged& st) {
+        const int k = kbeg + (c < nchunks ? c : nchunks - 1) * kShrinkChunk + 8 * piece;
+        const int kk = k < kend ? k : kbeg;
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) st.v[j] = load16(src[j] + kk);
+      };
+      auto sstore = [&](int b, const Staged& st) {
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+          const int r = row0 + 32 * j;
+          stage[b][r * 8 + (piece ^ (r & 7))] = st.v[j];
+        }
+      };
+      f32x4 acc[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      auto compute = [&](int b, int c) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int pc = 4 * i + grp;
+          const int xr = 16 * wave + col;
+          const uint32_t in = kbeg + c * kShrinkChunk + 8 * pc < kend ? 0xFFFFFFFFu : 0u;
+          const u32x4 xv = stage[b][xr * 8 + (pc ^ (xr & 7))] & in;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const int ar = kLdsTile + 16 * nb + col;
+            const u32x4 av = stage[b][ar * 8 + (pc ^ (ar & 7))];
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, xv), acc[nb], 0, 0, 0);
+          }
+        }
+      };
+      Staged ra, rb;
+      gload(0, ra);
+      gload(1, rb);
+      sstore(0, ra);
+      gload(2, ra);
+      __syncthreads();
+      int c = 0;
+      for (; c + 2 <= nchunks; c += 2) {
+        compute(0, c);
+        sstore(1, rb);
+        gload(c + 3, rb);
+        __syncthreads();
+        compute(1, c + 1);
+        sstore(0, ra);
+        gload(c + 4, ra);
+        __syncthreads();
+      }
+      if (c < nchunks) {
+        compute(0, c);
+        __syncthreads();
+      }
+      if (lm == l)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) store_out(nb, acc[nb] * p.scale);
+    }
+  }
+}
+
+template <int NB>
+hipError_t launch_shrink_batch_nb(ShrinkParams p, int grid, hipStream_t stream) {
+  const int meta_wgs = (p.max_loras + 1 + kXcds - 1) / kXcds * kXcds;
+  // what stays resident beside the metadata workgroups
+  const int resident = resident_grid<shrink_batch_kernel<NB>>(kShrinkThreads, 1 << 30);
+  const int room = (resident - meta_wgs) / kXcds * kXcds;
+  grid = grid < room ? grid : (room >= kXcds ? room : kXcds);
+  p.shrink_grid = grid;
+  const int total = meta_wgs + grid;
+  hipLaunchKernelGGL((shrink_batch_kernel<NB>), dim3(total), dim3(kShrinkThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int NB>
 hipError_t launch_shrink_lds_nb(const ShrinkParams& p, int grid, hipStream_t stream) {
   if (p.part_sum) {
@@ -810,13 +993,38 @@ hipError_t launch_prep_shrink(const int32_t* mapping, int num_tokens, const uint
                               int num_slices, int rank, float scale, float* buf, int num_splits,
                               const lora_meta_t& meta, int max_tokens, int max_loras,
                               int num_cus, hipStream_t stream, int* part_counters,
-                              float* part_sum) {
+                              float* part_sum, bool batch_order) {
   // few adapter outputs: the shrink in batch order (token_step.hip), which
   // needs no grouping before its loads
   if (token_shrink_fits(max_tokens, max_loras, num_slices, rank))
     return launch_token_prep_shrink(mapping, num_tokens, x, ldx, hidden, lora_a, num_slices, rank,
                                     scale, buf, num_splits, meta, max_tokens, max_loras, stream);
   const int nb = shrink_nb(num_slices, rank);
+  if (batch_order && shrink_tile_blocks(max_tokens, nb) == 4) {
+    // large batch of request runs: the batch-order LDS shrink beside the
+    // metadata workgroups, one launch
+    ShrinkParams p = shrink_params(x, ldx, hidden, lora_a, num_slices, rank, scale, buf,
+                                   num_splits, meta, max_tokens, max_loras);
+    p.mapping = mapping;
+    p.num_tokens = num_tokens;
+    p.meta_out = MetaOut{meta.sorted_token_ids, meta.active_lora_ids, meta.num_tokens_per_lora,
+                         meta.lora_token_start, meta.num_active, meta.tile_token_ids,
+                         meta.tile_lora, meta.num_tiles, meta.num_runs};
+    const int64_t tiles = (static_cast<int64_t>(max_tokens) + kLdsTile - 1) / kLdsTile;
+    int64_t g = tiles * num_splits * p.num_groups;
+    const int64_t cap = static_cast<int64_t>(num_cus) * 3;
+    g = g < cap ? g : cap;
+    const int grid = static_cast<int>((g + kXcds - 1) / kXcds * kXcds);
+    switch (nb) {
+      case 1: return launch_shrink_batch_nb<1>(p, grid, stream);
+      case 2: return launch_shrink_batch_nb<2>(p, grid, stream);
+      case 3: return launch_shrink_batch_nb<3>(p, grid, stream);
+      case 4: return launch_shrink_batch_nb<4>(p, grid, stream);
+      case 5:
+      case 6: return launch_shrink_batch_nb<6>(p, grid, stream);
+      default: return launch_shrink_batch_nb<8>(p, grid, stream);
+    }
+  }
   if (shrink_tile_blocks(max_tokens, nb) != 1 || max_tokens > kWave * kPerThread ||
       max_loras > kMaxFusedLoras) {
     const hipError_t e = launch_metadata(mapping, num_tokens, max_tokens, max_loras, meta, stream);

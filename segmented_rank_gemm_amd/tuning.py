@@ -15,7 +15,9 @@ change how the work is cut but never the result are:
   back so that the shrink workgroups' loads are served first
   (``lora_step_options_t.start_delay_ns``); on the multi-launch path for large
   rank-32/64 batches, whether the shrink sums the parts for the expand
-  (``part_sums``).
+  (``part_sums``); for large batches, whether the shrink runs in batch order
+  beside the metadata (``batch_order_shrink``: faster on batches of request
+  runs, so it is measured on the workload's own batch).
 
 Where the optimum lies depends on how the batch's tiles round against the
 compute units, and the tile count is a property of the batch's adapter mix,
@@ -180,16 +182,18 @@ def plan(hidden: int, max_tokens: int, max_loras: int, slices: Sequence[int],
     """Launch choices for a shape: the table's measured ones where the table
     has the shape, else the library's size rules.  Returns
     {"num_splits": n, "expand": ExpandConfig or None, "start_delay_ns": ns or None,
-     "part_sums": bool, "source": "table" | "size rule"}."""
+     "part_sums": bool, "batch_order_shrink": bool, "source": "table" | "size rule"}."""
     e = lookup(hidden, max_tokens, max_loras, slices, rank)
     if e is not None:
         delay = e.get("start_delay_ns")
         return {"num_splits": int(e["num_splits"]), "expand": ExpandConfig(**e["expand"]),
                 "start_delay_ns": None if delay is None else int(delay),
-                "part_sums": bool(e.get("part_sums", False)), "source": "table"}
+                "part_sums": bool(e.get("part_sums", False)),
+                "batch_order_shrink": bool(e.get("batch_order_shrink", False)), "source": "table"}
     return {"num_splits": lora_shrink_default_splits(hidden, max_tokens, max_loras, len(slices),
                                                      rank),
-            "expand": None, "start_delay_ns": None, "part_sums": False, "source": "size rule"}
+            "expand": None, "start_delay_ns": None, "part_sums": False,
+            "batch_order_shrink": False, "source": "size rule"}
 
 
 def _entry_for(lora_b: Sequence[torch.Tensor], num_splits: int, meta: LoraMeta) -> Optional[dict]:
@@ -215,10 +219,11 @@ def expand_config_for(lora_b: Sequence[torch.Tensor], num_splits: int,
     return None if e is None else ExpandConfig(**e["expand"])
 
 
-def part_sums_for(lora_b: Sequence[torch.Tensor], num_splits: int, meta: LoraMeta) -> bool:
-    """Whether the table has the shrink sum the parts for the call at hand."""
+def flag_for(name: str, lora_b: Sequence[torch.Tensor], num_splits: int, meta: LoraMeta) -> bool:
+    """The table's yes/no choice `name` ("part_sums", "batch_order_shrink") for
+    the call at hand (no when the table has none)."""
     e = _entry_for(lora_b, num_splits, meta)
-    return bool(e is not None and e.get("part_sums", False))
+    return bool(e is not None and e.get(name, False))
 
 
 def start_delay_for(lora_b: Sequence[torch.Tensor], num_splits: int,
@@ -274,7 +279,7 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
                 a=[t.clone() for t in base["a"]], b=[t.clone() for t in base["b"]],
                 meta=LoraMeta(maxT, w.max_loras)) for _ in range(copies)]
 
-    def time_step(n, cfg, delay=None, sums=False):
+    def time_step(n, cfg, delay=None, sums=False, batch=False):
         bufs = [torch.empty((n, S, maxT, r), dtype=torch.float32, device="cuda")
                 for _ in range(copies)]
 
@@ -283,7 +288,7 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
             lora_fused_step(o["mapping"], w.num_tokens, o["x"], o["a"], o["b"], float(w.scale),
                             bufs[i], n, o["y"], o["meta"], ws, stream=stream,
                             expand_config=cfg if cfg is not None else ExpandConfig(),
-                            start_delay_ns=delay, part_sums=sums)
+                            start_delay_ns=delay, part_sums=sums, batch_order_shrink=batch)
 
         for i in range(copies):
             step(i, None)
@@ -295,17 +300,28 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
     cands = candidate_splits(w.hidden, maxT, w.max_loras, S, r)
     if one_launch:
         cands = sorted({c for c in cands if c >= 4} | ({rule, 20, 24, 32} & set(range(1, 65))))
+    # large batches: the grouped shrink after the metadata kernel, or the
+    # batch-order shrink beside it (decided on this batch, then kept)
+    batch_possible = not one_launch and maxT > 512
+    batch = False
     us_splits = {}
     for n in cands:
         us_splits[n] = time_step(n, None)
         log(f"[tune] {w.name} splits={n}: {us_splits[n]:.2f} us")
-    best_n = min(us_splits, key=us_splits.get)
+    us_batch = {}
+    if batch_possible:
+        for n in cands:
+            us_batch[n] = time_step(n, None, batch=True)
+            log(f"[tune] {w.name} batch-order shrink, splits={n}: {us_batch[n]:.2f} us")
+        if min(us_batch.values()) < min(us_splits.values()):
+            batch = True
+    best_n = min(us_batch, key=us_batch.get) if batch else min(us_splits, key=us_splits.get)
     us_expand = {}
     best_cfg = ExpandConfig()
     if not one_launch:
         for cfg in _expand_candidates(r):
             key = json.dumps(cfg.as_dict(), sort_keys=True)
-            us_expand[key] = time_step(best_n, cfg)
+            us_expand[key] = time_step(best_n, cfg, batch=batch)
             log(f"[tune] {w.name} splits={best_n} expand={key}: {us_expand[key]:.2f} us")
         best_key = min(us_expand, key=us_expand.get)
         best_cfg = ExpandConfig(**json.loads(best_key))
@@ -352,9 +368,11 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
         "expand": best_cfg.as_dict(),
         "start_delay_ns": best_delay,
         "part_sums": best_sums,
+        "batch_order_shrink": batch and not best_sums,
         "step_us": round(best_us, 3),
         "rule": {"num_splits": int(rule), "step_us": round(us_splits.get(rule, float("nan")), 3)},
         "step_us_by_splits": {str(k): round(v, 3) for k, v in us_splits.items()},
+        "step_us_by_splits_batch_order": {str(k): round(v, 3) for k, v in us_batch.items()},
         "step_us_by_expand": {k: round(v, 3) for k, v in us_expand.items()},
         "step_us_by_start_delay_ns": {k: round(v, 3) for k, v in us_delay.items()},
         "step_us_with_part_sums": {k: round(v, 3) for k, v in us_sums.items()},

@@ -237,12 +237,12 @@ def test_fused_step_rejects(kw):
 
 def test_fused_step_rejects_long_start_delay():
     # lora_step_options_t: wait_polls, then the three ints of the expand's
-    # config, then start_delay_ns and part_sums
+    # config, then start_delay_ns, part_sums and batch_order_shrink
     O = srg._StepOptions
     assert (O.wait_polls.offset, O.expand.offset, O.start_delay_ns.offset,
-            O.part_sums.offset) == (0, 4, 16, 20)
-    assert ctypes.sizeof(O) == 24
-    assert _fused(options=ctypes.byref(O(-1, srg.ExpandConfig(), 100001, 0))) == 1
+            O.part_sums.offset, O.batch_order_shrink.offset) == (0, 4, 16, 20, 24)
+    assert ctypes.sizeof(O) == 28
+    assert _fused(options=ctypes.byref(O(-1, srg.ExpandConfig(), 100001, 0, 0))) == 1
 
 
 def test_fused_step_rejects_unsupported_rank():

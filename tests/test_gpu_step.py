@@ -33,10 +33,12 @@ def _workspace(w):
     return srg.fused_step_workspace(w.max_tokens, w.max_loras, w.num_slices, w.rank)
 
 
-def _run_fused(d, ws, wait_polls=None, stream=None, start_delay_ns="table", part_sums=False):
+def _run_fused(d, ws, wait_polls=None, stream=None, start_delay_ns="table", part_sums=False,
+               batch_order_shrink=False):
     srg.lora_fused_step(d.mapping, d.w.num_tokens, d.x, d.lora_a, d.lora_b, float(d.w.scale),
                         d.buf, d.num_splits, d.y, d.meta, ws, wait_polls=wait_polls,
-                        stream=stream, start_delay_ns=start_delay_ns, part_sums=part_sums)
+                        stream=stream, start_delay_ns=start_delay_ns, part_sums=part_sums,
+                        batch_order_shrink=batch_order_shrink)
 
 
 def _check_against_two_calls(w, d_step, d_two):
@@ -194,6 +196,49 @@ def test_part_sums_same_bits(T, maxT, hidden, slices, rank, L, scale, splits):
         _check_against_two_calls(w, d, d_two)
         assert np.array_equal(H.from_dev_bf16(d_two.y), H.from_dev_bf16(d.y))
     H.full_check(w, runs[0])
+
+
+def _runs_mapping(rng, T, L, median=64):
+    """Request runs: consecutive tokens of one adapter (some of none)."""
+    out, t = [], 0
+    while t < T:
+        n = int(min(T - t, max(1, rng.lognormal(np.log(median), 1.0))))
+        out += [int(rng.integers(-1, L))] * n
+        t += n
+    return np.array(out, dtype=np.int64)
+
+
+@pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,kind,splits,scale", [
+    (8192, 8192, 4096, [11008, 11008], 16, 4, "runs", 2, 1.0),    # the gate_up prefill shape
+    (4096, 4096, 8192, [8192, 1024, 1024], 32, 64, "runs", 7, 1.0),  # the 70B qkv shape
+    (1000, 1536, 1032, [136, 264], 8, 6, "runs", 3, -0.5),        # ragged tail, unused slots
+    (700, 700, 640, [256], 64, 16, "iid", 5, 1.0),                # a map drawn per token
+    (777, 1024, 520, [96, 32], 16, 3, "runs", 12, 1.0),           # empty parts (12 x 64 > 520)
+    (600, 600, 512, [128], 16, 4, "none", 2, 1.0),                # no token has an adapter
+])
+def test_batch_order_shrink_same_bits(T, maxT, hidden, slices, rank, L, kind, splits, scale):
+    """Large batches through lora_fused_step with batch_order_shrink: the
+    shrink in batch order beside the metadata workgroups, one launch.  Same
+    meta, parts and y, bit for bit, as the metadata kernel then the grouped
+    shrink (lora_prepare_and_shrink + lora_expand); y within the path's
+    tolerance of the oracle."""
+    rng = np.random.default_rng(T * 3 + L)
+    if kind == "runs":
+        mapping = _runs_mapping(rng, T, L)
+    elif kind == "iid":
+        mapping = rng.integers(-1, L, size=T)
+    else:
+        mapping = np.full(T, -1, dtype=np.int64)
+    w = make_custom_workload(T + 11, T, hidden, slices, rank, L, scale, mapping, max_tokens=maxT)
+    ws = _workspace(w)
+    d_two = H.upload(w, num_splits=splits)
+    H.run_step_fused(d_two)
+    d = H.upload(w, num_splits=splits)
+    _run_fused(d, ws, batch_order_shrink=True)
+    torch.cuda.synchronize()
+    _check_against_two_calls(w, d, d_two)
+    assert np.array_equal(H.from_dev_bf16(d_two.y), H.from_dev_bf16(d.y))
+    _check_y(w, d)
 
 
 def _fused_step_fuzz_cases(n=20, seed=77):
