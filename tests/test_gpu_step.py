@@ -241,6 +241,52 @@ def test_batch_order_shrink_same_bits(T, maxT, hidden, slices, rank, L, kind, sp
     _check_y(w, d)
 
 
+def _large_option_cases(n=14, seed=91):
+    """Random large shapes for the batch-order shrink and the part sums."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        rank = int(rng.choice([8, 16, 32, 64]))
+        maxT = int(rng.integers(513, 2049))
+        T = int(rng.integers(1, maxT + 1))
+        S = int(rng.integers(1, 4))
+        slices = [8 * int(rng.integers(1, 129)) for _ in range(S)]
+        hidden = 8 * int(rng.integers(1, 1025))
+        L = int(rng.integers(1, 33))
+        splits = int(rng.integers(1, 13))
+        kind = ["runs", "iid", "mixed"][i % 3]
+        out.append((T, maxT, hidden, slices, rank, L, kind, splits, i))
+    return out
+
+
+@pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,kind,splits,seed", _large_option_cases())
+def test_large_batch_options_fuzz(T, maxT, hidden, slices, rank, L, kind, splits, seed):
+    """lora_fused_step on random large shapes with each of its large-batch
+    options (batch-order shrink; part sums where they apply): the same meta,
+    parts and y, bit for bit, as lora_prepare_and_shrink + lora_expand, twice
+    on the same workspace."""
+    rng = np.random.default_rng(1000 + seed)
+    if kind == "runs":
+        mapping = _runs_mapping(rng, T, L, median=48)
+    elif kind == "iid":
+        mapping = rng.integers(-1, L, size=T)
+    else:
+        mapping = _runs_mapping(rng, T, L, median=8)
+    w = make_custom_workload(2000 + seed, T, hidden, slices, rank, L, 0.5, mapping, max_tokens=maxT)
+    ws = _workspace(w)
+    d_two = H.upload(w, num_splits=splits)
+    H.run_step_fused(d_two)
+    y_ref = H.from_dev_bf16(d_two.y)
+    for opts in (dict(batch_order_shrink=True), dict(part_sums=True),
+                 dict(batch_order_shrink=True)):
+        d = H.upload(w, num_splits=splits)
+        _run_fused(d, ws, **opts)
+        torch.cuda.synchronize()
+        _check_against_two_calls(w, d, d_two)
+        assert np.array_equal(y_ref, H.from_dev_bf16(d.y)), opts
+    H.full_check(w, d_two)
+
+
 def _fused_step_fuzz_cases(n=20, seed=77):
     rng = np.random.default_rng(seed)
     kinds = ["wild", "all_none", "single", "runs", "extreme"]
