@@ -321,6 +321,7 @@ def run_config(idx, args):
     import torch
 
     import segmented_rank_gemm_amd as srg
+    from segmented_rank_gemm_amd import measure
     from workloads import CONFIGS, make_workload, workload_stats
 
     log(f"[bench] workload {idx} ({CONFIGS[idx]['name']}): generating inputs")
@@ -473,9 +474,9 @@ def run_config(idx, args):
     Rc = rot["expand"]
     srcs = [torch.empty(cb, dtype=torch.uint8, device="cuda") for _ in range(Rc)]
     dsts = [torch.empty(cb, dtype=torch.uint8, device="cuda") for _ in range(Rc)]
-    g_copy = capture([lambda s, r=r: srg.lora_stream_copy(srcs[r], dsts[r], s) for r in range(Rc)])
+    g_copy = capture([lambda s, r=r: measure.lora_stream_copy(srcs[r], dsts[r], s) for r in range(Rc)])
     copy_s = time_graph(g_copy, reps) / Rc
-    g_upd = capture([lambda s, r=r: srg.lora_stream_update(srcs[r], s) for r in range(Rc)])
+    g_upd = capture([lambda s, r=r: measure.lora_stream_update(srcs[r], s) for r in range(Rc)])
     upd_s = time_graph(g_upd, reps) / Rc
     del g_copy, g_upd, srcs, dsts
 

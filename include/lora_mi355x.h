@@ -423,21 +423,8 @@ lora_status_t lora_fused_step_static(const int32_t *token_lora_mapping, int32_t 
 /* lora_status_string - static, human-readable name of a status code. */
 const char *lora_status_string(lora_status_t status);
 
-/*
- * lora_stream_copy - measurement aid: copy `bytes` bytes from src to dst with
- * the same 16-byte vector loads and stores the kernels above use, giving the
- * practical HBM read+write ceiling next to the nominal 8 TB/s.  bytes must be a
- * multiple of 16, both pointers 16-byte aligned, buffers not overlapping.
- */
-lora_status_t lora_stream_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
-
-/*
- * lora_stream_update - measurement aid: read every 16-byte piece of `buf`,
- * change it and write it back in place (the output access pattern of
- * lora_expand), giving the practical in-place update ceiling.  bytes must be a
- * multiple of 16, buf 16-byte aligned.  The buffer's contents are scrambled.
- */
-lora_status_t lora_stream_update(void *buf, int64_t bytes, hipStream_t stream);
+/* The measurement aids lora_stream_copy and lora_stream_update live in a
+ * library of their own: lora_measure.h, liblora_measure.so. */
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ __all__ = [
     "lora_fused_step_launches",
     "lora_fused_step_static", "lora_prepare_metadata_grouped", "ExpandConfig",
     "fused_step_workspace",
-    "lora_shrink_default_splits", "lora_expand", "lora_stream_copy", "lora_stream_update",
+    "lora_shrink_default_splits", "lora_expand",
     "lora_status_string",
     "LORA_MAX_LORAS", "LORA_MAX_SLICES", "LORA_MAX_SPLITS", "SUPPORTED_RANKS",
 ]
@@ -180,10 +180,6 @@ def lib() -> ctypes.CDLL:
                                              ctypes.c_float, _VP, _I32, _VP, _I64, MP,
                                              ctypes.POINTER(_StepOptions), _I32, _I32, _VP]
         L.lora_fused_step_static.restype = ctypes.c_int
-        L.lora_stream_copy.argtypes = [_VP, _VP, _I64, _VP]
-        L.lora_stream_copy.restype = ctypes.c_int
-        L.lora_stream_update.argtypes = [_VP, _I64, _VP]
-        L.lora_stream_update.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -448,18 +444,3 @@ def _flat_dev_bytes(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
     return int(t.data_ptr()), t.numel() * t.element_size()
 
-
-def lora_stream_copy(src: torch.Tensor, dst: torch.Tensor,
-                     stream: Optional[torch.cuda.Stream] = None) -> None:
-    """Copy all of src into the first bytes of dst (both contiguous device tensors)."""
-    sp, nbytes = _flat_dev_bytes(src, "src")
-    dp, dbytes = _flat_dev_bytes(dst, "dst")
-    if dbytes < nbytes:
-        raise ValueError("dst smaller than src")
-    _check("lora_stream_copy", lib().lora_stream_copy(sp, dp, int(nbytes), _stream_handle(stream)))
-
-
-def lora_stream_update(buf: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
-    """Read, change and write back every byte of buf (a contiguous device tensor)."""
-    bp, nbytes = _flat_dev_bytes(buf, "buf")
-    _check("lora_stream_update", lib().lora_stream_update(bp, int(nbytes), _stream_handle(stream)))

@@ -1,7 +1,8 @@
-"""Compile the HIP sources of the library into ``liblora_mi355x.so`` (gfx950).
+"""Compile the HIP sources into ``liblora_mi355x.so`` (the multi-LoRA path)
+and ``liblora_measure.so`` (the measurement aids of lora_measure.h), gfx950.
 
 Each ``csrc/*.hip`` file is compiled to an object in parallel, then linked
-into one shared library next to this file.  Packed-FP32 instructions are
+into its shared library next to this file.  Packed-FP32 instructions are
 switched off for all device code.
 """
 
@@ -16,10 +17,12 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblora_mi355x.so")
+MEASURE_LIB = os.path.join(HERE, "liblora_measure.so")
 ARCH = "gfx950"
 
 SOURCES = ["lora_abi.hip", "metadata.hip", "metadata_grouped.hip", "shrink.hip", "expand.hip",
-           "token_step.hip", "stream_copy.hip"]
+           "token_step.hip"]
+MEASURE_SOURCES = ["stream_copy.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
@@ -42,15 +45,21 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
+def _link(objs, lib: str, verbose: bool) -> None:
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", lib + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(lib + ".tmp", lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + MEASURE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in MEASURE_SOURCES], MEASURE_LIB, verbose)
     return LIB
 
 

@@ -28,9 +28,6 @@ hipError_t launch_expand(const float* buf, int num_splits, const uint16_t* const
 int64_t part_sum_workspace_bytes(int max_tokens, int max_loras, int num_slices, int rank);
 void part_sum_layout(void* workspace, int max_tokens, int max_loras, int num_slices, int rank,
                      int num_splits, int** counters, float** plane);
-hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int num_cus,
-                              hipStream_t stream);
-hipError_t launch_stream_update(void* buf, int64_t bytes, int num_cus, hipStream_t stream);
 hipError_t launch_prep_shrink(const int32_t* mapping, int num_tokens, const uint16_t* x,
                               int64_t ldx, int hidden, const uint16_t* const* lora_a,
                               int num_slices, int rank, float scale, float* buf, int num_splits,
@@ -366,20 +363,6 @@ lora_status_t lora_fused_step_static(const int32_t* token_lora_mapping, int32_t 
   return fused_step(token_lora_mapping, num_tokens, x, ldx, hidden, lora_a, lora_b, slice_sizes,
                     num_slices, rank, scale, buf, num_splits, y, ldy, meta, nullptr, 0, true,
                     options, max_tokens, max_loras, stream);
-}
-
-lora_status_t lora_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
-  if (!src || !dst || bytes <= 0 || bytes % 16 != 0 || !aligned16(src) || !aligned16(dst))
-    return LORA_ERR_INVALID_ARGUMENT;
-  const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
-  if (s < d + static_cast<uintptr_t>(bytes) && d < s + static_cast<uintptr_t>(bytes))
-    return LORA_ERR_INVALID_ARGUMENT;
-  return launch_status(lora::launch_stream_copy(src, dst, bytes, current_cus(), stream));
-}
-
-lora_status_t lora_stream_update(void* buf, int64_t bytes, hipStream_t stream) {
-  if (!buf || bytes <= 0 || bytes % 16 != 0 || !aligned16(buf)) return LORA_ERR_INVALID_ARGUMENT;
-  return launch_status(lora::launch_stream_update(buf, bytes, current_cus(), stream));
 }
 
 }  // extern "C"

@@ -5,6 +5,7 @@
 // against; the update is the access pattern of the expand's output.
 
 #include "device_common.hpp"
+#include "lora_measure.h"
 
 namespace lora {
 
@@ -76,3 +77,26 @@ hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, int num
 }
 
 }  // namespace lora
+
+namespace {
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+lora_status_t launch_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_LAUNCH; }
+}  // namespace
+
+extern "C" {
+
+lora_status_t lora_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  if (!src || !dst || bytes <= 0 || bytes % 16 != 0 || !aligned16(src) || !aligned16(dst))
+    return LORA_ERR_INVALID_ARGUMENT;
+  const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+  if (s < d + static_cast<uintptr_t>(bytes) && d < s + static_cast<uintptr_t>(bytes))
+    return LORA_ERR_INVALID_ARGUMENT;
+  return launch_status(lora::launch_stream_copy(src, dst, bytes, lora::kCus, stream));
+}
+
+lora_status_t lora_stream_update(void* buf, int64_t bytes, hipStream_t stream) {
+  if (!buf || bytes <= 0 || bytes % 16 != 0 || !aligned16(buf)) return LORA_ERR_INVALID_ARGUMENT;
+  return launch_status(lora::launch_stream_update(buf, bytes, lora::kCus, stream));
+}
+
+}  // extern "C"

@@ -9,15 +9,15 @@ import re
 import pytest
 
 import segmented_rank_gemm_amd as srg
+from segmented_rank_gemm_amd import measure
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
-                      "lora_mi355x.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 
 FAKE = 0x10000  # a 16-byte aligned non-null address that is never dereferenced
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(header="lora_mi355x.h"):
+    text = open(os.path.join(INCLUDE, header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", text)))
 
@@ -25,15 +25,23 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["lora_prepare_metadata", "lora_shrink", "lora_expand", "lora_status_string",
-              "lora_prepare_and_shrink",
-              "lora_shrink_default_splits", "lora_stream_copy", "lora_stream_update"]:
+              "lora_prepare_and_shrink", "lora_fused_step", "lora_fused_step_static",
+              "lora_fused_step_workspace_bytes", "lora_fused_step_launches",
+              "lora_prepare_metadata_grouped", "lora_shrink_default_splits"]:
         assert n in names
+    # the measurement aids are not part of the path's interface
+    assert "lora_stream_copy" not in names and "lora_stream_update" not in names
+    assert set(_declared("lora_measure.h")) == {"lora_stream_copy", "lora_stream_update"}
 
 
 def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(srg.LIB_PATH)
     for n in _declared():
         assert hasattr(L, n), n
+    M = ctypes.CDLL(measure.MEASURE_LIB_PATH)
+    for n in _declared("lora_measure.h"):
+        assert hasattr(M, n), n
+    assert not hasattr(L, "lora_stream_copy")
 
 
 def test_status_strings():
@@ -149,7 +157,7 @@ def test_expand_rejects(kw, status):
 
 
 def test_stream_copy_rejects():
-    L = srg.lib()
+    L = measure.measure_lib()
     assert L.lora_stream_copy(None, FAKE, 64, None) == 1
     assert L.lora_stream_copy(FAKE, FAKE + 4096, 20, None) == 1
     assert L.lora_stream_copy(FAKE, FAKE + 32, 64, None) == 1  # overlap
