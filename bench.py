@@ -417,6 +417,26 @@ def run_config(idx, args):
     step3_s = per.pop("step3")
     step2_s = per.pop("step2")
 
+    # large batches: the same step with the large-batch options the table did
+    # not choose, where they apply (measured beside the chosen one; same bits)
+    options = {}
+    if not sets.one_launch and w.max_tokens > 512:
+        variants = [("batch_order_shrink", dict(batch_order_shrink=not sets.batch_order_shrink,
+                                                part_sums=False))]
+        if w.rank >= 32 and splits >= 2:
+            variants.append(("part_sums", dict(batch_order_shrink=False,
+                                               part_sums=not sets.part_sums)))
+        chosen = (sets.batch_order_shrink, sets.part_sums)
+        n = rot["fused_step"]
+        m = n * max(1, math.ceil(MIN_GRAPH_LAUNCHES / n))
+        for name, flags in variants:
+            sets.batch_order_shrink, sets.part_sums = flags["batch_order_shrink"], flags["part_sums"]
+            g = capture([lambda s, r=r: sets.fused(r % n, s) for r in range(m)])
+            options[f"{name}={'on' if flags[name] else 'off'}"] = time_graph(g, reps) / m * 1e6
+            del g
+        sets.batch_order_shrink, sets.part_sums = chosen
+        options["as_chosen"] = per["fused_step"] * 1e6
+
     # V0-style input: the same batch regrouped by adapter (each group one
     # contiguous run), through the general metadata kernel and the one-pass
     # grouped one (same outputs)
@@ -551,6 +571,7 @@ def run_config(idx, args):
             "frac_of_peak": (st["shrink_bytes"] + st["expand_bytes"]) / pair_s / 1e9 / HBM_PEAK_GBS,
         },
         "layer_stack": stack,
+        "step_us_by_large_batch_option": options or None,
         "grouped_input": dict(grouped, batch="the same batch regrouped by adapter (V0-style)"),
         "copy_ceiling": {"bytes_read_plus_written": 2 * cb, "us": copy_s * 1e6,
                          "GBs": 2 * cb / copy_s / 1e9},
