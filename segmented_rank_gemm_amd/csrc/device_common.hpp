@@ -285,12 +285,6 @@ __device__ __forceinline__ uint32_t opaque_mask(bool keep) {
 __device__ __forceinline__ u32x4 masked(u32x4 v, bool keep) { return v & opaque_mask(keep); }
 __device__ __forceinline__ u32x2 masked(u32x2 v, bool keep) { return v & opaque_mask(keep); }
 
-// Summing a row's rank vector over the shrink's parts (the shared-B expand,
-// or the shrink's last workgroup of a tile when it hands the expand one summed
-// plane): start at +0, add parts in part order, loaded in batches of this many
-// with a part past the last adding +0.  Both places follow this one order, so
-// either source gives the expand the same bits.
-__host__ __device__ constexpr int part_sum_batch(int rank) { return rank == 64 ? 4 : 8; }
 // ints per (tile, output group) arrival counter of the part sums: 64 bytes
 constexpr int kPartCounterInts = 16;
 

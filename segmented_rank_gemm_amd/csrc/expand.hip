@@ -443,8 +443,11 @@ __device__ int shared_chunks_per_range(const ExpandParams& p, int tiles, int gri
 
 // Rank 32 fits three waves per SIMD (158 VGPRs), so three workgroups share a CU
 // (70B qkv batch: 39.3 against 40.8 us); rank 64 would spill there.
-// SUMS: the rank vectors come summed (p.part_sum), else from buf's parts.
-template <int RANK, bool SUMS = false>
+// SUMS: the rank vectors come summed (p.part_sum), else from buf's parts,
+// whose loads go out GROUP parts at a time (the sum is the same bits for any
+// GROUP: it starts at +0 and adds the parts in order, and the masked parts
+// past the last add +0 to a sum that is never -0).
+template <int RANK, bool SUMS = false, int GROUP = (RANK == 64 ? 4 : 8)>
 __global__ __launch_bounds__(kExpandThreads) __attribute__((amdgpu_waves_per_eu(RANK == 32 ? 3 : 1)))
 void expand_shared_kernel(ExpandParams p) {
   constexpr int kSteps = RANK / 16;
@@ -568,7 +571,7 @@ void expand_shared_kernel(ExpandParams p) {
     {
       constexpr int kSpan = RANK / 4;              // ranks summed per lane
       constexpr int kLd = kSpan / 4;               // 16-byte loads per part
-      constexpr int kGroup = part_sum_batch(RANK);  // parts per batch of loads
+      constexpr int kGroup = GROUP;                 // parts per batch of loads
       const int g4 = lane >> 4;
       const int64_t plane = static_cast<int64_t>(p.num_slices) * p.max_tokens * RANK;
       const float* src0 = p.buf +
@@ -707,6 +710,19 @@ hipError_t launch_expand_shared(const ExpandParams& p, int grid, hipStream_t str
     hipLaunchKernelGGL((expand_shared_kernel<RANK, true>), dim3(grid), dim3(kExpandThreads), 0,
                        stream, p);
     return hipGetLastError();
+  }
+  // Rank 64 with 5 or 6 parts: all parts in one batch of loads, one round
+  // trip instead of two, at one workgroup per CU (226 VGPRs); it pays while
+  // the batch is small (down_proj shape, 16 adapters, 6 parts: 18.5 against
+  // 19.3 us at 2048 tokens, 26.5 against 27.7 at 4096) and loses once the
+  // tiles take several rounds (49.4 against 42.8 at 8192).
+  if constexpr (RANK == 64) {
+    if (p.num_splits > 4 && p.num_splits <= 6 && p.max_tokens <= 4096) {
+      grid = resident_grid<expand_shared_kernel<RANK, false, 6>>(kExpandThreads, grid);
+      hipLaunchKernelGGL((expand_shared_kernel<RANK, false, 6>), dim3(grid),
+                         dim3(kExpandThreads), 0, stream, p);
+      return hipGetLastError();
+    }
   }
   grid = resident_grid<expand_shared_kernel<RANK>>(kExpandThreads, grid);
   hipLaunchKernelGGL((expand_shared_kernel<RANK>), dim3(grid), dim3(kExpandThreads), 0, stream, p);

@@ -417,9 +417,11 @@ void shrink_lds_kernel(ShrinkParams p) {
   // stores; once all of a unit's have completed, one thread counts the part
   // in at its (tile, output group) counter, and the workgroup that brings the
   // count to num_splits reads every part of that tile and group back
-  // (device-coherent loads: other XCDs wrote them), sums them in the expand's
-  // order (part_sum_batch) into part_sum and returns the counter to zero.
-  // Integer counters only: the sum is the same bits whichever unit is last.
+  // (device-coherent loads: other XCDs wrote them), sums them in part order
+  // from +0, as the expand does, into part_sum and returns the counter to
+  // zero.  Integer counters only: the sum is the same bits whichever unit is
+  // last.  (A sum that starts at +0 is never -0, so the +0 the expand adds for
+  // the parts past the last of its batch changes no bit.)
   constexpr bool sums = SUMS;  // p.part_sum and p.part_counters set
   const __amdgpu_buffer_rsrc_t rbuf = buffer_rsrc(p.buf, sums ? p.buf_bytes : 0u);
   auto store_part = [&](int64_t e, f32x4 v) {
@@ -475,11 +477,6 @@ void shrink_lds_kernel(ShrinkParams p) {
 #pragma unroll
           for (int k = 0; k < NB; ++k) v[k] += __builtin_bit_cast(f32x4, w[i][k]);
     }
-    // the expand's batches end with parts past the last that add +0 (which
-    // turns a -0 sum into +0): one such add has the same effect
-    if (p.num_splits % part_sum_batch(p.rank) != 0)
-#pragma unroll
-      for (int k = 0; k < NB; ++k) v[k] += f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < NB; ++k)
       if (ok[k]) store16(p.part_sum + e0[k], __builtin_bit_cast(u32x4, v[k]));
