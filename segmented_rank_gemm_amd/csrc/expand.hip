@@ -442,13 +442,16 @@ __device__ int shared_chunks_per_range(const ExpandParams& p, int tiles, int gri
 }
 
 // Rank 32 fits three waves per SIMD (158 VGPRs), so three workgroups share a CU
-// (70B qkv batch: 39.3 against 40.8 us); rank 64 would spill there.
+// (70B qkv batch: 39.3 against 40.8 us); rank 64 would spill there and runs
+// two: the six-part batch is built for two waves per SIMD (left to itself the
+// compiler took 32 accumulator registers more than that allows), the other
+// rank-64 builds fit two as they are.
 // SUMS: the rank vectors come summed (p.part_sum), else from buf's parts,
 // whose loads go out GROUP parts at a time (the sum is the same bits for any
 // GROUP: it starts at +0 and adds the parts in order, and the masked parts
 // past the last add +0 to a sum that is never -0).
 template <int RANK, bool SUMS = false, int GROUP = (RANK == 64 ? 4 : 8)>
-__global__ __launch_bounds__(kExpandThreads) __attribute__((amdgpu_waves_per_eu(RANK == 32 ? 3 : 1)))
+__global__ __launch_bounds__(kExpandThreads) __attribute__((amdgpu_waves_per_eu(RANK == 32 ? 3 : GROUP > 4 ? 2 : 1)))
 void expand_shared_kernel(ExpandParams p) {
   constexpr int kSteps = RANK / 16;
   constexpr int kRowPieces = RANK / 8;           // 16-byte pieces per B row
@@ -712,12 +715,10 @@ hipError_t launch_expand_shared(const ExpandParams& p, int grid, hipStream_t str
     return hipGetLastError();
   }
   // Rank 64 with 5 or 6 parts: all parts in one batch of loads, one round
-  // trip instead of two, at one workgroup per CU (226 VGPRs); it pays while
-  // the batch is small (down_proj shape, 16 adapters, 6 parts: 18.5 against
-  // 19.3 us at 2048 tokens, 26.5 against 27.7 at 4096) and loses once the
-  // tiles take several rounds (49.4 against 42.8 at 8192).
+  // trip instead of two (226 VGPRs, two waves per SIMD).  down_proj shape, 16 adapters, 6 parts:
+  // 18.5 against 19.3 us at 2048 tokens, 76.4 against 80.5 at 16384.
   if constexpr (RANK == 64) {
-    if (p.num_splits > 4 && p.num_splits <= 6 && p.max_tokens <= 4096) {
+    if (p.num_splits > 4 && p.num_splits <= 6) {
       grid = resident_grid<expand_shared_kernel<RANK, false, 6>>(kExpandThreads, grid);
       hipLaunchKernelGGL((expand_shared_kernel<RANK, false, 6>), dim3(grid),
                          dim3(kExpandThreads), 0, stream, p);
