@@ -150,6 +150,8 @@ LARGE_BATCH_PARTS = [
     # two parts to the most parts the hidden dimension has 64-element chunks for
     (520, 11008, [4096], 64, 16, 2),
     (520, 11008, [4096], 64, 16, 64),
+    (777, 1032, [256, 136], 64, 5, 5),    # rank 64 with 5 or 6 parts: the expand loads
+    (5000, 2048, [1024], 64, 16, 6),      # every part in one batch; units over several rounds
     (1500, 4096, [2048, 2048], 16, 4, 8),
     (3000, 8192, [8192, 1024, 1024], 32, 64, 6),
     (2048, 1024, [512], 8, 1, 3),

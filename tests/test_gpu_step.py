@@ -165,7 +165,8 @@ def test_fused_step_start_delay_same_bits(T, maxT, hidden, slices, rank, L, spli
 
 
 @pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,scale,splits", [
-    (900, 1024, 2048, [1024], 64, 16, 0.75, 6),             # down_proj-like: 6 parts, batches of 4
+    (900, 1024, 2048, [1024], 64, 16, 0.75, 6),             # down_proj-like: 6 parts in one batch
+    (1000, 1000, 1536, [384, 128], 64, 9, 1.25, 5),         # rank 64, 5 parts in one batch
     (1500, 1536, 1024, [512, 128, 128], 32, 12, 1.0, 7),    # GQA qkv-like: 6 output blocks
     (700, 768, 1024, [256], 64, 5, -0.5, 4),                 # parts a whole batch; negative scale
     (640, 640, 768, [384, 64], 32, 8, 0.5, 8),               # rank 32: batches of 8
