@@ -451,7 +451,8 @@ __device__ int shared_chunks_per_range(const ExpandParams& p, int tiles, int gri
 // GROUP: it starts at +0 and adds the parts in order, and the masked parts
 // past the last add +0 to a sum that is never -0).
 template <int RANK, bool SUMS = false, int GROUP = (RANK == 64 ? 4 : 8)>
-__global__ __launch_bounds__(kExpandThreads) __attribute__((amdgpu_waves_per_eu(RANK == 32 ? 3 : GROUP > 4 ? 2 : 1)))
+__global__ __launch_bounds__(kExpandThreads)
+__attribute__((amdgpu_waves_per_eu(RANK == 32 ? 3 : GROUP > 4 ? 2 : 1)))
 void expand_shared_kernel(ExpandParams p) {
   constexpr int kSteps = RANK / 16;
   constexpr int kRowPieces = RANK / 8;           // 16-byte pieces per B row
@@ -715,8 +716,9 @@ hipError_t launch_expand_shared(const ExpandParams& p, int grid, hipStream_t str
     return hipGetLastError();
   }
   // Rank 64 with 5 or 6 parts: all parts in one batch of loads, one round
-  // trip instead of two (226 VGPRs, two waves per SIMD).  down_proj shape, 16 adapters, 6 parts:
-  // 18.5 against 19.3 us at 2048 tokens, 76.4 against 80.5 at 16384.
+  // trip instead of two (226 VGPRs, two waves per SIMD).  down_proj shape,
+  // 16 adapters, 6 parts: 18.5 against 19.3 us at 2048 tokens, 76.4 against
+  // 80.5 at 16384.
   if constexpr (RANK == 64) {
     if (p.num_splits > 4 && p.num_splits <= 6) {
       grid = resident_grid<expand_shared_kernel<RANK, false, 6>>(kExpandThreads, grid);
