@@ -288,6 +288,50 @@ def test_large_batch_options_fuzz(T, maxT, hidden, slices, rank, L, kind, splits
     H.full_check(w, d_two)
 
 
+@pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,splits,opts", [
+    (700, 768, 1024, [512], 64, 6, 6, dict(part_sums=True)),                 # counters + plane
+    (900, 1024, 520, [256, 128], 16, 4, 3, dict(batch_order_shrink=True)),   # metadata beside the shrink
+])
+def test_large_batch_options_graph_replays(T, maxT, hidden, slices, rank, L, splits, opts):
+    """One capture of lora_fused_step with a large-batch option, replayed on
+    new batches copied into the captured buffers, with eager work and
+    synchronisations between the replays.  Every replay gives the meta, parts
+    and y of lora_prepare_and_shrink + lora_expand on its own batch, bit for
+    bit, and y within the path's tolerance of the oracle."""
+    rng = np.random.default_rng(T + rank)
+    kinds = [_runs_mapping(rng, T, L, median=48), rng.integers(-1, L, size=T),
+             np.full(T, -1), rng.integers(-3, L + 3, size=T), np.full(T, L - 1),
+             _runs_mapping(rng, T, L, median=8)]
+    batches = [make_custom_workload(3000 + i, T, hidden, slices, rank, L, 0.75, m, max_tokens=maxT)
+               for i, m in enumerate(kinds)]
+    d = H.upload(batches[0], num_splits=splits)
+    ws = _workspace(batches[0])
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        _run_fused(d, ws, stream=torch.cuda.current_stream(), **opts)
+    for w in batches:
+        fresh = H.upload(w, num_splits=splits)
+        d.w = w
+        d.mapping.copy_(fresh.mapping)
+        d.x.copy_(fresh.x)
+        d.y.copy_(fresh.y)
+        for dst, src in zip(d.lora_a + d.lora_b, fresh.lora_a + fresh.lora_b):
+            dst.copy_(src)
+        d.buf.fill_(float("nan"))
+        d.meta.sorted_token_ids.fill_(-7)
+        d_two = H.upload(w, num_splits=splits)
+        H.run_step_fused(d_two)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _check_against_two_calls(w, d, d_two)
+        assert np.array_equal(H.from_dev_bf16(d_two.y), H.from_dev_bf16(d.y))
+        if int((np.asarray(w.mapping) >= 0).sum()) > 0:
+            H.full_check(w, d)
+
+
 def _fused_step_fuzz_cases(n=20, seed=77):
     rng = np.random.default_rng(seed)
     kinds = ["wild", "all_none", "single", "runs", "extreme"]
