@@ -407,7 +407,8 @@ lora_status_t lora_fused_step(const int32_t *token_lora_mapping, int32_t num_tok
  * device address is looked up on the first call on each device.
  *
  * Arguments, outputs, sizes and the multi-launch path for other sizes: as
- * lora_fused_step.  A size whose counters would not fit the array returns
+ * lora_fused_step, except that options->part_sums is ignored (the part sums
+ * need a workspace; the expand then sums the parts, the same bits).  A size whose counters would not fit the array returns
  * LORA_ERR_UNSUPPORTED with nothing enqueued (no size the one-launch path
  * accepts does); a failed lookup of the array returns LORA_ERR_LAUNCH.
  */

@@ -403,15 +403,18 @@ def lora_fused_step_static(token_lora_mapping: torch.Tensor, num_tokens: int, x:
                            scale: float, buf: torch.Tensor, num_splits: int, y: torch.Tensor,
                            meta: LoraMeta, wait_polls: Optional[int] = None,
                            stream: Optional[torch.cuda.Stream] = None, expand_config="table",
-                           start_delay_ns="table") -> None:
+                           start_delay_ns="table", batch_order_shrink="table") -> None:
     """lora_fused_step with the library's own counter array instead of a
-    workspace (nothing is allocated; calls that overlap on one GPU race)."""
+    workspace (nothing is allocated; calls that overlap on one GPU race).
+    No part sums (they need a workspace); the other launch choices as for
+    lora_fused_step."""
     ptr = _mapping_ptr(token_lora_mapping, num_tokens)
     S, rank, hidden, aptrs = _shrink_args(x, lora_a, buf, num_splits, meta)
     Sb, rank_b, bptrs, nsz = _expand_args(buf, num_splits, lora_b, y, meta)
     if Sb != S or rank_b != rank:
         raise ValueError("lora_a and lora_b disagree on slices or rank")
-    opts = _step_options(wait_polls, expand_config, start_delay_ns, lora_b, num_splits, meta)
+    opts = _step_options(wait_polls, expand_config, start_delay_ns, lora_b, num_splits, meta,
+                         False, batch_order_shrink)
     _check("lora_fused_step_static", lib().lora_fused_step_static(
         ptr, int(num_tokens), _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), hidden, aptrs,
         bptrs, nsz, S, rank, float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits),

@@ -63,3 +63,11 @@ def test_static_counters_largest_batch_and_refusal():
                                d.buf, d.num_splits, d.y, d.meta)
     torch.cuda.synchronize()
     H.full_check(w, d)
+    # and with the batch-order shrink beside the metadata (no array either):
+    # the same bits as the default multi-launch call
+    d2 = H.upload(w)
+    srg.lora_fused_step_static(d2.mapping, w.num_tokens, d2.x, d2.lora_a, d2.lora_b,
+                               float(w.scale), d2.buf, d2.num_splits, d2.y, d2.meta,
+                               batch_order_shrink=True)
+    torch.cuda.synchronize()
+    _same_bits(d2, d)
