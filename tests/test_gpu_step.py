@@ -119,6 +119,34 @@ def test_fused_step_full_size(cfg):
 @pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,splits", [
     (256, 256, 4096, [4096, 4096, 4096], 8, 4, 16),
     (333, 400, 1032, [136, 8, 24, 200], 8, 6, 7),
+])
+def test_fused_step_short_waits_same_bits(T, maxT, hidden, slices, rank, L, splits):
+    """wait_polls of 1, 4 and 16: some expand units run out of polls and
+    compute their tile's parts while the shrink units still write and count
+    theirs.  Same metadata, parts and y, bit for bit, as the step that waits;
+    the workspace is zero-filled after every call, and a call that waits on
+    the same workspace afterwards gives the same bits again."""
+    rng = np.random.default_rng(T + 7)
+    mapping = rng.integers(-1, L, size=T)
+    w = make_custom_workload(T + 11, T, hidden, slices, rank, L, 1.25, mapping, max_tokens=maxT)
+    ws = _workspace(w)
+    d_ref = H.upload(w, num_splits=splits)
+    _run_fused(d_ref, ws)
+    torch.cuda.synchronize()
+    y_ref = H.from_dev_bf16(d_ref.y)
+    for polls in (1, 4, 16, None):
+        d = H.upload(w, num_splits=splits)
+        _run_fused(d, ws, wait_polls=polls)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0, polls
+        _check_against_two_calls(w, d, d_ref)
+        assert np.array_equal(y_ref, H.from_dev_bf16(d.y)), polls
+    H.full_check(w, d_ref)
+
+
+@pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,splits", [
+    (256, 256, 4096, [4096, 4096, 4096], 8, 4, 16),
+    (333, 400, 1032, [136, 8, 24, 200], 8, 6, 7),
     (200, 256, 8192, [1024], 8, 3, 2),
     (100, 128, 512, [96, 32], 16, 4, 3),
 ])
