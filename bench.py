@@ -322,9 +322,9 @@ def run_config(idx, args):
 
     import segmented_rank_gemm_amd as srg
     from segmented_rank_gemm_amd import measure
-    from workloads import CONFIGS, make_workload, workload_stats
+    from workloads import WORKLOADS, make_workload, workload_stats
 
-    log(f"[bench] workload {idx} ({CONFIGS[idx]['name']}): generating inputs")
+    log(f"[bench] workload {idx} ({WORKLOADS[idx]['name']}): generating inputs")
     w = make_workload(idx)
     st = workload_stats(w)
     from segmented_rank_gemm_amd.tuning import plan
@@ -528,7 +528,7 @@ def run_config(idx, args):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": CONFIGS[idx]["name"], "num_tokens": w.num_tokens,
+            "workload": WORKLOADS[idx]["name"], "num_tokens": w.num_tokens,
             "active_tokens": st["active_tokens"], "hidden": w.hidden, "slices": w.slices,
             "rank": w.rank, "max_loras": w.max_loras, "active_adapters": st["active_adapters"],
             "scale": w.scale, "accumulate": "fp32", "shrink_parts": splits,
@@ -541,7 +541,7 @@ def run_config(idx, args):
         "roofline": {
             "bound": "hbm", "kernel": dom, "achieved": achieved,
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(dom, CONFIGS[idx]["name"]),
+            "traffic": measured_traffic(dom, WORKLOADS[idx]["name"]),
             "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_us": dom_s * 1e6,
             "step_kernels_us": {k: v[0] * 1e6 for k, v in step_kernels.items()},

@@ -10,7 +10,7 @@ import torch
 import oracle
 import segmented_rank_gemm_amd as srg
 from tests import gpu_harness as H
-from workloads import CONFIGS, make_fuzz_mapping, make_mapping
+from workloads import WORKLOADS, make_fuzz_mapping, make_mapping
 
 pytestmark = pytest.mark.gpu
 
@@ -51,11 +51,11 @@ def _grouped(ids, rng, order="ascending"):
     return np.concatenate([ids[ids == k] for k in keys]) if ids.size else ids
 
 
-@pytest.mark.parametrize("cfg", range(len(CONFIGS)))
+@pytest.mark.parametrize("cfg", range(len(WORKLOADS)))
 @pytest.mark.parametrize("order", ["ascending", "shuffled"])
 def test_grouped_batches_of_the_workloads(cfg, order):
     # each workload's adapter map, regrouped the way a V0 scheduler would
-    L = CONFIGS[cfg]["max_loras"]
+    L = WORKLOADS[cfg]["max_loras"]
     rng = np.random.default_rng(cfg)
     m = make_mapping(cfg)
     ids = np.where((m >= -1) & (m < L), m, -1)
@@ -82,11 +82,11 @@ def test_grouped_edge_cases(T, maxT, L, kind):
     _check(np.asarray(m, dtype=np.int64), maxT, L)
 
 
-@pytest.mark.parametrize("cfg", range(len(CONFIGS)))
+@pytest.mark.parametrize("cfg", range(len(WORKLOADS)))
 def test_ungrouped_batches_fall_back(cfg):
     # the workloads' own maps are not grouped: same outputs through the fallback
     m = make_mapping(cfg)
-    _check(m, len(m) + 3, CONFIGS[cfg]["max_loras"])
+    _check(m, len(m) + 3, WORKLOADS[cfg]["max_loras"])
 
 
 @pytest.mark.parametrize("T,L,kind", [(300, 4, "wild"), (4096, 64, "runs"), (9000, 7, "wild"),

@@ -13,7 +13,7 @@ import torch
 import oracle
 import segmented_rank_gemm_amd as srg
 from tests import gpu_harness as H
-from workloads import (CONFIGS, make_custom_workload, make_fuzz_mapping,
+from workloads import (WORKLOADS, make_custom_workload, make_fuzz_mapping,
                        make_integer_exact_workload, make_mapping, make_workload)
 
 pytestmark = pytest.mark.gpu
@@ -46,11 +46,11 @@ def _run_metadata(mapping, T, max_tokens, L):
 
 # ------------------------------------------------------------------ metadata
 
-@pytest.mark.parametrize("cfg", range(len(CONFIGS)))
+@pytest.mark.parametrize("cfg", range(len(WORKLOADS)))
 def test_metadata_bit_exact_full_size(cfg):
     mapping = make_mapping(cfg)
     T = mapping.shape[0]
-    L = CONFIGS[cfg]["max_loras"]
+    L = WORKLOADS[cfg]["max_loras"]
     got = _run_metadata(mapping, T, T + 37, L)
     _check_meta(got, oracle.prepare_metadata(mapping, L), T, T + 37, mapping=mapping, L=L)
 
@@ -77,7 +77,7 @@ def test_metadata_bit_exact_fuzz(T, maxT, L, kind):
 REDUCED_T = [16, 200, 1000, 700, 900]
 
 
-@pytest.mark.parametrize("cfg", range(len(CONFIGS)))
+@pytest.mark.parametrize("cfg", range(len(WORKLOADS)))
 @pytest.mark.parametrize("splits", ["default", 1, 3])
 def test_step_parity_reduced(cfg, splits):
     w = make_workload(cfg, num_tokens=REDUCED_T[cfg], max_tokens=REDUCED_T[cfg] + 19)
@@ -87,7 +87,7 @@ def test_step_parity_reduced(cfg, splits):
     _full_check(w, d)
 
 
-@pytest.mark.parametrize("cfg", range(len(CONFIGS)))
+@pytest.mark.parametrize("cfg", range(len(WORKLOADS)))
 def test_step_parity_full_size(cfg):
     # full sizes, default number of parts: the launch configuration the benchmark times
     w = make_workload(cfg)

@@ -4,13 +4,13 @@ the range the C ABI accepts, and plan() hands it out."""
 
 import segmented_rank_gemm_amd as srg
 from segmented_rank_gemm_amd.tuning import load_table, plan, shape_key
-from workloads import CONFIGS, make_workload
+from workloads import WORKLOADS, make_workload
 
 
 def test_table_covers_the_benchmark_workloads():
     table = load_table()
-    for c in range(1, len(CONFIGS)):
-        cfg = CONFIGS[c]
+    for c in range(1, len(WORKLOADS)):
+        cfg = WORKLOADS[c]
         key = shape_key(cfg["hidden"], cfg["num_tokens"], cfg["max_loras"], cfg["slices"],
                         cfg["rank"])
         assert key in table, key
@@ -37,4 +37,4 @@ def test_plan_falls_back_to_the_rule():
     p = plan(4096, 300, 4, [4096], 8)  # a shape the table does not hold
     assert p["source"] == "size rule" and p["expand"] is None
     assert p["num_splits"] == srg.lora_shrink_default_splits(4096, 300, 4, 1, 8)
-    assert make_workload(1).max_tokens == CONFIGS[1]["num_tokens"]
+    assert make_workload(1).max_tokens == WORKLOADS[1]["num_tokens"]

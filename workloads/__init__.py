@@ -6,7 +6,7 @@ arithmetic, so both the GPU path and the CPU oracle can consume what it makes.
 """
 
 from .gen import (  # noqa: F401
-    CONFIGS,
+    WORKLOADS,
     Workload,
     bf16_bits_from_f32,
     f32_from_bf16_bits,

@@ -39,7 +39,7 @@ import numpy as np
 # --------------------------------------------------------------------------
 # The five workloads.  ``ids`` describes how the token -> adapter map is drawn.
 # --------------------------------------------------------------------------
-CONFIGS = [
+WORKLOADS = [
     dict(
         name="tiny",
         num_tokens=16, hidden=256, slices=[256], rank=8, max_loras=2, scale=1.0,
@@ -184,7 +184,7 @@ def make_workload(index: int, seed: Optional[int] = None, num_tokens: Optional[i
     reduced-size parity cases; ``max_tokens`` (default ``num_tokens``) sizes the
     row dimension of x and y0, rows beyond ``num_tokens`` being extra draws.
     """
-    cfg = CONFIGS[index]
+    cfg = WORKLOADS[index]
     rng = np.random.default_rng(index if seed is None else seed)
     T = cfg["num_tokens"] if num_tokens is None else int(num_tokens)
     maxT = T if max_tokens is None else int(max_tokens)
@@ -205,7 +205,7 @@ def make_mapping(index: int, seed: Optional[int] = None,
                  num_tokens: Optional[int] = None) -> np.ndarray:
     """Only the adapter map of workload ``index`` (identical to the one
     ``make_workload`` draws with the same seed and size: it is the first draw)."""
-    cfg = CONFIGS[index]
+    cfg = WORKLOADS[index]
     rng = np.random.default_rng(index if seed is None else seed)
     T = cfg["num_tokens"] if num_tokens is None else int(num_tokens)
     return _draw_mapping(rng, T, cfg["ids"])
