@@ -42,6 +42,16 @@ __device__ __forceinline__ u32x2 load8(const void* p) {
 }
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *(LORA_GLOBAL u32x4*)(p) = v; }
 
+// 16 bytes per lane from global memory straight into LDS (gfx950's
+// global_load_lds_dwordx4): lane i's bytes land at lds + 16 i, so one
+// instruction fills 1 KB of LDS in lane order while each lane names its own
+// source.  `lds` must be the same for every lane of the wave.  Completion is
+// counted like any vector load (vmcnt); no VGPR holds the data.
+__device__ __forceinline__ void load16_to_lds(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((LORA_GLOBAL void*)(src),
+                                   (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+}
+
 // Streamed data touched once (the y rows): non-temporal hint, so it does not
 // displace the adapter weights that every tile re-reads from L2.
 __device__ __forceinline__ u32x4 load16_stream(const void* p) {

@@ -52,17 +52,33 @@ __device__ __forceinline__ int round_up_tile(int v) {
   return (v + kMetaTile - 1) / kMetaTile * kMetaTile;
 }
 
+// LDS of one metadata workgroup.
+template <int THREADS>
+struct MetaLds {
+  static constexpr int kWaves = THREADS / kWave;
+  int present[LORA_MAX_LORAS + 1];
+  int wave_below[kWaves], wave_members[kWaves], wave_none[kWaves], wave_scan[kWaves];
+  int wave_runs[kWaves];
+  int32_t staged[THREADS * kPerThread];  // one block's members of g, in rank order
+};
+
 // Group g's share of the metadata, by one workgroup of THREADS threads (every
 // thread of the workgroup calls it); a block of the map is THREADS * 8 tokens.
+// `sh`: the workgroup's LDS for it (a kernel whose other workgroups need more
+// LDS for other work passes part of that, so that it does not add to it).
 template <int THREADS>
 __device__ __forceinline__ void metadata_group(const int32_t* __restrict__ mapping, int num_tokens,
-                                               int max_loras, const MetaOut& out, int g) {
+                                               int max_loras, const MetaOut& out, int g,
+                                               MetaLds<THREADS>& sh) {
   constexpr int kWaves = THREADS / kWave;
   constexpr int kBlock = THREADS * kPerThread;
-  __shared__ int present[LORA_MAX_LORAS + 1];
-  __shared__ int wave_below[kWaves], wave_members[kWaves], wave_none[kWaves], wave_scan[kWaves];
-  __shared__ int wave_runs[kWaves];
-  __shared__ int32_t staged[kBlock];  // one block's members of g, in rank order
+  int* const present = sh.present;
+  int* const wave_below = sh.wave_below;
+  int* const wave_members = sh.wave_members;
+  int* const wave_none = sh.wave_none;
+  int* const wave_scan = sh.wave_scan;
+  int* const wave_runs = sh.wave_runs;
+  int32_t* const staged = sh.staged;
 
   const int groups = max_loras + 1;
   const int tid = threadIdx.x;
@@ -200,6 +216,14 @@ __device__ __forceinline__ void metadata_group(const int32_t* __restrict__ mappi
     placed += block_total;
     if (b0 + kBlock < num_tokens) __syncthreads();  // wave_scan and staged are reused
   }
+}
+
+// The same, with LDS of its own.
+template <int THREADS>
+__device__ __forceinline__ void metadata_group(const int32_t* __restrict__ mapping, int num_tokens,
+                                               int max_loras, const MetaOut& out, int g) {
+  __shared__ MetaLds<THREADS> sh;
+  metadata_group<THREADS>(mapping, num_tokens, max_loras, out, g, sh);
 }
 
 }  // namespace lora

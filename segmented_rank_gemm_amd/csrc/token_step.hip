@@ -129,7 +129,9 @@ __device__ __forceinline__ int adapter_of(const TokenParams& p, int t) {
 // 16-token blocks held by every wave, each A piece feeding MW matrix-core
 // ops).  Every thread of the workgroup calls it.  COHERENT: the part is
 // written with device-coherent stores (read by other workgroups of the same
-// launch).  `red` is the LDS of the cross-wave sum, NB * 4 KB.
+// launch).  `red` is the unit's LDS: with one chunk per wave, each wave's
+// A rows (16 * NB rows of 128 bytes, 2 KB per block) and then its share of the
+// cross-wave sum, NB * 8 KB in all; otherwise the cross-wave sum, NB * 4 KB.
 template <int NB, int MW, int DEPTH, bool COHERENT>
 __device__ __forceinline__ void token_shrink_unit(const TokenParams& p, int u, f32x4* red,
                                                   const uint16_t* const* slice_a) {
@@ -218,8 +220,6 @@ __device__ __forceinline__ void token_shrink_unit(const TokenParams& p, int u, f
   int kc = kbeg + wave * kShrinkChunk;
   const int nw = kc < kend ? (kend - kc + kStride - 1) / kStride : 0;  // wave-uniform
   kc = kc < kend ? kc : ksafe;
-  Chunk c0;
-  load(kc, c0);
 
   f32x4 acc[MW][NB];
 #pragma unroll
@@ -244,11 +244,83 @@ __device__ __forceinline__ void token_shrink_unit(const TokenParams& p, int u, f
     }
   };
   if constexpr (DEPTH == 1) {
-    // at most one chunk per wave (parts of at most 256 elements): one register set
-    if (nw > 0) mma(c0);
+    // At most one chunk per wave (parts of at most 256 elements).  A goes
+    // through this wave's own LDS region with whole-line loads: instruction j
+    // fetches rows 8j..8j+7 of the group, 8 lanes per 128-byte line (lane
+    // 8 rr + e reads row 8j + rr, piece e ^ rr, so the region holds row R's
+    // piece q at 16-byte slot 8R + (q ^ (R & 7)) and the MFMA-layout reads
+    // below hit distinct banks).  A load in the operand layout would touch 16
+    // lines for half a line each; whole lines move faster through the CU.
+    // Rows 8j..8j+7 are ranks 8i..8i+7 of one (adapter, slice) (r is a
+    // multiple of 8): contiguous rows of one A_s.  A group past the last
+    // output re-reads the last one (masked by amask).  x stays in registers.
+    u32x4* const stg = reinterpret_cast<u32x4*>(red) + wave * (2 * NB * kWave);
+    {
+      const int rr = lane >> 3;
+      const int kq = kc + 8 * ((lane & 7) ^ rr);
+      const int lane_off = rr * p.hidden + (kq < kend ? kq : ksafe);
+      int l = o0 / p.sr;  // (adapter, position in its S*r outputs) of row group j
+      int rem = o0 - l * p.sr;
+      // the slices' A from the kernel arguments, held as values in scalar
+      // registers (an LDS read between these loads would wait for every one
+      // issued before it; a select of argument addresses, for a scalar load)
+      uint64_t sa_v[LORA_MAX_SLICES];
+#pragma unroll
+      for (int s = 0; s < LORA_MAX_SLICES; ++s) {
+        sa_v[s] = reinterpret_cast<uint64_t>(p.a[s]);
+        asm volatile("" : "+s"(sa_v[s]));
+      }
+#pragma unroll
+      for (int j = 0; j < 2 * NB; ++j) {
+        const bool past = o0 + 8 * j >= p.nout;  // workgroup-uniform
+        const int lj = past ? p.max_loras - 1 : l;
+        const int rj = past ? p.sr - 8 : rem;
+        const int sj = rj >> p.rank_shift;
+        uint64_t sa = sa_v[0];
+#pragma unroll
+        for (int s = 1; s < LORA_MAX_SLICES; ++s) sa = sj == s ? sa_v[s] : sa;
+        const uint16_t* base = reinterpret_cast<const uint16_t*>(sa) +
+                               (static_cast<int64_t>(lj) * p.rank + (rj & (p.rank - 1))) * p.hidden;
+        load16_to_lds(base + lane_off, stg + j * kWave);
+        rem += 8;
+        if (rem == p.sr) {
+          rem = 0;
+          ++l;
+        }
+      }
+    }
+    u32x4 xv[MW][2];
+    uint32_t kmask[2];
+    {
+      const bool full = kc + kShrinkChunk <= kend;  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int k = piece(kc, i, full, kmask[i]);
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb) xv[mb][i] = load16(xrow[mb] + k);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (nw > 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb) xv[mb][i] &= xmask[mb] & kmask[i];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const u32x4 av = stg[(16 * nb + col) * 8 + ((4 * i + grp) ^ (col & 7))] & amask[nb];
+#pragma unroll
+          for (int mb = 0; mb < MW; ++mb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, xv[mb][i]),
+                acc[mb][nb], 0, 0, 0);
+        }
+      }
+    }
   } else if (nw > 0) {
     // two chunks in flight, alternating two register sets (as in shrink.hip)
-    Chunk c1;
+    Chunk c0, c1;
+    load(kc, c0);
     int j = 0;
     for (; j + 2 < nw; j += 2) {
       load(kc + (j + 1) * kStride, c1);
@@ -271,17 +343,20 @@ __device__ __forceinline__ void token_shrink_unit(const TokenParams& p, int u, f
   // The four waves' sums in wave order, one 16-token block at a time; wave w
   // stores output blocks w, w+4, ...  This lane holds outputs o0 + 16*nb +
   // 4*grp + j (j < 4) of token tok[mb]: one adapter and one slice (r is a
-  // multiple of 8); kept if the adapter is the token's.
+  // multiple of 8); kept if the adapter is the token's.  Each wave's sums go
+  // to the start of its own A region (with one chunk per wave), which only it
+  // has read so far.
+  constexpr int kRedWave = DEPTH == 1 ? 2 * NB : NB;  // f32x4 blocks of 64 between waves
   const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(p.buf, p.buf_bytes);
 #pragma unroll
   for (int mb = 0; mb < MW; ++mb) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) red[(wave * NB + nb) * kWave + lane] = acc[mb][nb];
+    for (int nb = 0; nb < NB; ++nb) red[(wave * kRedWave + nb) * kWave + lane] = acc[mb][nb];
     __syncthreads();
     for (int nb = wave; nb < NB; nb += kShrinkWaves) {
       f32x4 v = red[nb * kWave + lane];
 #pragma unroll
-      for (int w = 1; w < kShrinkWaves; ++w) v += red[(w * NB + nb) * kWave + lane];
+      for (int w = 1; w < kShrinkWaves; ++w) v += red[(w * kRedWave + nb) * kWave + lane];
       const int o = o0 + 16 * nb + 4 * grp;
       const int l = o / p.sr;
       if (o < p.nout && l == lid[mb]) {
@@ -588,8 +663,10 @@ __device__ __forceinline__ void token_expand_unit(const TokenParams& p, int u, u
 
 // STEP = false: lora_prepare_and_shrink for small batches (shrink workgroups,
 // then metadata workgroups; plain stores, no counters).  STEP = true: the
-// one-launch step.  Dynamic LDS: the shrink's cross-wave sums (NB * 4 KB) or
-// the expand's B regions (4 waves * LCAP adapters * 256 * RANK bytes).
+// one-launch step.  Dynamic LDS: the shrink's (NB * 8 KB with one chunk per
+// wave, NB * 4 KB otherwise), the expand's B regions (4 waves * LCAP
+// adapters * 256 * RANK bytes) or the metadata's, whichever is largest: every
+// workgroup does one kind of work, so they share it.
 // Waves per SIMD each instantiation is built for: three where the registers
 // fit without spilling (the decode shapes), so that a one-launch grid of
 // shrink, expand and metadata workgroups is resident at once; two otherwise.
@@ -608,7 +685,8 @@ void token_kernel(TokenParams p) {
   const int b = blockIdx.x;
   const int work = p.shrink_grid + (STEP ? p.expand_grid : 0);
   if (b >= work) {  // workgroup-uniform
-    metadata_group<kShrinkThreads>(p.mapping, p.num_tokens, p.max_loras, p.meta_out, b - work);
+    metadata_group<kShrinkThreads>(p.mapping, p.num_tokens, p.max_loras, p.meta_out, b - work,
+                                   *reinterpret_cast<MetaLds<kShrinkThreads>*>(tok_lds));
     return;
   }
   if (threadIdx.x < LORA_MAX_SLICES) slice_a[threadIdx.x] = p.a[threadIdx.x];
@@ -745,12 +823,15 @@ template <int NB, int DEPTH, int RANK, int LCAP, bool STEP>
 static hipError_t launch_token(const TokenParams& p, hipStream_t stream) {
   constexpr int MW = kTokShrinkMw;
   const int grid = p.shrink_grid + (STEP ? p.expand_grid : 0) + p.max_loras + 1;
-  const size_t red = static_cast<size_t>(kShrinkWaves) * NB * kWave * sizeof(f32x4);
+  // one chunk per wave: A staged per wave (twice the sums' size), the sums in it
+  const size_t red = static_cast<size_t>(kShrinkWaves) * NB * kWave * sizeof(f32x4) * (DEPTH == 1 ? 2 : 1);
   const size_t bst = STEP ? static_cast<size_t>(kShrinkWaves) * LCAP * 16 * RANK * sizeof(u32x4) +
                                16 * RANK * sizeof(float)
                           : 0;
+  size_t lds = red > bst ? red : bst;
+  lds = lds > sizeof(MetaLds<kShrinkThreads>) ? lds : sizeof(MetaLds<kShrinkThreads>);
   hipLaunchKernelGGL((token_kernel<NB, MW, DEPTH, RANK, LCAP, STEP>), dim3(grid), dim3(kShrinkThreads),
-                     red > bst ? red : bst, stream, p);
+                     lds, stream, p);
   return hipGetLastError();
 }
 
@@ -784,13 +865,13 @@ hipError_t launch_token_prep_shrink(const int32_t* mapping, int num_tokens, cons
   return launch_token_nb<8, 4, false>(p, nb, stream);
 }
 
-// Default hold-off of the expand units (ns): the time a shrink unit's own
-// loads take to arrive, about 30 ns per KB of A and x it reads (measured on
-// the decode batch: a unit reading 56 KB, best at 1.5-1.9 us, 5% off the
-// step; the time is flat within +-0.2 us of the best and grows fast past it).
+// Default hold-off of the expand units (ns): about the time a shrink unit's
+// own loads take to arrive, 36 ns per KB of A and x it reads (measured on the
+// decode batch: a unit reading 56 KB, best at 1.9-2.2 us, 6% off the step
+// without a hold-off; 0.2 us either side costs up to 1%, 0.5 us up to 4%).
 static int token_step_default_delay_ns(const TokenParams& p, int nb) {
   const int64_t bytes = static_cast<int64_t>(16 * nb + kTokTile * kTokShrinkMw) * p.split_len * 2;
-  return static_cast<int>(30 * bytes / 1024);
+  return static_cast<int>(36 * bytes / 1024);
 }
 
 // The one-launch step.  The caller checked token_step_fits and the workspace.

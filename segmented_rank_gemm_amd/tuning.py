@@ -236,7 +236,7 @@ def start_delay_for(lora_b: Sequence[torch.Tensor], num_splits: int,
     return int(e["start_delay_ns"])
 
 
-_DELAY_CANDIDATES_NS = (0, 800, 1000, 1200, 1400, 1600, 1800, 2000, 2200, 2600)
+_DELAY_CANDIDATES_NS = (0, 800, 1200, 1400, 1600, 1800, 1900, 2000, 2100, 2200, 2400, 2600, 3000)
 
 
 def _expand_candidates(rank: int) -> List[ExpandConfig]:
