@@ -83,6 +83,14 @@ __device__ __forceinline__ u32x2 load8_coherent(__amdgpu_buffer_rsrc_t r, uint32
 __device__ __forceinline__ void store16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCachePolicyCoherent);
 }
+// Streamed data written through to that level as well (sc1 with the
+// non-temporal hint): no dirty line of it is left in an XCD's L2 when the
+// kernel ends.
+constexpr int kCachePolicyStreamCoherent = 18;  // sc1 | nt
+__device__ __forceinline__ void store16_stream_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                        u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCachePolicyStreamCoherent);
+}
 
 // Low / high bf16 of a packed pair, widened exactly to fp32.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -192,6 +192,38 @@ def test_fused_step_start_delay_same_bits(T, maxT, hidden, slices, rank, L, spli
     H.full_check(w, runs[0])
 
 
+def test_fused_step_y_beyond_4gib():
+    """y rows 8 MiB apart, so that the step's y spans more than 4 GiB: the
+    one-launch kernel then stores y through 64-bit addresses instead of the
+    32-bit offsets of its written-through stores.  Same criteria; the row
+    padding keeps its sentinel."""
+    T, hidden, slices, rank, L = 512, 256, [128, 136], 8, 4
+    ldy = (1 << 22) + 64  # elements: T * ldy * 2 bytes > 4 GiB
+    assert T * ldy * 2 >= 1 << 32
+    assert srg.lora_fused_step_launches(T, L, len(slices), rank) == 1
+    rng = np.random.default_rng(4242)
+    mapping = rng.integers(-1, L, size=T)
+    w = make_custom_workload(4242, T, hidden, slices, rank, L, 1.5, mapping)
+    d = H.upload(w)
+    big = torch.full((T, ldy), 0x7FC1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    big[:, :w.n_total] = d.y[:, :w.n_total]
+    d.y = big
+    ws = _workspace(w)
+    _run_fused(d, ws)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0
+    ref = oracle.run_step(w)
+    act = H.sanitize(w.mapping, L) >= 0
+    yg = H.from_dev_bf16(big[:, :w.n_total])
+    rep = H.y_report(yg, ref["y64"], ref["y_bf16"])
+    assert rep["max_excess_over_half_ulp"] <= rep["tol"], rep
+    assert np.array_equal(yg[~act], w.y0[~act])
+    for lo in (w.n_total, ldy - 64):
+        assert np.all(H.from_dev_bf16(big[:, lo:lo + 64]) == 0x7FC1), lo
+    del big, d
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("T,maxT,hidden,slices,rank,L,scale,splits", [
     (900, 1024, 2048, [1024], 64, 16, 0.75, 6),             # down_proj-like: 6 parts in one batch
     (1000, 1000, 1536, [384, 128], 64, 9, 1.25, 5),         # rank 64, 5 parts in one batch
