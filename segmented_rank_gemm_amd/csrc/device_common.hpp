@@ -52,8 +52,9 @@ __device__ __forceinline__ void load16_to_lds(const void* src, void* lds) {
                                    (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
 }
 
-// Streamed data touched once (the y rows): non-temporal hint, so it does not
-// displace the adapter weights that every tile re-reads from L2.
+// Streamed data touched once (the y rows; x rows where one unit reads them):
+// non-temporal hint, so it does not displace the adapter weights that every
+// tile re-reads from L2.
 __device__ __forceinline__ u32x4 load16_stream(const void* p) {
   return __builtin_nontemporal_load((const LORA_GLOBAL u32x4*)(p));
 }
