@@ -261,6 +261,9 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
     };
     const uint16_t* xrow[MW];
     uint32_t xmask[MW];
+    // x rows with the streaming hint: read once per unit, while the A rows
+    // are re-read by every tile of the adapter (decode shrink 4.79 -> 4.62 us;
+    // the large-batch kernels, whose x goes through LDS, did not move)
     auto load_x = [&](int kc, Chunk& c) {
       const bool full = kc + kShrinkChunk <= kend;
 #pragma unroll
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
         uint32_t km;
         const int k = piece(kc, i, full, km);
 #pragma unroll
-        for (int mb = 0; mb < MW; ++mb) c.x[mb][i] = load16(xrow[mb] + k);
+        for (int mb = 0; mb < MW; ++mb) c.x[mb][i] = load16_stream(xrow[mb] + k);
       }
     };
 
