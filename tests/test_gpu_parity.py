@@ -427,6 +427,10 @@ PREP_CASES = [  # T, maxT, hidden, slices, rank, L, kind, splits
     (512, 512, 1024, [256, 256, 256, 256], 64, 16, "runs", 4),  # 16 output blocks: 2 groups
     (700, 720, 1024, [512, 512], 16, 4, "wild", 3),             # larger: two launches
     (3000, 3500, 512, [256, 128], 32, 40, "runs", 4),           # 512-thread metadata
+    # one chunk per wave, A rows straight into LDS:
+    (96, 96, 1000, [128], 8, 16, "wild", 4),       # 8 output blocks; the last part's last chunk partial
+    (64, 80, 96, [40], 8, 5, "wild", 1),           # 40 outputs in 4 blocks; waves 2-3 have no chunk
+    (33, 48, 200, [64, 64], 16, 3, "runs", 1),     # 6 blocks; a chunk of 8 elements
 ]
 
 
