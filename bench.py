@@ -114,7 +114,7 @@ class Sets:
     every expand call takes the given launch choices."""
 
     def __init__(self, w, R, num_splits, expand_cfg=None, start_delay_ns=None, part_sums=False,
-                 batch_order_shrink=False):
+                 batch_order_shrink=False, y_delay_ns=None):
         import torch
 
         import segmented_rank_gemm_amd as srg
@@ -123,6 +123,7 @@ class Sets:
         self.w, self.R, self.num_splits = w, R, num_splits
         self.expand_cfg = expand_cfg
         self.start_delay_ns = start_delay_ns  # None: the library's default
+        self.y_delay_ns = y_delay_ns
         self.part_sums = bool(part_sums)
         self.batch_order_shrink = bool(batch_order_shrink)
         T, maxT = w.num_tokens, w.max_tokens
@@ -204,7 +205,8 @@ class Sets:
                             s["buf"], self.num_splits, s["y"], m, self.workspace, stream=stream,
                             expand_config=self.expand_cfg, start_delay_ns=self.start_delay_ns,
                             part_sums=self.part_sums,
-                            batch_order_shrink=self.batch_order_shrink)
+                            batch_order_shrink=self.batch_order_shrink,
+                            y_delay_ns=self.y_delay_ns)
 
     def step(self, r, stream=None):
         """The whole path: lora_fused_step."""
@@ -333,14 +335,15 @@ def run_config(idx, args):
     pl = plan(w.hidden, w.max_tokens, w.max_loras, w.slices, w.rank)
     if args.rules:
         pl = {"num_splits": rule_splits, "expand": srg.ExpandConfig(), "start_delay_ns": None,
-              "part_sums": False, "batch_order_shrink": False, "source": "size rule"}
+              "y_delay_ns": None, "part_sums": False, "batch_order_shrink": False,
+              "source": "size rule"}
     splits = pl["num_splits"]
     expand_cfg = pl["expand"] or srg.ExpandConfig()
     sb = set_bytes(w, splits)
     R = args.rotate or max(2, math.ceil(ROTATE_BYTES / sb))
     log(f"[bench] {R} rotated buffer sets of {sb / 1e6:.1f} MB, {splits} shrink parts")
     sets = Sets(w, R, splits, expand_cfg, pl["start_delay_ns"], pl["part_sums"],
-                pl["batch_order_shrink"])
+                pl["batch_order_shrink"], pl["y_delay_ns"])
 
     # eager pass on every set so the metadata exists before single-kernel graphs replay
     for r in range(R):
@@ -535,6 +538,7 @@ def run_config(idx, args):
             "shrink_parts_from": pl["source"], "shrink_parts_rule": rule_splits,
             "expand_config": expand_cfg.as_dict(), "expand_config_from": pl["source"],
             "start_delay_ns": pl["start_delay_ns"] if pl["start_delay_ns"] is not None else "default",
+            "y_delay_ns": pl["y_delay_ns"] if pl["y_delay_ns"] is not None else "default",
             "part_sums": pl["part_sums"], "batch_order_shrink": pl["batch_order_shrink"],
             "rotated_sets": R, "rotated_sets_per_kernel": rot, "parallelism": "single GPU",
         },

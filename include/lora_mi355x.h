@@ -353,11 +353,12 @@ typedef struct lora_step_options {
   int32_t wait_polls;
   /* Launch choices of the expand on the multi-launch path (see lora_expand). */
   lora_expand_config_t expand;
-  /* One-launch path: how long (ns) each expand workgroup holds its own y and
-   * B loads back after it starts, so that the shrink workgroups' loads, which
-   * share each CU's fetch path with them, are served first.  Changes timing
-   * only, never results.  Negative: a default from the shrink's per-workgroup
-   * bytes; 0: no hold-off; above 100000: LORA_ERR_INVALID_ARGUMENT. */
+  /* One-launch path: how long (ns) each expand workgroup holds its own B
+   * loads back after it starts, so that the shrink workgroups' loads, which
+   * share each CU's fetch path with them, are served first (its y loads: see
+   * y_delay_ns).  Changes timing only, never results.  Negative: a default
+   * from the shrink's per-workgroup bytes; 0: no hold-off; above 100000:
+   * LORA_ERR_INVALID_ARGUMENT. */
   int32_t start_delay_ns;
   /* Multi-launch path, large batches at rank 32 or 64: 1 = the shrink sums
    * the parts for the expand (see above); 0 or negative = the expand sums
@@ -372,6 +373,11 @@ typedef struct lora_step_options {
    * drawn per token.  0 or negative: off (the default).  Ignored together
    * with part_sums = 1. */
   int32_t batch_order_shrink;
+  /* One-launch path: the same for the expand workgroups' y loads, which go
+   * out before their B loads (y comes from HBM, B mostly from L2); a value
+   * above start_delay_ns issues B right after y.  Same range and meaning of
+   * negative and 0. */
+  int32_t y_delay_ns;
 } lora_step_options_t;
 
 int64_t lora_fused_step_workspace_bytes(int32_t max_tokens, int32_t max_loras,

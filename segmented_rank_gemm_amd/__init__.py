@@ -73,7 +73,7 @@ class ExpandConfig(ctypes.Structure):
 class _StepOptions(ctypes.Structure):
     _fields_ = [("wait_polls", ctypes.c_int32), ("expand", ExpandConfig),
                 ("start_delay_ns", ctypes.c_int32), ("part_sums", ctypes.c_int32),
-                ("batch_order_shrink", ctypes.c_int32)]
+                ("batch_order_shrink", ctypes.c_int32), ("y_delay_ns", ctypes.c_int32)]
 
 
 def _expand_config(config, lora_b=None, num_splits=None, meta=None) -> Optional[ExpandConfig]:
@@ -90,15 +90,16 @@ def _expand_config(config, lora_b=None, num_splits=None, meta=None) -> Optional[
     return ExpandConfig(**config)
 
 
-def _start_delay(start_delay_ns, lora_b=None, num_splits=None, meta=None) -> Optional[int]:
+def _start_delay(start_delay_ns, lora_b=None, num_splits=None, meta=None,
+                 name="start_delay_ns") -> Optional[int]:
     """None: the library's default; "table": the measured choice for the call's
     shape in segmented_rank_gemm_amd/tuning_table.json (the default if the
     table does not have it); else nanoseconds."""
     if isinstance(start_delay_ns, str):
         if start_delay_ns != "table":
-            raise ValueError(f"start delay {start_delay_ns!r}: expected 'table', None or ns")
+            raise ValueError(f"{name} {start_delay_ns!r}: expected 'table', None or ns")
         from .tuning import start_delay_for
-        return start_delay_for(lora_b, num_splits, meta)
+        return start_delay_for(lora_b, num_splits, meta, name)
     return None if start_delay_ns is None else int(start_delay_ns)
 
 
@@ -114,16 +115,19 @@ def _table_flag(value, name, lora_b, num_splits, meta) -> bool:
 
 
 def _step_options(wait_polls, expand_config, start_delay_ns=None, lora_b=None, num_splits=None,
-                  meta=None, part_sums=False, batch_order_shrink=False):
+                  meta=None, part_sums=False, batch_order_shrink=False, y_delay_ns=None):
     cfg = _expand_config(expand_config, lora_b, num_splits, meta)
     delay = _start_delay(start_delay_ns, lora_b, num_splits, meta)
+    y_delay = _start_delay(y_delay_ns, lora_b, num_splits, meta, "y_delay_ns")
     sums = _table_flag(part_sums, "part_sums", lora_b, num_splits, meta)
     batch = _table_flag(batch_order_shrink, "batch_order_shrink", lora_b, num_splits, meta)
-    if wait_polls is None and cfg is None and delay is None and not sums and not batch:
+    if (wait_polls is None and cfg is None and delay is None and y_delay is None and not sums
+            and not batch):
         return None
     cfg = cfg or ExpandConfig()
     return ctypes.byref(_StepOptions(-1 if wait_polls is None else int(wait_polls), cfg,
-                                     -1 if delay is None else delay, int(sums), int(batch)))
+                                     -1 if delay is None else delay, int(sums), int(batch),
+                                     -1 if y_delay is None else y_delay))
 
 
 TILE = 16  # positions per tile of the padded grouped order (LORA_TILE)
@@ -372,11 +376,12 @@ def lora_fused_step(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.
                     workspace: Optional[torch.Tensor], wait_polls: Optional[int] = None,
                     stream: Optional[torch.cuda.Stream] = None, expand_config="table",
                     start_delay_ns="table", part_sums="table",
-                    batch_order_shrink="table") -> None:
+                    batch_order_shrink="table", y_delay_ns="table") -> None:
     """Metadata, shrink and expand of one batch (one launch where the sizes
     allow); arguments as for lora_prepare_and_shrink and lora_expand, plus the
     zero-filled workspace of fused_step_workspace (reused call after call).
-    start_delay_ns: the one-launch path's expand hold-off (timing only);
+    start_delay_ns, y_delay_ns: the one-launch path's expand hold-offs before
+    its B and its y loads (timing only; None: the library's defaults);
     part_sums: large rank-32/64 batches, the shrink sums the parts for the
     expand (same bits); batch_order_shrink: large batches, the shrink in batch
     order beside the metadata in one launch (same bits).  "table": the
@@ -390,7 +395,7 @@ def lora_fused_step(token_lora_mapping: torch.Tensor, num_tokens: int, x: torch.
     if workspace is not None:
         wptr, wbytes = _flat_dev_bytes(workspace, "workspace")
     opts = _step_options(wait_polls, expand_config, start_delay_ns, lora_b, num_splits, meta,
-                         part_sums, batch_order_shrink)
+                         part_sums, batch_order_shrink, y_delay_ns)
     _check("lora_fused_step", lib().lora_fused_step(
         ptr, int(num_tokens), _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), hidden, aptrs,
         bptrs, nsz, S, rank, float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits),
@@ -403,7 +408,8 @@ def lora_fused_step_static(token_lora_mapping: torch.Tensor, num_tokens: int, x:
                            scale: float, buf: torch.Tensor, num_splits: int, y: torch.Tensor,
                            meta: LoraMeta, wait_polls: Optional[int] = None,
                            stream: Optional[torch.cuda.Stream] = None, expand_config="table",
-                           start_delay_ns="table", batch_order_shrink="table") -> None:
+                           start_delay_ns="table", batch_order_shrink="table",
+                           y_delay_ns="table") -> None:
     """lora_fused_step with the library's own counter array instead of a
     workspace (nothing is allocated; calls that overlap on one GPU race).
     No part sums (they need a workspace); the other launch choices as for
@@ -414,7 +420,7 @@ def lora_fused_step_static(token_lora_mapping: torch.Tensor, num_tokens: int, x:
     if Sb != S or rank_b != rank:
         raise ValueError("lora_a and lora_b disagree on slices or rank")
     opts = _step_options(wait_polls, expand_config, start_delay_ns, lora_b, num_splits, meta,
-                         False, batch_order_shrink)
+                         False, batch_order_shrink, y_delay_ns)
     _check("lora_fused_step_static", lib().lora_fused_step_static(
         ptr, int(num_tokens), _dev_ptr(x, torch.bfloat16, "x"), int(x.stride(0)), hidden, aptrs,
         bptrs, nsz, S, rank, float(scale), _dev_ptr(buf, torch.float32, "buf"), int(num_splits),

@@ -41,8 +41,8 @@ hipError_t launch_token_step(const int32_t* mapping, int num_tokens, const uint1
                              const uint16_t* const* lora_b, const int32_t* slice_sizes,
                              int num_slices, int rank, float scale, float* buf, int num_splits,
                              uint16_t* y, int64_t ldy, const lora_meta_t& meta, int* counters,
-                             int wait_polls, int start_delay_ns, int max_tokens, int max_loras,
-                             hipStream_t stream);
+                             int wait_polls, int start_delay_ns, int y_delay_ns, int max_tokens,
+                             int max_loras, hipStream_t stream);
 int64_t token_step_scratch_bytes();
 hipError_t token_step_scratch(int** out);
 int shrink_group_blocks(int nb_total);
@@ -53,7 +53,7 @@ namespace {
 
 constexpr int32_t kMaxTokens = 1 << 24;
 constexpr int32_t kMaxHidden = 65536;
-constexpr int32_t kMaxStartDelayNs = 100000;  // lora_step_options_t.start_delay_ns
+constexpr int32_t kMaxStartDelayNs = 100000;  // lora_step_options_t.start_delay_ns, y_delay_ns
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -295,7 +295,9 @@ static lora_status_t fused_step(const int32_t* token_lora_mapping, int32_t num_t
   st = expand_args(buf, num_splits, lora_b, slice_sizes, num_slices, rank, y, ldy);
   if (st != LORA_OK) return st;
   if (!expand_config_ok(options_expand(options), rank)) return LORA_ERR_INVALID_ARGUMENT;
-  if (options && options->start_delay_ns > kMaxStartDelayNs) return LORA_ERR_INVALID_ARGUMENT;
+  if (options && (options->start_delay_ns > kMaxStartDelayNs ||
+                  options->y_delay_ns > kMaxStartDelayNs))
+    return LORA_ERR_INVALID_ARGUMENT;
   const int64_t need = lora_fused_step_workspace_bytes(max_tokens, max_loras, num_slices, rank);
   const bool one_launch = lora::token_step_fits(max_tokens, max_loras, num_slices, rank);
   if (need > 0 && one_launch) {
@@ -311,9 +313,10 @@ static lora_status_t fused_step(const int32_t* token_lora_mapping, int32_t num_t
     }
     const int polls = options && options->wait_polls >= 0 ? options->wait_polls : 65536;
     const int delay = options ? options->start_delay_ns : -1;
+    const int y_delay = options ? options->y_delay_ns : -1;
     return launch_status(lora::launch_token_step(
         token_lora_mapping, num_tokens, x, ldx, hidden, lora_a, lora_b, slice_sizes, num_slices,
-        rank, scale, buf, num_splits, y, ldy, *meta, counters, polls, delay, max_tokens,
+        rank, scale, buf, num_splits, y, ldy, *meta, counters, polls, delay, y_delay, max_tokens,
         max_loras, stream));
   }
   // Multi-launch path.  With a workspace (large batches at ranks 32 and 64):

@@ -105,7 +105,8 @@ struct TokenParams {
   int expand_grid;   // workgroups of the expand (a multiple of 8)
   int* counters;     // [tiles][kCounterInts]
   int wait_polls;
-  int start_delay_ticks;  // expand units' hold-off before their first loads, 100 MHz ticks
+  int start_delay_ticks;  // expand units' hold-off before their B loads, 100 MHz ticks
+  int y_delay_ticks;      // ... before their y loads
   MetaOut meta_out;  // written by the workgroups past shrink_grid + expand_grid
 };
 
@@ -475,16 +476,22 @@ __device__ __forceinline__ void token_expand_unit(const TokenParams& p, int u, u
     // Hold this unit's y and B loads back while the shrink units' loads are
     // served: they share each CU's fetch path with them, and the parts the
     // unit waits for come sooner that way; y and B still arrive before the
-    // parts do.  Timed on the chip's constant 100 MHz clock.
-    if (p.start_delay_ticks > 0) {
+    // parts do.  y (from HBM, the slower to arrive) goes out first, after a
+    // shorter hold-off, B (mostly L2 hits) after the longer one: on the decode
+    // batch 9.23 us per step against 9.90 with both at 2 us.  Timed on the
+    // chip's constant 100 MHz clock from here.
+    {
       const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
-      while (__builtin_amdgcn_s_memrealtime() - t_start <
-             static_cast<uint64_t>(p.start_delay_ticks))
-        __builtin_amdgcn_s_sleep(2);
-      asm volatile("" ::: "memory");
+      auto hold_until = [&](int ticks) {
+        while (__builtin_amdgcn_s_memrealtime() - t_start < static_cast<uint64_t>(ticks))
+          __builtin_amdgcn_s_sleep(2);
+        asm volatile("" ::: "memory");
+      };
+      hold_until(p.y_delay_ticks);
+      load_y();
+      hold_until(p.start_delay_ticks);
+      load_b();
     }
-    load_b();
-    load_y();
 
     // Every adapter's chunk into this wave's own LDS regions, while the
     // parts are still being computed.
@@ -880,13 +887,19 @@ hipError_t launch_token_prep_shrink(const int32_t* mapping, int num_tokens, cons
   return launch_token_nb<8, 4, false>(p, nb, stream);
 }
 
-// Default hold-off of the expand units (ns): about the time a shrink unit's
-// own loads take to arrive, 36 ns per KB of A and x it reads (measured on the
-// decode batch: a unit reading 56 KB, best at 1.9-2.2 us, 6% off the step
-// without a hold-off; 0.2 us either side costs up to 1%, 0.5 us up to 4%).
+// Default hold-offs of the expand units (ns), in proportion to what a shrink
+// unit loads (A and x): B after 46 ns per KB, y after 14 (measured on the
+// decode batch, a unit reading 56 KB: best at B 2.4-2.6 us with y 0.6-0.8 us,
+// 7% off the step with both at 2 us; y at 0 or 1.2 us, or B at 2.2 or 3 us,
+// cost 2-10%).
+static int64_t token_shrink_unit_kb(const TokenParams& p, int nb) {
+  return static_cast<int64_t>(16 * nb + kTokTile * kTokShrinkMw) * p.split_len * 2 / 1024;
+}
 static int token_step_default_delay_ns(const TokenParams& p, int nb) {
-  const int64_t bytes = static_cast<int64_t>(16 * nb + kTokTile * kTokShrinkMw) * p.split_len * 2;
-  return static_cast<int>(36 * bytes / 1024);
+  return static_cast<int>(46 * token_shrink_unit_kb(p, nb));
+}
+static int token_step_default_y_delay_ns(const TokenParams& p, int nb) {
+  return static_cast<int>(14 * token_shrink_unit_kb(p, nb));
 }
 
 // The one-launch step.  The caller checked token_step_fits and the workspace.
@@ -895,8 +908,8 @@ hipError_t launch_token_step(const int32_t* mapping, int num_tokens, const uint1
                              const uint16_t* const* lora_b, const int32_t* slice_sizes,
                              int num_slices, int rank, float scale, float* buf, int num_splits,
                              uint16_t* y, int64_t ldy, const lora_meta_t& meta, int* counters,
-                             int wait_polls, int start_delay_ns, int max_tokens, int max_loras,
-                             hipStream_t stream) {
+                             int wait_polls, int start_delay_ns, int y_delay_ns, int max_tokens,
+                             int max_loras, hipStream_t stream) {
   int nb = 2;
   TokenParams p = token_params(mapping, num_tokens, x, ldx, hidden, lora_a, num_slices, rank,
                                scale, buf, num_splits, meta, max_tokens, max_loras, nb);
@@ -924,7 +937,9 @@ hipError_t launch_token_step(const int32_t* mapping, int num_tokens, const uint1
   p.counters = counters;
   p.wait_polls = wait_polls;
   if (start_delay_ns < 0) start_delay_ns = token_step_default_delay_ns(p, nb);
+  if (y_delay_ns < 0) y_delay_ns = token_step_default_y_delay_ns(p, nb);
   p.start_delay_ticks = (start_delay_ns + 5) / 10;
+  p.y_delay_ticks = (y_delay_ns + 5) / 10;
   // y written through where its byte offsets fit 32 bits (all but y of 4 GiB
   // or more)
   const bool wt = static_cast<int64_t>(num_tokens) * ldy * 2 < (int64_t{1} << 32);

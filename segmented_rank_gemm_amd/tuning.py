@@ -11,9 +11,10 @@ change how the work is cut but never the result are:
   was captured with.
 * the expand's launch choices (``lora_expand_config_t``): the column-range
   length, the unit order and the workgroups per CU its grid is sized for.
-* on the one-launch path, how long the expand workgroups hold their own loads
-  back so that the shrink workgroups' loads are served first
-  (``lora_step_options_t.start_delay_ns``); on the multi-launch path for large
+* on the one-launch path, how long the expand workgroups hold their own B and
+  y loads back so that the shrink workgroups' loads are served first
+  (``lora_step_options_t.start_delay_ns``, ``y_delay_ns``); on the
+  multi-launch path for large
   rank-32/64 batches, whether the shrink sums the parts for the expand
   (``part_sums``); for large batches, whether the shrink runs in batch order
   beside the metadata (``batch_order_shrink``: faster on batches of request
@@ -182,17 +183,19 @@ def plan(hidden: int, max_tokens: int, max_loras: int, slices: Sequence[int],
     """Launch choices for a shape: the table's measured ones where the table
     has the shape, else the library's size rules.  Returns
     {"num_splits": n, "expand": ExpandConfig or None, "start_delay_ns": ns or None,
-     "part_sums": bool, "batch_order_shrink": bool, "source": "table" | "size rule"}."""
+     "y_delay_ns": ns or None, "part_sums": bool, "batch_order_shrink": bool,
+     "source": "table" | "size rule"}."""
     e = lookup(hidden, max_tokens, max_loras, slices, rank)
     if e is not None:
-        delay = e.get("start_delay_ns")
+        delay, y_delay = e.get("start_delay_ns"), e.get("y_delay_ns")
         return {"num_splits": int(e["num_splits"]), "expand": ExpandConfig(**e["expand"]),
                 "start_delay_ns": None if delay is None else int(delay),
+                "y_delay_ns": None if y_delay is None else int(y_delay),
                 "part_sums": bool(e.get("part_sums", False)),
                 "batch_order_shrink": bool(e.get("batch_order_shrink", False)), "source": "table"}
     return {"num_splits": lora_shrink_default_splits(hidden, max_tokens, max_loras, len(slices),
                                                      rank),
-            "expand": None, "start_delay_ns": None, "part_sums": False,
+            "expand": None, "start_delay_ns": None, "y_delay_ns": None, "part_sums": False,
             "batch_order_shrink": False, "source": "size rule"}
 
 
@@ -226,17 +229,20 @@ def flag_for(name: str, lora_b: Sequence[torch.Tensor], num_splits: int, meta: L
     return bool(e is not None and e.get(name, False))
 
 
-def start_delay_for(lora_b: Sequence[torch.Tensor], num_splits: int,
-                    meta: LoraMeta) -> Optional[int]:
-    """The table's one-launch expand hold-off (ns) for the call at hand, or
-    None (the library's default)."""
+def start_delay_for(lora_b: Sequence[torch.Tensor], num_splits: int, meta: LoraMeta,
+                    name: str = "start_delay_ns") -> Optional[int]:
+    """The table's one-launch expand hold-off `name` ("start_delay_ns" before
+    the B loads, "y_delay_ns" before the y loads) for the call at hand, in ns,
+    or None (the library's default)."""
     e = _entry_for(lora_b, num_splits, meta)
-    if e is None or e.get("start_delay_ns") is None:
+    if e is None or e.get(name) is None:
         return None
-    return int(e["start_delay_ns"])
+    return int(e[name])
 
 
-_DELAY_CANDIDATES_NS = (0, 800, 1200, 1400, 1600, 1800, 1900, 2000, 2100, 2200, 2400, 2600, 3000)
+# (y hold-off, B hold-off) pairs timed for one-launch shapes, ns
+_HOLD_CANDIDATES_NS = tuple((yd, bd) for yd in (0, 400, 600, 800, 1000, 1200)
+                            for bd in (1600, 2000, 2200, 2400, 2600, 2800, 3200))
 
 
 def _expand_candidates(rank: int) -> List[ExpandConfig]:
@@ -279,7 +285,7 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
                 a=[t.clone() for t in base["a"]], b=[t.clone() for t in base["b"]],
                 meta=LoraMeta(maxT, w.max_loras)) for _ in range(copies)]
 
-    def time_step(n, cfg, delay=None, sums=False, batch=False):
+    def time_step(n, cfg, delay=None, sums=False, batch=False, y_delay=None):
         bufs = [torch.empty((n, S, maxT, r), dtype=torch.float32, device="cuda")
                 for _ in range(copies)]
 
@@ -288,7 +294,8 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
             lora_fused_step(o["mapping"], w.num_tokens, o["x"], o["a"], o["b"], float(w.scale),
                             bufs[i], n, o["y"], o["meta"], ws, stream=stream,
                             expand_config=cfg if cfg is not None else ExpandConfig(),
-                            start_delay_ns=delay, part_sums=sums, batch_order_shrink=batch)
+                            start_delay_ns=delay, part_sums=sums, batch_order_shrink=batch,
+                            y_delay_ns=y_delay)
 
         for i in range(copies):
             step(i, None)
@@ -343,17 +350,20 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
         if us_sums[skey] < min(us_expand.values()):
             best_sums, best_n, best_cfg = True, sn, ExpandConfig(**json.loads(skey))
             us_expand = dict(us_expand, **{"part sums " + k: v for k, v in us_sums.items()})
-    # the one-launch path's expand hold-off, at the best part count (None:
-    # the library's default from the shrink's per-workgroup bytes)
+    # the one-launch path's expand hold-offs (y, then B), at the best part
+    # count (None: the library's defaults from the shrink's per-workgroup bytes)
     us_delay = {}
-    best_delay = None
+    best_delay = best_y_delay = None
     if one_launch:
         us_delay["default"] = us_splits[best_n]
-        for d in _DELAY_CANDIDATES_NS:
-            us_delay[str(d)] = time_step(best_n, None, d)
-            log(f"[tune] {w.name} splits={best_n} start_delay_ns={d}: {us_delay[str(d)]:.2f} us")
+        for yd, bd in _HOLD_CANDIDATES_NS:
+            key = f"{yd},{bd}"
+            us_delay[key] = time_step(best_n, None, bd, y_delay=yd)
+            log(f"[tune] {w.name} splits={best_n} y_delay_ns={yd} start_delay_ns={bd}: "
+                f"{us_delay[key]:.2f} us")
         best_key = min(us_delay, key=us_delay.get)
-        best_delay = None if best_key == "default" else int(best_key)
+        if best_key != "default":
+            best_y_delay, best_delay = (int(v) for v in best_key.split(","))
     best_us = min(us_expand.values()) if us_expand else (
         min(us_delay.values()) if us_delay else us_splits[best_n])
     del ops
@@ -367,6 +377,7 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
         "num_splits": int(best_n),
         "expand": best_cfg.as_dict(),
         "start_delay_ns": best_delay,
+        "y_delay_ns": best_y_delay,
         "part_sums": best_sums,
         "batch_order_shrink": batch and not best_sums,
         "step_us": round(best_us, 3),
@@ -374,7 +385,7 @@ def tune_workload(w, reps: int = 20, log=print) -> dict:
         "step_us_by_splits": {str(k): round(v, 3) for k, v in us_splits.items()},
         "step_us_by_splits_batch_order": {str(k): round(v, 3) for k, v in us_batch.items()},
         "step_us_by_expand": {k: round(v, 3) for k, v in us_expand.items()},
-        "step_us_by_start_delay_ns": {k: round(v, 3) for k, v in us_delay.items()},
+        "step_us_by_hold_offs_ns": {k: round(v, 3) for k, v in us_delay.items()},
         "step_us_with_part_sums": {k: round(v, 3) for k, v in us_sums.items()},
     }
 

@@ -245,12 +245,14 @@ def test_fused_step_rejects(kw):
 
 def test_fused_step_rejects_long_start_delay():
     # lora_step_options_t: wait_polls, then the three ints of the expand's
-    # config, then start_delay_ns, part_sums and batch_order_shrink
+    # config, then start_delay_ns, part_sums, batch_order_shrink and y_delay_ns
     O = srg._StepOptions
     assert (O.wait_polls.offset, O.expand.offset, O.start_delay_ns.offset,
-            O.part_sums.offset, O.batch_order_shrink.offset) == (0, 4, 16, 20, 24)
-    assert ctypes.sizeof(O) == 28
-    assert _fused(options=ctypes.byref(O(-1, srg.ExpandConfig(), 100001, 0, 0))) == 1
+            O.part_sums.offset, O.batch_order_shrink.offset, O.y_delay_ns.offset) == (
+                0, 4, 16, 20, 24, 28)
+    assert ctypes.sizeof(O) == 32
+    assert _fused(options=ctypes.byref(O(-1, srg.ExpandConfig(), 100001, 0, 0, -1))) == 1
+    assert _fused(options=ctypes.byref(O(-1, srg.ExpandConfig(), -1, 0, 0, 100001))) == 1
 
 
 def test_fused_step_rejects_unsupported_rank():

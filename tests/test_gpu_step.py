@@ -34,11 +34,11 @@ def _workspace(w):
 
 
 def _run_fused(d, ws, wait_polls=None, stream=None, start_delay_ns="table", part_sums=False,
-               batch_order_shrink=False):
+               batch_order_shrink=False, y_delay_ns="table"):
     srg.lora_fused_step(d.mapping, d.w.num_tokens, d.x, d.lora_a, d.lora_b, float(d.w.scale),
                         d.buf, d.num_splits, d.y, d.meta, ws, wait_polls=wait_polls,
                         stream=stream, start_delay_ns=start_delay_ns, part_sums=part_sums,
-                        batch_order_shrink=batch_order_shrink)
+                        batch_order_shrink=batch_order_shrink, y_delay_ns=y_delay_ns)
 
 
 def _check_against_two_calls(w, d_step, d_two):
@@ -172,19 +172,19 @@ def test_fused_step_without_waits_same_bits(T, maxT, hidden, slices, rank, L, sp
     (77, 96, 640, [40, 264], 16, 4, 3),
 ])
 def test_fused_step_start_delay_same_bits(T, maxT, hidden, slices, rank, L, splits):
-    """The expand units' hold-off changes timing only: no hold-off, the
-    library's default and a long one give the same bits, and the workspace
-    ends zero-filled each time."""
+    """The expand units' hold-offs change timing only: none, the library's
+    defaults, long ones and y held back longer than B give the same bits, and
+    the workspace ends zero-filled each time."""
     rng = np.random.default_rng(T * 7 + rank)
     mapping = rng.integers(-1, L, size=T)
     w = make_custom_workload(T, T, hidden, slices, rank, L, 0.75, mapping, max_tokens=maxT)
     ws = _workspace(w)
     runs = []
-    for delay in (0, None, 4000):
+    for y_delay, delay in ((0, 0), (None, None), (800, 4000), (3000, 500)):
         d = H.upload(w, num_splits=splits)
-        _run_fused(d, ws, start_delay_ns=delay)
+        _run_fused(d, ws, start_delay_ns=delay, y_delay_ns=y_delay)
         torch.cuda.synchronize()
-        assert int(ws.count_nonzero()) == 0, delay
+        assert int(ws.count_nonzero()) == 0, (y_delay, delay)
         runs.append(d)
     for d in runs[1:]:
         _check_against_two_calls(w, d, runs[0])
