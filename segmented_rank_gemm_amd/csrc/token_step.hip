@@ -245,16 +245,30 @@ __device__ __forceinline__ void token_shrink_unit(const TokenParams& p, int u, f
     }
   };
   if constexpr (DEPTH == 1) {
-    // At most one chunk per wave (parts of at most 256 elements).  A goes
-    // through this wave's own LDS region with whole-line loads: instruction j
-    // fetches rows 8j..8j+7 of the group, 8 lanes per 128-byte line (lane
-    // 8 rr + e reads row 8j + rr, piece e ^ rr, so the region holds row R's
-    // piece q at 16-byte slot 8R + (q ^ (R & 7)) and the MFMA-layout reads
-    // below hit distinct banks).  A load in the operand layout would touch 16
-    // lines for half a line each; whole lines move faster through the CU.
-    // Rows 8j..8j+7 are ranks 8i..8i+7 of one (adapter, slice) (r is a
-    // multiple of 8): contiguous rows of one A_s.  A group past the last
-    // output re-reads the last one (masked by amask).  x stays in registers.
+    // At most one chunk per wave (parts of at most 256 elements).  x first,
+    // into registers: read once (by this unit only), so with the streaming
+    // hint, and ahead of A since x comes from HBM and A mostly from L2 (decode
+    // step 9.96 -> 9.89 us for the hint, 9.20 -> 8.93 us for the order).
+    u32x4 xv[MW][2];
+    uint32_t kmask[2];
+    {
+      const bool full = kc + kShrinkChunk <= kend;  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int k = piece(kc, i, full, kmask[i]);
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb) xv[mb][i] = load16_stream(xrow[mb] + k);
+      }
+    }
+    // A goes through this wave's own LDS region with whole-line loads:
+    // instruction j fetches rows 8j..8j+7 of the group, 8 lanes per 128-byte
+    // line (lane 8 rr + e reads row 8j + rr, piece e ^ rr, so the region holds
+    // row R's piece q at 16-byte slot 8R + (q ^ (R & 7)) and the MFMA-layout
+    // reads below hit distinct banks).  A load in the operand layout would
+    // touch 16 lines for half a line each; whole lines move faster through
+    // the CU.  Rows 8j..8j+7 are ranks 8i..8i+7 of one (adapter, slice) (r is
+    // a multiple of 8): contiguous rows of one A_s.  A group past the last
+    // output re-reads the last one (masked by amask).
     u32x4* const stg = reinterpret_cast<u32x4*>(red) + wave * (2 * NB * kWave);
     {
       const int rr = lane >> 3;
@@ -288,19 +302,6 @@ __device__ __forceinline__ void token_shrink_unit(const TokenParams& p, int u, f
           rem = 0;
           ++l;
         }
-      }
-    }
-    // x, read once (by this unit only), with the streaming hint (decode
-    // step 9.96 -> 9.89 us)
-    u32x4 xv[MW][2];
-    uint32_t kmask[2];
-    {
-      const bool full = kc + kShrinkChunk <= kend;  // wave-uniform
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int k = piece(kc, i, full, kmask[i]);
-#pragma unroll
-        for (int mb = 0; mb < MW; ++mb) xv[mb][i] = load16_stream(xrow[mb] + k);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -888,18 +889,17 @@ hipError_t launch_token_prep_shrink(const int32_t* mapping, int num_tokens, cons
 }
 
 // Default hold-offs of the expand units (ns), in proportion to what a shrink
-// unit loads (A and x): B after 46 ns per KB, y after 14 (measured on the
-// decode batch, a unit reading 56 KB: best at B 2.4-2.6 us with y 0.6-0.8 us,
-// 7% off the step with both at 2 us; y at 0 or 1.2 us, or B at 2.2 or 3 us,
-// cost 2-10%).
+// unit loads (A and x): B after 43 ns per KB, y after 11 (measured on the
+// decode batch, a unit reading 56 KB: best at B 2.2-2.4 us with y 0.6-0.8 us;
+// both at 2 us cost 7%, y at 0 or 1.2 us, or B at 2.0 or 2.8 us, 2-10%).
 static int64_t token_shrink_unit_kb(const TokenParams& p, int nb) {
   return static_cast<int64_t>(16 * nb + kTokTile * kTokShrinkMw) * p.split_len * 2 / 1024;
 }
 static int token_step_default_delay_ns(const TokenParams& p, int nb) {
-  return static_cast<int>(46 * token_shrink_unit_kb(p, nb));
+  return static_cast<int>(43 * token_shrink_unit_kb(p, nb));
 }
 static int token_step_default_y_delay_ns(const TokenParams& p, int nb) {
-  return static_cast<int>(14 * token_shrink_unit_kb(p, nb));
+  return static_cast<int>(11 * token_shrink_unit_kb(p, nb));
 }
 
 // The one-launch step.  The caller checked token_step_fits and the workspace.
