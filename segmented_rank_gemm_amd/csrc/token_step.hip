@@ -433,10 +433,7 @@ __device__ __forceinline__ void token_expand_unit(const TokenParams& p, int u, u
     const bool has_chunk = ch < chunks_s;
     const int chc = has_chunk ? ch : chunks_s - 1;
 
-    // First round trip: the arrivals (wave 0), the ids, B of every adapter
-    // slot, y; all issued before anything waits.
-    int arrived = 0;
-    if (wave == 0) arrived = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // First round trip: the ids (y and B follow after their hold-offs).
     const int ta = t0 + c;  // rank-operand row
     const int la = adapter_of(p, ta);
     int td[4], ld[4];
@@ -516,7 +513,7 @@ __device__ __forceinline__ void token_expand_unit(const TokenParams& p, int u, u
         // Four polls in flight, issued a short sleep apart, each checked as it
         // returns (loads return in order) and reissued: a count that becomes
         // complete is seen about one round trip later, not up to two.
-        bool done = arrived >= target;
+        bool done = false;
         if (!done && p.wait_polls > 0) {
           auto poll = [&]() {
             __builtin_amdgcn_s_sleep(2);
