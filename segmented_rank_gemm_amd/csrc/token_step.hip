@@ -162,6 +162,8 @@ __device__ __forceinline__ void token_shrink_unit(const TokenParams& p, int u, f
   const int kend = min(p.hidden, kbeg + p.split_len);
 
   // A rows: output o = o0 + 16*nb + col (MFMA M index); past the last: the last, masked.
+  // (The row pointers serve the two-chunk register path; with one chunk per
+  // wave A goes through LDS, addressed per 8-row group below.)
   const uint16_t* arow[NB];
   uint32_t amask[NB];
 #pragma unroll
