@@ -30,8 +30,10 @@
 // expand_grid workgroups expand, and the last max_loras + 1 compute the
 // metadata (the metadata kernel's code).  A shrink unit writes its part with
 // device-coherent stores, waits for them to complete, and increments its
-// tile's arrival counter; an expand unit fetches its y, B and ids, then polls
-// the counter until every part of its tile has arrived and reads the parts
+// tile's arrival counter; an expand unit fetches its ids, then (each after a
+// hold-off that leaves the shrink units' loads the fetch path first) its y
+// and B, then polls the counter until every part of its tile has arrived and
+// reads the parts
 // with device-coherent loads.  Workgroups are dispatched in index order on
 // each XCD and every shrink workgroup precedes every expand workgroup, so a
 // waiting expand unit never holds a slot a part it waits for still needs; the
@@ -478,8 +480,9 @@ __device__ __forceinline__ void token_expand_unit(const TokenParams& p, int u, u
     // unit waits for come sooner that way; y and B still arrive before the
     // parts do.  y (from HBM, the slower to arrive) goes out first, after a
     // shorter hold-off, B (mostly L2 hits) after the longer one: on the decode
-    // batch 9.23 us per step against 9.90 with both at 2 us.  Timed on the
-    // chip's constant 100 MHz clock from here.
+    // batch 9.23 us per step against 9.90 with both at 2 us (8.7 us once the
+    // shrink's x went out ahead of its A).  Timed on the chip's constant
+    // 100 MHz clock from here.
     {
       const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
       auto hold_until = [&](int ticks) {
