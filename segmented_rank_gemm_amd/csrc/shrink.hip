@@ -699,6 +699,23 @@ void shrink_batch_kernel(ShrinkParams p) {
       const int r = row0 + 32 * j;
       if (r < kLdsTile) src[j] = p.x + static_cast<int64_t>(t0 + r < p.num_tokens ? t0 + r : t0) * p.ldx;
     }
+    // The x pieces of the first two chunks go out right behind the map: they
+    // do not depend on the tile's adapters (the first pass below then loads
+    // only its A pieces for those chunks).  Pieces j < kLdsTile / 32 are x rows.
+    struct Staged {
+      u32x4 v[kJ];
+    };
+    auto chunk_k = [&](int c) {
+      const int k = kbeg + (c < nchunks ? c : nchunks - 1) * kShrinkChunk + 8 * piece;
+      return k < kend ? k : kbeg;
+    };
+    Staged ra, rb;
+#pragma unroll
+    for (int j = 0; j < kLdsTile / 32; ++j) {
+      ra.v[j] = load16(src[j] + chunk_k(0));
+      rb.v[j] = load16(src[j] + chunk_k(1));
+    }
+    bool x_in_flight = true;
     // the tile's adapters, lowest lane first (the same order in every wave):
     // the first, or all the others
     uint64_t pending = __ballot(lr >= 0);
@@ -720,13 +737,10 @@ void shrink_batch_kernel(ShrinkParams p) {
                    (static_cast<int64_t>(l) * p.rank + (o & (p.rank - 1))) * p.hidden;
         }
       }
-      // the chunk loop of shrink_lds_kernel, unchanged
-      struct Staged {
-        u32x4 v[kJ];
-      };
+      // the chunk loop of shrink_lds_kernel (its first two chunks' x already
+      // in flight on the first pass)
       auto gload = [&](int c, Staged& st) {
-        const int k = kbeg + (c < nchunks ? c : nchunks - 1) * kShrinkChunk + 8 * piece;
-        const int kk = k < kend ? k : kbeg;
+        const int kk = chunk_k(c);
 #pragma unroll
         for (int j = 0; j < kJ; ++j) st.v[j] = load16(src[j] + kk);
       };
@@ -756,9 +770,17 @@ void shrink_batch_kernel(ShrinkParams p) {
           }
         }
       };
-      Staged ra, rb;
-      gload(0, ra);
-      gload(1, rb);
+      if (x_in_flight) {
+#pragma unroll
+        for (int j = kLdsTile / 32; j < kJ; ++j) {
+          ra.v[j] = load16(src[j] + chunk_k(0));
+          rb.v[j] = load16(src[j] + chunk_k(1));
+        }
+        x_in_flight = false;
+      } else {
+        gload(0, ra);
+        gload(1, rb);
+      }
       sstore(0, ra);
       gload(2, ra);
       __syncthreads();
