@@ -29,6 +29,9 @@ def test_table_entries_are_valid():
         assert 0 <= x["chunks_per_range"] <= max_cpr
         assert x["range_fastest"] in (-1, 0, 1)
         assert 0 <= x["workgroups_per_cu"] <= 16
+        # hold-offs: the library's default (None) or inside what the ABI accepts
+        for k in ("start_delay_ns", "y_delay_ns"):
+            assert e[k] is None or 0 <= e[k] <= 100000, (key, k)
         # the measured choice is no slower than the rule it replaces
         assert e["step_us"] <= e["rule"]["step_us"] + 1e-9
 
