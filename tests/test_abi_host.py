@@ -255,6 +255,18 @@ def test_fused_step_rejects_long_start_delay():
     assert _fused(options=ctypes.byref(O(-1, srg.ExpandConfig(), -1, 0, 0, 100001))) == 1
 
 
+def test_step_options_carry_both_hold_offs():
+    # the binding's options: explicit hold-offs reach their fields; defaults
+    # everywhere mean no options struct at all
+    r = srg._step_options(None, None, 2000, None, None, None, False, False, 600)
+    o = r._obj
+    assert (o.wait_polls, o.start_delay_ns, o.part_sums, o.batch_order_shrink, o.y_delay_ns) == (
+        -1, 2000, 0, 0, 600)
+    o = srg._step_options(7, None, None, y_delay_ns=None)._obj
+    assert (o.wait_polls, o.start_delay_ns, o.y_delay_ns) == (7, -1, -1)
+    assert srg._step_options(None, None, None) is None
+
+
 def test_fused_step_rejects_unsupported_rank():
     # rank 12: valid range, no kernel for it (checked before anything is enqueued)
     assert _fused(rank=12) == 2
