@@ -118,13 +118,18 @@ int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t m
     return 0;
   // Enough (tile, part, output group) units for ~1 workgroup per CU of a
   // 256-CU device at the largest batch, with parts of at least 256 hidden
-  // elements.  Small batches (16-token tiles): ~2 units per CU, but no more
-  // parts than the expand sums with one batch of loads (16 for rank 8, else 8)
-  // and parts * rank <= 256 (at most 1 KB of parts per token).  Large batches
-  // (64-token tiles): also parts of about 1400 elements (at least 4), so that
-  // several workgroups share each CU, up to 8 parts (measured on the prefill,
-  // down_proj and 70B shapes; a second batch of loads in the expand at rank 64
-  // costs far less than the shrink gains).
+  // elements.  Small batches (16-token tiles) at ranks 8 and 16: parts of at
+  // most 256 elements, one 64-element chunk per wave, the batch-order
+  // shrink's fast path (measured through lora_fused_step, µs: qkv 3 x 4096,
+  // rank 8, 512 tokens 22.3 at the former 15 parts -> 13.9 at 16; rank 16,
+  // 256 tokens 18.4 at 8 -> 14.1 at 16; hidden 8192, rank 8, 256 tokens 15.6
+  // at 16 -> 12.7 at 32; the two-call path gained too).  Other small batches:
+  // ~2 units per CU, but no more parts than the expand sums with one batch of
+  // loads (8) and parts * rank <= 256 (at most 1 KB of parts per token).
+  // Large batches (64-token tiles): also parts of about 1400 elements (at
+  // least 4), so that several workgroups share each CU, up to 8 parts
+  // (measured on the prefill, down_proj and 70B shapes; a second batch of
+  // loads in the expand at rank 64 costs far less than the shrink gains).
   const int nb_total = (num_slices * rank + 15) / 16;
   const int nb = lora::shrink_group_blocks(nb_total);
   const int64_t groups = (nb_total + nb - 1) / nb;
@@ -140,11 +145,14 @@ int32_t lora_shrink_default_splits(int32_t hidden, int32_t max_tokens, int32_t m
     by_work = by_work < 4 ? 4 : by_work;
     splits = splits > by_work ? splits : by_work;
     cap = 8;
+  } else if (rank <= 16) {
+    splits = (hidden + 255) / 256;  // parts of at most 256 elements
+    cap = LORA_MAX_SPLITS;
   } else {
-    const int64_t group = rank == 8 ? 16 : 8;  // parts the expand sums per batch of loads
+    const int64_t group = 8;  // parts the expand sums per batch of loads
     cap = 256 / rank < group ? 256 / rank : group;
   }
-  splits = splits < by_len ? splits : by_len;
+  if (mw == 4 || rank > 16) splits = splits < by_len ? splits : by_len;
   splits = splits < cap ? splits : cap;
   splits = splits < 1 ? 1 : (splits > LORA_MAX_SPLITS ? LORA_MAX_SPLITS : splits);
   return static_cast<int32_t>(splits);
