@@ -844,9 +844,24 @@ static TokenParams token_params(const int32_t* mapping, int num_tokens, const ui
   return p;
 }
 
+// Default hold-offs of the expand units (ns), in proportion to what a shrink
+// unit loads (A and x): B after 43 ns per KB, y after 11 (measured on the
+// decode batch, a unit reading 56 KB: best at B 2.2-2.4 us with y 0.6-0.8 us;
+// both at 2 us cost 7%, y at 0 or 1.2 us, or B at 2.0 or 2.8 us, 2-10%).
+static int64_t token_shrink_unit_kb(const TokenParams& p, int nb) {
+  return static_cast<int64_t>(16 * nb + kTokTile * kTokShrinkMw) * p.split_len * 2 / 1024;
+}
+static int token_step_default_delay_ns(const TokenParams& p, int nb) {
+  return static_cast<int>(43 * token_shrink_unit_kb(p, nb));
+}
+static int token_step_default_y_delay_ns(const TokenParams& p, int nb) {
+  return static_cast<int>(11 * token_shrink_unit_kb(p, nb));
+}
+
 template <int NB, int DEPTH, int RANK, int LCAP, bool STEP, bool WT>
-static hipError_t launch_token(const TokenParams& p, hipStream_t stream) {
+static hipError_t launch_token(const TokenParams& params, hipStream_t stream) {
   constexpr int MW = kTokShrinkMw;
+  TokenParams p = params;
   const int grid = p.shrink_grid + (STEP ? p.expand_grid : 0) + p.max_loras + 1;
   // one chunk per wave: A staged per wave (twice the sums' size), the sums in it
   const size_t red = static_cast<size_t>(kShrinkWaves) * NB * kWave * sizeof(f32x4) * (DEPTH == 1 ? 2 : 1);
@@ -855,6 +870,28 @@ static hipError_t launch_token(const TokenParams& p, hipStream_t stream) {
                           : 0;
   size_t lds = red > bst ? red : bst;
   lds = lds > sizeof(MetaLds<kShrinkThreads>) ? lds : sizeof(MetaLds<kShrinkThreads>);
+  if constexpr (STEP) {
+    // Default hold-offs (negative ticks): none when the shrink's workgroups
+    // alone fill every slot of the device, since the expand's then start only
+    // as shrink workgroups end, with nothing left to make way for (rank 16,
+    // 256 tokens, two workgroups per CU: 14.1 -> 12.9 us); else the sizes'
+    // defaults.  Workgroups per CU: looked up once per kernel and kept.
+    if (p.start_delay_ticks < 0 || p.y_delay_ticks < 0) {
+      static const int per_cu = [lds] {
+        int v = 0;
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                   &v, token_kernel<NB, MW, DEPTH, RANK, LCAP, STEP, WT>, kShrinkThreads, lds) ==
+                       hipSuccess
+                   ? v
+                   : 0;
+      }();
+      const bool crowded = per_cu > 0 && p.shrink_grid >= per_cu * kCus;
+      if (p.start_delay_ticks < 0)
+        p.start_delay_ticks = crowded ? 0 : (token_step_default_delay_ns(p, NB) + 5) / 10;
+      if (p.y_delay_ticks < 0)
+        p.y_delay_ticks = crowded ? 0 : (token_step_default_y_delay_ns(p, NB) + 5) / 10;
+    }
+  }
   hipLaunchKernelGGL((token_kernel<NB, MW, DEPTH, RANK, LCAP, STEP, WT>), dim3(grid), dim3(kShrinkThreads),
                      lds, stream, p);
   return hipGetLastError();
@@ -890,19 +927,6 @@ hipError_t launch_token_prep_shrink(const int32_t* mapping, int num_tokens, cons
   return launch_token_nb<8, 4, false>(p, nb, stream);
 }
 
-// Default hold-offs of the expand units (ns), in proportion to what a shrink
-// unit loads (A and x): B after 43 ns per KB, y after 11 (measured on the
-// decode batch, a unit reading 56 KB: best at B 2.2-2.4 us with y 0.6-0.8 us;
-// both at 2 us cost 7%, y at 0 or 1.2 us, or B at 2.0 or 2.8 us, 2-10%).
-static int64_t token_shrink_unit_kb(const TokenParams& p, int nb) {
-  return static_cast<int64_t>(16 * nb + kTokTile * kTokShrinkMw) * p.split_len * 2 / 1024;
-}
-static int token_step_default_delay_ns(const TokenParams& p, int nb) {
-  return static_cast<int>(43 * token_shrink_unit_kb(p, nb));
-}
-static int token_step_default_y_delay_ns(const TokenParams& p, int nb) {
-  return static_cast<int>(11 * token_shrink_unit_kb(p, nb));
-}
 
 // The one-launch step.  The caller checked token_step_fits and the workspace.
 hipError_t launch_token_step(const int32_t* mapping, int num_tokens, const uint16_t* x,
@@ -938,10 +962,9 @@ hipError_t launch_token_step(const int32_t* mapping, int num_tokens, const uint1
   p.expand_grid = (p.expand_units + kXcds - 1) / kXcds * kXcds;
   p.counters = counters;
   p.wait_polls = wait_polls;
-  if (start_delay_ns < 0) start_delay_ns = token_step_default_delay_ns(p, nb);
-  if (y_delay_ns < 0) y_delay_ns = token_step_default_y_delay_ns(p, nb);
-  p.start_delay_ticks = (start_delay_ns + 5) / 10;
-  p.y_delay_ticks = (y_delay_ns + 5) / 10;
+  // negative: the defaults, resolved at the launch (they depend on the kernel)
+  p.start_delay_ticks = start_delay_ns < 0 ? -1 : (start_delay_ns + 5) / 10;
+  p.y_delay_ticks = y_delay_ns < 0 ? -1 : (y_delay_ns + 5) / 10;
   // y written through where its byte offsets fit 32 bits (all but y of 4 GiB
   // or more)
   const bool wt = static_cast<int64_t>(num_tokens) * ldy * 2 < (int64_t{1} << 32);
