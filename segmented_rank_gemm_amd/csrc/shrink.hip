@@ -382,15 +382,20 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
 // rows and 16*NB A rows with full-line loads (8 lanes per 128-byte row line,
 // every byte of every line used) into LDS, where the row's 16-byte pieces are
 // XOR-swizzled by row so that the MFMA-layout reads (16 rows x 16 bytes per
-// instruction) hit 16 distinct banks.  Two chunks are in flight in registers
-// ahead of the one being computed; LDS is double-buffered, one barrier per
+// instruction) hit 16 distinct banks.  Two or four chunks are in flight in
+// registers ahead of the one being computed; LDS is double-buffered, one barrier per
 // chunk.  Wave w owns token block w (16 tokens) and all output blocks, so no
 // cross-wave reduction is needed.
 constexpr int kLdsTile = 64;  // tokens per tile (4 waves x 16)
+// Chunks in flight in registers: four at four output blocks (down_proj,
+// rank 64: 21.3-21.4 against 21.8-22.1 us), else two (measured at four: the
+// gate_up prefill shape's two blocks 18.4 against 18.1 us, the 70B qkv
+// shape's six 30.4 against 28.6 us); two with part sums (four would spill).
+constexpr int lds_depth(int nb, bool sums) { return nb == 4 && !sums ? 4 : 2; }
 
 // Three workgroups per CU (registers and LDS allow it up to NB = 6), so that a
 // batch's units all run in one round.
-template <int NB, bool SUMS = false>
+template <int NB, bool SUMS = false, int DEPTH = lds_depth(NB, SUMS)>
 __global__ __launch_bounds__(kShrinkThreads) __attribute__((amdgpu_waves_per_eu(NB <= 6 ? 3 : 2)))
 void shrink_lds_kernel(ShrinkParams p) {
   constexpr int kRows = kLdsTile + 16 * NB;       // x rows, then A rows
@@ -570,31 +575,36 @@ void shrink_lds_kernel(ShrinkParams p) {
       }
     };
 
-    // Two chunks in flight in registers ahead of the one computed.  Chunks go
-    // in pairs (LDS buffer 0, then 1) with one exit test per pair, so that
-    // every path into a wait has the same loads outstanding; loads and LDS
-    // stores past the last chunk repeat it into a buffer no one reads any
-    // more.  An odd last chunk sits in buffer 0.  (The previous unit ended on
-    // a barrier after its last read of stage.)
-    Staged ra, rb;
-    gload(0, ra);
-    gload(1, rb);
-    sstore(0, ra);
-    gload(2, ra);
+    // DEPTH chunks in flight in registers ahead of the one computed (chunk j
+    // in r[j % DEPTH], LDS buffer j % 2).  Chunks go in groups of DEPTH with
+    // one exit test per group, so that every path into a wait has the same
+    // loads outstanding; loads past the last chunk repeat it into registers
+    // no one stores any more.  (The previous unit ended on a barrier after
+    // its last read of stage.)
+    static_assert(DEPTH >= 2 && DEPTH % 2 == 0, "chunk c sits in LDS buffer c % 2");
+    Staged r[DEPTH];
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) gload(i, r[i]);
+    sstore(0, r[0]);
+    gload(DEPTH, r[0]);
     __syncthreads();
     int c = 0;
-    for (; c + 2 <= nchunks; c += 2) {
-      compute(0, c);
-      sstore(1, rb);
-      gload(c + 3, rb);
-      __syncthreads();
-      compute(1, c + 1);
-      sstore(0, ra);
-      gload(c + 4, ra);
-      __syncthreads();
+    for (; c + DEPTH <= nchunks; c += DEPTH) {
+#pragma unroll
+      for (int i = 0; i < DEPTH; ++i) {
+        compute(i & 1, c + i);
+        sstore((i + 1) & 1, r[(i + 1) % DEPTH]);
+        gload(c + i + 1 + DEPTH, r[(i + 1) % DEPTH]);
+        __syncthreads();
+      }
     }
-    if (c < nchunks) {
-      compute(0, c);
+    // the last nchunks % DEPTH chunks: chunk c is in buffer 0, the rest in
+    // registers
+#pragma unroll
+    for (int i = 0; i < DEPTH - 1; ++i) {
+      if (c + i >= nchunks) break;  // uniform
+      compute(i & 1, c + i);
+      if (c + i + 1 < nchunks) sstore((i + 1) & 1, r[(i + 1) % DEPTH]);
       __syncthreads();
     }
 
