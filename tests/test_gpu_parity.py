@@ -155,6 +155,12 @@ LARGE_BATCH_PARTS = [
     (1500, 4096, [2048, 2048], 16, 4, 8),
     (3000, 8192, [8192, 1024, 1024], 32, 64, 6),
     (2048, 1024, [512], 8, 1, 3),
+    # 64 outputs (four blocks: four chunks in flight), parts of 35 chunks (a
+    # three-chunk tail after the four-chunk groups), 41 chunks with the last
+    # one partial (one-chunk tail) and 6 chunks (two-chunk tail)
+    (600, 4480, [1024], 64, 8, 2),
+    (700, 2600, [512, 256], 32, 5, 1),
+    (640, 768, [128, 128, 128, 128], 16, 3, 2),
 ]
 
 
